@@ -1,0 +1,50 @@
+"""The pins catch plausible mistakes in the oracle (CPU only).
+
+Each case plants one mistake in a copy of the oracle's C source (a wrong
+index, a dropped term, a wrong sign or an operand mix-up), builds that copy in a
+temporary directory and runs every pin on it: at least one pin must fail. The
+real oracle is never modified.
+"""
+import os
+
+import pytest
+
+import oracle
+from oracle_pins import ALL_PINS
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle_attn.c")
+
+MUTANTS = {
+    "causal_off_by_one": ("if (causal && j > q_offset + i)", "if (causal && j >= q_offset + i)"),
+    "q_offset_ignored": ("if (causal && j > q_offset + i)", "if (causal && j > i)"),
+    "head_map_interleaved": ("const int64_t g = h / (Hq / Hkv);", "const int64_t g = h % Hkv;"),
+    "scale_one_over_d": ("const double scale = 1.0 / sqrt((double)D);", "const double scale = 1.0 / (double)D;"),
+    "scale_dropped": ("s[j] = scale * dot;", "s[j] = dot;"),
+    "lse_max_dropped": ("*lse_out = M + log(l);", "*lse_out = log(l);"),
+    "no_normalisation": ("for (int64_t d = 0; d < D; ++d) o_row[d] /= l;", ""),
+    "k_v_swapped_in_scores": ("(double)qi[d] * (double)kb[j * D + d]", "(double)qi[d] * (double)vb[j * D + d]"),
+    "segment_batch_index": ("seg_k[b * Lk + j]", "seg_k[j]"),
+    "segment_test_inverted": ("seg_q[b * Lq + i] != seg_k[b * Lk + j]", "seg_q[b * Lq + i] == seg_k[b * Lk + j]"),
+    "merge_weight_mixup": ("(w1 * o1[r * D + d] + w2 * o2[r * D + d])", "(w1 * o1[r * D + d] + w1 * o2[r * D + d])"),
+    "merge_sign": ("const double w1 = exp(l1 - M), w2 = exp(l2 - M);", "const double w1 = exp(M - l1), w2 = exp(l2 - M);"),
+    "empty_row_nan": ("  if (nvis == 0) {\n    *lse_out = -INFINITY;", "  if (nvis < 0) {\n    *lse_out = -INFINITY;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, tmp_path):
+    before, after = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(before) == 1, "mutation site not found: %s" % name
+    mutant_src = tmp_path / "mutant.c"
+    mutant_src.write_text(src.replace(before, after))
+    lib_path = str(tmp_path / "libmutant.so")
+    oracle.compile_source(str(mutant_src), lib_path, werror=False)
+    orc = oracle.Oracle(oracle.open_library(lib_path))
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            pin(orc)
+        except (AssertionError, ValueError, FloatingPointError):
+            caught.append(pin.__name__)
+    assert caught, "no pin caught mutant %s" % name
