@@ -1,0 +1,240 @@
+"""Benchmark: exact causal GQA attention forward on one MI355X.
+
+One step = one forward over the workload (default: the fp32 causal forward at
+L = 30,468, B = 1, Hq = 16, Hkv = 4, D = 256; synthetic N(0,1) inputs already
+resident in HBM). Prints ONE JSON line. `value` is TFLOP/s counted as 4*D per
+visible (query, key) pair per query head (the causal half of the L x L work).
+Secondary workloads (the other lengths, bf16, the shared-prefix branch form and
+the packed-segment form) are reported under "secondary".
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "causal GQA attn fwd TFLOP/s + % MFMA peak (fp32 & bf16, L=32k/64k); peak GiB"
+HQ, HKV, D = 16, 4, 256
+
+
+def dev_inputs(x, torch):
+    dev = "cuda:0"
+    if x.dtype == "f32":
+        return tuple(torch.from_numpy(a).to(dev) for a in (x.q, x.k, x.v))
+    return tuple(torch.from_numpy(b.view(np.int16)).to(dev).view(torch.bfloat16) for b in (x.q_bits, x.k_bits, x.v_bits))
+
+
+def time_calls(fn, steps, warmup, torch):
+    """Wall time per step (host clock around K synchronized steps) and the mean
+    per-call GPU time from HIP events recorded on the launch stream."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    ev_ms = [a.elapsed_time(b) for a, b in evs]
+    return wall_ms, float(np.mean(ev_ms)), float(np.min(ev_ms)), float(np.max(ev_ms))
+
+
+def run_fwd_workload(name, x, steps, warmup, torch, gqa, work, seg=None):
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    q, k, v = dev_inputs(x, torch)
+    sq = sk = None
+    if seg is not None:
+        sq = torch.from_numpy(seg[None]).to("cuda:0")
+        sk = sq
+    o = torch.empty_like(q)
+    B, Hq, Lq, Dh = q.shape
+    lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device)
+    free0, _ = torch.cuda.mem_get_info()
+    fn = lambda: gqa.fwd(q, k, v, causal=x.causal, q_offset=x.q_offset, seg_q=sq, seg_k=sk, out=o, lse=lse)
+    wall_ms, ev_ms, ev_min, ev_max = time_calls(fn, steps, warmup, torch)
+    free1, _ = torch.cuda.mem_get_info()
+    peak = torch.cuda.max_memory_allocated() - base
+    Lk, Hkv_ = k.shape[2], k.shape[1]
+    fl = work.flops(B, Hq, Lq, Lk, Dh, causal=x.causal, q_offset=x.q_offset,
+                    seg_q=None if seg is None else seg[None], seg_k=None if seg is None else seg[None])
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
+    return dict(workload=name, flops=fl, wall_ms=wall_ms, kernel_ms=ev_ms, kernel_ms_min=ev_min,
+                kernel_ms_max=ev_max, tflops=fl / (wall_ms * 1e-3) / 1e12, kernel_tflops=fl / (ev_ms * 1e-3) / 1e12,
+                peak_gib=peak / 2 ** 30, library_alloc_bytes=int(free0 - free1),
+                bytes=work.hbm_bytes(B, Hq, Hkv_, Lq, Lk, Dh, 4 if x.dtype == "f32" else 2, seg is not None))
+
+
+def run_branch(steps, warmup, torch, gqa, work, synth):
+    """Shared-prefix branch form, fp32: S = 30,468 prefix tokens, 40 branches of
+    m = 256 query rows at positions S.. . Prefix part: one non-causal call of all
+    n*m rows against the prefix; suffix part: one causal call over the branch keys
+    with one segment per branch; then the lse merge."""
+    br = synth.Branch(S=30468, n=40, m=256, seed=0, dtype="f32")
+    qb, kb, vb, ids = br.branch_layout()
+    dev = "cuda:0"
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    q = torch.from_numpy(qb).to(dev)
+    kp = torch.from_numpy(br.k_p[None]).to(dev)
+    vp = torch.from_numpy(br.v_p[None]).to(dev)
+    ks = torch.from_numpy(kb).to(dev)
+    vs = torch.from_numpy(vb).to(dev)
+    sid = torch.from_numpy(ids[None]).to(dev)
+    o1 = torch.empty_like(q)
+    o2 = torch.empty_like(q)
+    l1 = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    l2 = torch.empty_like(l1)
+
+    def fn():
+        gqa.fwd(q, kp, vp, causal=False, out=o1, lse=l1)
+        gqa.fwd(q, ks, vs, causal=True, seg_q=sid, seg_k=sid, out=o2, lse=l2)
+        gqa.merge(o1, l1, o2, l2, out=o1, out_lse=l1)
+
+    wall_ms, ev_ms, ev_min, ev_max = time_calls(fn, steps, warmup, torch)
+    peak = torch.cuda.max_memory_allocated() - base
+    n, m, S = br.n, br.m, br.S
+    fl = 4 * D * HQ * n * (m * S + m * (m + 1) // 2)
+    del q, kp, vp, ks, vs, o1, o2, l1, l2
+    torch.cuda.empty_cache()
+    return dict(workload="branch f32 S=30468 n=40 m=256 (prefix call + segmented suffix call + merge)",
+                flops=fl, wall_ms=wall_ms, kernel_ms=ev_ms, tflops=fl / (wall_ms * 1e-3) / 1e12,
+                kernel_tflops=fl / (ev_ms * 1e-3) / 1e12, peak_gib=peak / 2 ** 30)
+
+
+def cpu_baseline(x, target_s=15.0):
+    """The oracle (fp64, OpenMP over rows) on a bounded sample of query rows of
+    the same workload, all heads; rows spread evenly over the sequence."""
+    import oracle
+    from long_context_causal_amd import work
+    L = x.q.shape[2]
+    threads = len(os.sched_getaffinity(0))
+    threads = min(threads, 16)
+
+    def pairs(rows):
+        return int(np.sum(np.minimum(x.k.shape[2], x.q_offset + rows + 1)))
+
+    calib = np.linspace(0, L - 1, 16).astype(np.int64)
+    t0 = time.perf_counter()
+    oracle.attn(x.q, x.k, x.v, causal=True, rows=calib, nthreads=threads)
+    dt = time.perf_counter() - t0
+    n = int(max(16, min(L, 16 * target_s / max(dt, 1e-3))))
+    rows = np.linspace(0, L - 1, n).astype(np.int64)
+    t0 = time.perf_counter()
+    oracle.attn(x.q, x.k, x.v, causal=True, rows=rows, nthreads=threads)
+    dt = time.perf_counter() - t0
+    fl = 4 * D * HQ * pairs(rows)
+    return dict(value=fl / dt / 1e12, unit="TFLOP/s", cores=threads, kind="oracle",
+                sample="%d of %d query rows (evenly spaced) x 16 heads of the fp32 causal forward at L=%d, "
+                       "all their visible keys; %.1f s" % (n, L, L, dt))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--quick", action="store_true", help="primary workload only")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--only", default=None, help="run one workload: f32-30468, f32-60926, bf16-60926, ...")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the forward is not sharded across GPUs "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import long_context_causal_amd as gqa
+    import synth
+    from long_context_causal_amd import work
+
+    gqa.load_library()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    workloads = {
+        "f32-15231": ("causal GQA fwd fp32 B=1 Hq=16 Hkv=4 D=256 L=15231", 15231, "f32"),
+        "f32-30468": ("causal GQA fwd fp32 B=1 Hq=16 Hkv=4 D=256 L=30468", 30468, "f32"),
+        "f32-60926": ("causal GQA fwd fp32 B=1 Hq=16 Hkv=4 D=256 L=60926", 60926, "f32"),
+        "bf16-60926": ("causal GQA fwd bf16 B=1 Hq=16 Hkv=4 D=256 L=60926", 60926, "bf16"),
+    }
+    primary_key = args.only or "f32-30468"
+    name, L, dt = workloads[primary_key]
+    x = synth.gqa(1, HQ, HKV, L, seed=0, dtype=dt)
+    prim = run_fwd_workload(name, x, args.steps, args.warmup, torch, gqa, work)
+    peak_t = work.PEAK_TFLOPS[dt]
+
+    secondary = []
+    if not args.quick and args.only is None:
+        for key in ("f32-15231", "f32-60926", "bf16-60926"):
+            nm, Ls, dts = workloads[key]
+            xs = synth.gqa(1, HQ, HKV, Ls, seed=0, dtype=dts)
+            r = run_fwd_workload(nm, xs, max(3, args.steps // 2), 2, torch, gqa, work)
+            del xs
+            secondary.append(r)
+        secondary.append(run_branch(max(3, args.steps // 2), 2, torch, gqa, work, synth))
+        # packed segments, bf16, L = 131,072, lengths uniform in [2k, 32k] (seed 1), and the
+        # single-segment comparator at the same L
+        Lseg = 131072
+        lens = synth.segment_lengths(Lseg, 2048, 32768, seed=1)
+        ids = synth.segment_ids(lens)
+        xs = synth.gqa(1, HQ, HKV, Lseg, seed=0, dtype="bf16")
+        r = run_fwd_workload("segmented bf16 L=131072, %d segments (2k-32k)" % len(lens), xs,
+                             max(3, args.steps // 2), 2, torch, gqa, work, seg=ids)
+        secondary.append(r)
+        r = run_fwd_workload("single-segment comparator bf16 L=131072 (no ids)", xs, 3, 1, torch, gqa, work)
+        secondary.append(r)
+        del xs
+    for r in [prim] + secondary:
+        dts = "bf16" if "bf16" in r["workload"] else "f32"
+        r["pct_mfma_peak"] = 100.0 * r["kernel_tflops"] / work.PEAK_TFLOPS[dts]
+
+    math_gib = work.score_matrix_bytes(HQ, L, L, 4) / 2 ** 30
+    out = {
+        "metric": METRIC,
+        "value": round(prim["tflops"], 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(prim["wall_ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dt,
+        "data": "synthetic: Q/K/V i.i.d. N(0,1), seed 0 (stand-in for post-RoPE activations)",
+        "config": {"workload": name, "B": 1, "Hq": HQ, "Hkv": HKV, "D": D, "seq_len": L, "causal": True,
+                   "flops_per_step": prim["flops"]},
+        "pct_mfma_peak": round(100.0 * prim["kernel_tflops"] / peak_t, 2),
+        "peak_gib": round(prim["peak_gib"], 3),
+        "math_path_gib": round(math_gib, 2),
+        "library_alloc_bytes": prim["library_alloc_bytes"],
+        "roofline": {"bound": "mfma", "achieved": round(prim["kernel_tflops"], 3), "peak": peak_t,
+                     "unit": "TFLOP/s", "frac": round(prim["kernel_tflops"] / peak_t, 4), "traffic": None,
+                     "kernel_ms": round(prim["kernel_ms"], 4)},
+    }
+    if secondary:
+        out["secondary"] = [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()} for r in secondary]
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(x)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,100 @@
+/*
+ * gqa_attn.h -- C ABI of the MI355X (gfx950) exact causal grouped-query
+ * attention forward with memory linear in sequence length.
+ *
+ * The operation. For every batch b, query head h and query row i:
+ *     s_j   = (q[b,h,i,:] . k[b,g,j,:]) / sqrt(D)     for every visible key j
+ *     o     = sum_j softmax(s)_j v[b,g,j,:]
+ *     lse   = ln sum_j exp(s_j)
+ * with g = h / (Hq/Hkv): contiguous groups of query heads share one key/value
+ * head, the sharing of 16 query heads over 4 key/value heads (system1-omni
+ * issue 27, "The closest planned or implemented model"; kev pull request 202,
+ * "Why fp32 fell to the L x L kernel", where the L x L math path computes the
+ * same attention by materialising the score matrix, and "The change", where
+ * repeating K/V per query head gives the same result with memory linear in L).
+ * Key j is visible to query row i iff
+ *     (!causal || j <= q_offset + i)  &&  (seg_q == NULL || seg_q[b,i] == seg_k[b,j]).
+ * q_offset places the queries at positions q_offset.. of the key sequence: a
+ * branch whose positions restart at the state length S uses q_offset = S
+ * (system1-omni issue 27, "Three differences from Cua-S1 that matter", item 3).
+ * Segment ids are separate for queries and keys, NULL meaning one segment
+ * (maxtext pull request 4929: with constant ids the segmented and the
+ * non-segmented kernels give the same result). A row with no visible key gets
+ * o = 0 and lse = -inf.
+ *
+ * Layouts (all contiguous, row-major, element offsets fit int64):
+ *   q, o  [B, Hq,  Lq, D]   in `dtype`
+ *   k, v  [B, Hkv, Lk, D]   in `dtype`
+ *   lse   [B, Hq,  Lq]      fp32, natural log
+ *   seg_q [B, Lq], seg_k [B, Lk]  int32 (any values; sorted ids skip more work)
+ * All pointers are device pointers on the current HIP device. Accumulation is
+ * fp32; bf16 outputs are rounded to nearest even. fp32 inputs use full-fp32
+ * matrix instructions (no reduced-precision products).
+ *
+ * Ownership and threading. The caller allocates every buffer. The library
+ * allocates no device memory, keeps no pointer after returning and never
+ * synchronises: work is enqueued on `stream` (a hipStream_t; NULL is the
+ * default stream) and outputs are valid once the stream reaches that point.
+ * Every element of o and lse is written. o must not overlap q, k or v.
+ * Calls are reentrant and deterministic (same inputs give the same bits).
+ *
+ * Errors. Arguments are checked before any HIP call; on an error nothing is
+ * enqueued and outputs are untouched. A launch failure returns
+ * GQA_ERR_LAUNCH. gqa_attn_strerror names every code.
+ */
+#ifndef GQA_ATTN_H
+#define GQA_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum gqa_dtype { GQA_F32 = 0, GQA_BF16 = 1 };
+
+enum gqa_status {
+  GQA_OK = 0,
+  GQA_ERR_NULL = 1,        /* q, k, v, o or lse is NULL */
+  GQA_ERR_SHAPE = 2,       /* an extent <= 0, Hq % Hkv != 0, q_offset < 0, or exactly one segment pointer NULL */
+  GQA_ERR_UNSUPPORTED = 3, /* D != 256, dtype not F32/BF16, Hq/Hkv not in {1,2,4,8,16}, or Lq/Lk >= 2^31 */
+  GQA_ERR_ALIGN = 4,       /* q, k, v, o not 16-byte aligned, or lse/seg not 4-byte aligned */
+  GQA_ERR_LAUNCH = 5,      /* the HIP runtime reported an error at launch */
+  GQA_ERR_ALIAS = 6        /* o overlaps q, k or v (or, for merge, partially overlaps an input) */
+};
+
+/*
+ * Attention forward (the operation above). Shapes as above; D must be 256.
+ * `stream` is a hipStream_t passed as void*. Returns a gqa_status.
+ */
+int gqa_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
+                 int64_t q_offset, const int32_t* seg_q, const int32_t* seg_k,
+                 int causal, int dtype, void* stream);
+
+/*
+ * Log-sum-exp merge of two attention results over disjoint key sets of the
+ * same query rows into the result over their union:
+ *     M = max(lse1, lse2),  w_x = exp(lse_x - M),
+ *     o = (w1 o1 + w2 o2) / (w1 + w2),  lse = M + ln(w1 + w2);
+ * both lse = -inf gives o = 0, lse = -inf. This joins the prefix part and the
+ * causal suffix part of a shared-prefix branch (system1-omni issue 27, "Three
+ * differences from Cua-S1 that matter", item 3: one state, then a branch per
+ * question). o1, o2, o: [rows, D] in `dtype`; lse1, lse2, lse: [rows] fp32.
+ * o may be exactly o1 or o2 and lse exactly lse1 or lse2 (in place); partial
+ * overlaps are rejected. D must be a positive multiple of 8.
+ */
+int gqa_attn_merge(const void* o1, const float* lse1, const void* o2, const float* lse2,
+                   void* o, float* lse, int64_t rows, int64_t D, int dtype, void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* gqa_attn_strerror(int code);
+
+/* ABI version: (major << 16) | minor. */
+int gqa_attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_ATTN_H */

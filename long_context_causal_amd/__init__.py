@@ -1,0 +1,151 @@
+"""MI355X (gfx950) exact causal grouped-query attention forward, memory linear in L.
+
+A thin ctypes binding over ``libgqa_attn.so`` (C ABI in ``include/gqa_attn.h``).
+Every step of the computation runs in the library's HIP kernels; this module
+only checks tensor metadata and passes device pointers, sizes and the current
+HIP stream. PyTorch is used for device memory and streams only. There is no
+fallback: if the library is missing, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgqa_attn.so")
+
+GQA_F32, GQA_BF16 = 0, 1
+STATUS = {0: "GQA_OK", 1: "GQA_ERR_NULL", 2: "GQA_ERR_SHAPE", 3: "GQA_ERR_UNSUPPORTED",
+          4: "GQA_ERR_ALIGN", 5: "GQA_ERR_LAUNCH", 6: "GQA_ERR_ALIAS"}
+EXPORTS = ("gqa_attn_fwd", "gqa_attn_merge", "gqa_attn_strerror", "gqa_attn_version")
+
+_lib = None
+
+
+class GqaError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__("%s (%d): %s" % (STATUS.get(code, "?"), code, msg))
+        self.code = code
+
+
+def load_library():
+    """Load libgqa_attn.so from the package directory (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libgqa_attn.so is not built at %s; run __graft_entry__.build() "
+                               "or python -m long_context_causal_amd.build" % LIB_PATH)
+        lib = ctypes.CDLL(LIB_PATH)
+        i64, p, c_int = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+        lib.gqa_attn_fwd.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i64, i64, i64, p, p, c_int, c_int, p]
+        lib.gqa_attn_fwd.restype = c_int
+        lib.gqa_attn_merge.argtypes = [p, p, p, p, p, p, i64, i64, c_int, p]
+        lib.gqa_attn_merge.restype = c_int
+        lib.gqa_attn_strerror.argtypes = [c_int]
+        lib.gqa_attn_strerror.restype = ctypes.c_char_p
+        lib.gqa_attn_version.argtypes = []
+        lib.gqa_attn_version.restype = c_int
+        _lib = lib
+    return _lib
+
+
+def strerror(code: int) -> str:
+    return load_library().gqa_attn_strerror(int(code)).decode()
+
+
+def version() -> tuple[int, int]:
+    v = load_library().gqa_attn_version()
+    return v >> 16, v & 0xFFFF
+
+
+def fwd_raw(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, D, q_offset, seg_q, seg_k, causal, dtype, stream) -> int:
+    """Direct call of gqa_attn_fwd with integer pointers; returns the status code."""
+    return load_library().gqa_attn_fwd(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, D, q_offset, seg_q, seg_k,
+                                       int(causal), int(dtype), stream)
+
+
+def merge_raw(o1, lse1, o2, lse2, o, lse, rows, D, dtype, stream) -> int:
+    """Direct call of gqa_attn_merge with integer pointers; returns the status code."""
+    return load_library().gqa_attn_merge(o1, lse1, o2, lse2, o, lse, rows, D, int(dtype), stream)
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.float32:
+        return GQA_F32
+    if t.dtype == torch.bfloat16:
+        return GQA_BF16
+    raise TypeError("tensors must be float32 or bfloat16, got %s" % t.dtype)
+
+
+def _check_dev(*ts):
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def _stream_ptr(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def fwd(q, k, v, *, causal=True, q_offset=0, seg_q=None, seg_k=None, out=None, lse=None, stream=None):
+    """Attention forward: q [B,Hq,Lq,D], k/v [B,Hkv,Lk,D] (fp32 or bf16, same dtype),
+    optional int32 segment ids seg_q [B,Lq] / seg_k [B,Lk]. Returns (o, lse) with
+    o like q and lse [B,Hq,Lq] fp32. Work is enqueued on `stream` (default: the
+    current stream)."""
+    import torch
+    _check_dev(q, k, v, seg_q, seg_k, out, lse)
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("q must be [B,Hq,Lq,D] and k, v [B,Hkv,Lk,D]")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k and v must share a dtype")
+    B, Hq, Lq, D = q.shape
+    Hkv, Lk = k.shape[1], k.shape[2]
+    if k.shape[0] != B or k.shape[3] != D:
+        raise ValueError("q and k/v disagree in batch or head size")
+    if (seg_q is None) != (seg_k is None):
+        raise ValueError("give both segment-id tensors or neither")
+    if seg_q is not None:
+        if seg_q.dtype != torch.int32 or seg_k.dtype != torch.int32:
+            raise TypeError("segment ids must be int32")
+        if seg_q.numel() != B * Lq or seg_k.numel() != B * Lk:
+            raise ValueError("segment ids must be [B,Lq] and [B,Lk]")
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device)
+    if out.shape != q.shape or out.dtype != q.dtype or lse.shape != (B, Hq, Lq) or lse.dtype != torch.float32:
+        raise ValueError("out must match q and lse must be [B,Hq,Lq] float32")
+    rc = fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                 B, Hq, Hkv, Lq, Lk, D, int(q_offset),
+                 None if seg_q is None else seg_q.data_ptr(), None if seg_k is None else seg_k.data_ptr(),
+                 causal, dt, _stream_ptr(stream))
+    if rc != 0:
+        raise GqaError(rc, strerror(rc))
+    return out, lse
+
+
+def merge(o1, lse1, o2, lse2, *, out=None, out_lse=None, stream=None):
+    """Log-sum-exp merge of two results over disjoint key sets of the same rows
+    (o* [..., D], lse* [...] float32). out/out_lse may be o1/lse1 (in place)."""
+    import torch
+    _check_dev(o1, lse1, o2, lse2, out, out_lse)
+    if o1.shape != o2.shape or lse1.shape != lse2.shape or tuple(o1.shape[:-1]) != tuple(lse1.shape):
+        raise ValueError("merge operands disagree in shape")
+    if lse1.dtype != torch.float32 or lse2.dtype != torch.float32 or o2.dtype != o1.dtype:
+        raise TypeError("lse must be float32 and o1/o2 share a dtype")
+    dt = _dtype_code(o1)
+    out = torch.empty_like(o1) if out is None else out
+    out_lse = torch.empty_like(lse1) if out_lse is None else out_lse
+    rc = merge_raw(o1.data_ptr(), lse1.data_ptr(), o2.data_ptr(), lse2.data_ptr(), out.data_ptr(),
+                   out_lse.data_ptr(), lse1.numel(), o1.shape[-1], dt, _stream_ptr(stream))
+    if rc != 0:
+        raise GqaError(rc, strerror(rc))
+    return out, out_lse

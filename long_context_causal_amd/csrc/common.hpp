@@ -1,0 +1,176 @@
+// common.hpp -- device-side pieces shared by the gfx950 attention kernels:
+// vector types, the work decode (which query block and head group a workgroup
+// owns), the per-workgroup segment scan that decides which key tiles are
+// visible, and small lane-exchange helpers.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gqa {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int kD = 256;             // head dimension the kernels are built for
+constexpr int kRowsPerWave = 32;    // query rows (one head, 32 positions) per wave
+constexpr int kMaxSegTiles = 16384; // key tiles a workgroup can classify for segment skipping
+
+// Arguments of one forward launch (passed by value).
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const int32_t* seg_q;
+  const int32_t* seg_k;
+  int64_t Lq, Lk, q_offset;
+  int Hq, Hkv, n_rep;
+  int hpc;        // query heads per workgroup (a divisor of n_rep)
+  int ppc;        // query positions per workgroup
+  int n_qb;       // number of position blocks
+  int G;          // B * Hkv * (n_rep / hpc): independent head groups per position block
+  int causal;
+  float scale_log2;  // log2(e) / sqrt(D): scores go straight to the base-2 domain
+};
+
+// Which (batch, kv head, head chunk, position block) a workgroup owns.
+// Block ids run over position blocks from the last (most keys under a causal
+// mask) to the first, and over head groups fastest. Workgroups are handed to
+// the 8 XCDs round-robin by id, so with 4 (or 8) head groups every XCD works on
+// one kv head and its K/V stream stays in that XCD's L2.
+struct Work {
+  int b, kvh, h0, qb;
+  int64_t p0;
+};
+
+__device__ __forceinline__ Work decode_work(const FwdParams& p) {
+  const int i = blockIdx.x;
+  Work w;
+  w.qb = p.n_qb - 1 - i / p.G;
+  const int gi = i % p.G;
+  const int nhc = p.n_rep / p.hpc;
+  const int hc = gi % nhc;
+  const int rest = gi / nhc;
+  w.kvh = rest % p.Hkv;
+  w.b = rest / p.Hkv;
+  w.h0 = w.kvh * p.n_rep + hc * p.hpc;
+  w.p0 = (int64_t)w.qb * p.ppc;
+  return w;
+}
+
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// max / sum of a value with the same value in lane l ^ 32.
+__device__ __forceinline__ float xor32_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ int wave_min_i(int x) {
+  for (int s = 32; s >= 1; s >>= 1) x = min(x, __shfl_xor(x, s));
+  return x;
+}
+__device__ __forceinline__ int wave_max_i(int x) {
+  for (int s = 32; s >= 1; s >>= 1) x = max(x, __shfl_xor(x, s));
+  return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Async 16-byte (or 4-byte) global -> LDS copy: lane l's bytes land at
+// lds_base + l * size. lds_base must be the same in every lane of the wave.
+__device__ __forceinline__ void g2lds16(const void* src, lds_void* lds_base) {
+  __builtin_amdgcn_global_load_lds(src, lds_base, 16, 0, 0);
+}
+__device__ __forceinline__ void g2lds4(const void* src, lds_void* lds_base) {
+  __builtin_amdgcn_global_load_lds(src, lds_base, 4, 0, 0);
+}
+__device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// ---------------------------------------------------------------------------
+// Segment scan. With segment ids, a key tile is visible to the workgroup when
+// the id range of its keys meets the id range of the workgroup's query rows; it
+// is "full" (no element mask needed for the segment part) when both ranges are
+// the same single id. Ranges are exact for any ids and tight for sorted
+// (packed) ids, and the per-tile state is two bits, so the metadata grows with
+// L / tile, never with (L / tile)^2.
+// ---------------------------------------------------------------------------
+struct SegBits {
+  unsigned vis[kMaxSegTiles / 32];
+  unsigned full[kMaxSegTiles / 32];
+  int qmin, qmax;
+};
+
+template <int W, int BK>
+__device__ void seg_scan(SegBits& sb, const FwdParams& p, const Work& w, int n_tiles) {
+  constexpr int KPL = 32;          // consecutive keys each lane reduces per round
+  constexpr int LPT = BK / KPL;    // lanes that share one tile
+  static_assert(BK % KPL == 0, "tile must be a whole number of lane chunks");
+  const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+  const int words = (n_tiles + 31) >> 5;
+  for (int i = tid; i < words; i += W * 64) { sb.vis[i] = 0u; sb.full[i] = 0u; }
+  if (tid == 0) { sb.qmin = INT32_MAX; sb.qmax = INT32_MIN; }
+  __syncthreads();
+  // query id range of this workgroup's rows
+  {
+    const int32_t* sq = p.seg_q + (int64_t)w.b * p.Lq;
+    int lo = INT32_MAX, hi = INT32_MIN;
+    for (int r = tid; r < p.ppc; r += W * 64) {
+      const int64_t i = w.p0 + r;
+      if (i < p.Lq) { const int s = sq[i]; lo = min(lo, s); hi = max(hi, s); }
+    }
+    lo = wave_min_i(lo);
+    hi = wave_max_i(hi);
+    if (lane == 0) { atomicMin(&sb.qmin, lo); atomicMax(&sb.qmax, hi); }
+  }
+  __syncthreads();
+  const int qmin = sb.qmin, qmax = sb.qmax;
+  const int32_t* sk = p.seg_k + (int64_t)w.b * p.Lk;
+  const int64_t n_keys = (int64_t)n_tiles * BK;
+  for (int64_t base = (int64_t)wave * 64 * KPL; base < n_keys; base += (int64_t)W * 64 * KPL) {
+    const int64_t k0 = base + (int64_t)lane * KPL;
+    int v[KPL];
+#pragma unroll
+    for (int e = 0; e < KPL; ++e) v[e] = (k0 + e < p.Lk) ? sk[k0 + e] : qmin;
+    int lo = INT32_MAX, hi = INT32_MIN;
+    const int nvalid = (int)max((int64_t)0, min((int64_t)KPL, p.Lk - k0));
+#pragma unroll
+    for (int e = 0; e < KPL; ++e) {
+      if (e < nvalid) { lo = min(lo, v[e]); hi = max(hi, v[e]); }
+    }
+#pragma unroll
+    for (int s = 1; s < LPT; s <<= 1) {
+      lo = min(lo, __shfl_xor(lo, s));
+      hi = max(hi, __shfl_xor(hi, s));
+    }
+    const int64_t t = k0 / BK;
+    if ((lane % LPT) == 0 && t < n_tiles && lo <= hi) {
+      if (lo <= qmax && hi >= qmin) atomicOr(&sb.vis[t >> 5], 1u << (t & 31));
+      if (lo == hi && qmin == qmax && lo == qmin) atomicOr(&sb.full[t >> 5], 1u << (t & 31));
+    }
+  }
+  __syncthreads();
+}
+
+// First visible tile index >= t (n_tiles if none).
+__device__ __forceinline__ int seg_next(const SegBits& sb, int t, int n_tiles) {
+  while (t < n_tiles) {
+    unsigned m = sb.vis[t >> 5] >> (t & 31);
+    if (m) return t + __builtin_ctz(m);
+    t = (t | 31) + 1;
+  }
+  return n_tiles;
+}
+
+}  // namespace gqa

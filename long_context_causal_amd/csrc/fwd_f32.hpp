@@ -1,0 +1,236 @@
+// fwd_f32.hpp -- causal grouped-query attention forward, fp32 inputs and
+// output, full-fp32 products on gfx950 MFMA (v_mfma_f32_32x32x2_f32; no
+// reduced-precision variant, matching the pages' fp32 runs with TF32 off).
+//
+// One workgroup = 4 waves, one per SIMD: Q (128 VGPRs per lane) and the O^T
+// accumulator (128) stay in registers. For Hq/Hkv = 4 the workgroup owns the 4
+// query heads of one KV head x 32 positions. Key tiles of 32 keys (32 KB each
+// for K and V) are copied HBM -> LDS once per workgroup with async
+// global_load_lds, double-buffered, and shared by the 4 heads.
+//
+// The data flow matches the bf16 kernel: S^T = K Q^T leaves one query row per
+// lane (16 of the 32 keys in registers), the base-2 online softmax with a lazy
+// rescale runs lane-locally plus one lane-pair exchange for the row max, and
+// O^T += V^T P^T takes P straight from the S^T registers. The fp32 MFMA takes
+// one element per lane per operand, so V needs no transposing read: lanes
+// 0-31 read 32 consecutive d of one key row.
+#pragma once
+#include "common.hpp"
+
+namespace gqa {
+
+constexpr int kBkF = 32;                    // keys per LDS tile
+constexpr int kTileBytesF = kBkF * kD * 4;  // 32 KB per K or V tile
+constexpr float kLazyF = 8.0f;
+
+// Byte offset of (key, 16-byte chunk) in an fp32 tile: 1 KB rows, chunks
+// XOR-swizzled by key % 8.
+__device__ __forceinline__ uint32_t swz_f(int key, int chunk16) {
+  return (uint32_t)key * 1024u + ((uint32_t)(chunk16 ^ (key & 7)) << 4);
+}
+
+struct SmemF {
+  __attribute__((aligned(16))) char k[2][kTileBytesF];
+  __attribute__((aligned(16))) char v[2][kTileBytesF];
+  __attribute__((aligned(16))) int segk[2][kBkF];
+  SegBits bits;
+};
+
+// Async copy of key tile t into LDS stage `st`: wave w copies key rows
+// w, w + W, ... (1 KB each, lane l fetching global chunk l ^ (row % 8)).
+// Missing keys past Lk re-read row Lk-1.
+// Per-lane pieces of the swizzled LDS addresses, precomputed once so the
+// inner loops use a few VGPRs plus immediate offsets. For key row kk and
+// 16-byte chunk c the swizzled chunk is c ^ (kk % 8); all terms that do not
+// depend on the lane are folded into immediates by the callers.
+struct LanesF {
+  uint32_t ld[2];   // tile copy: (lane ^ (row % 8)) * 16 for rows w + 8i and w + 4 + 8i
+  uint32_t kq[4];   // K read for chunk 2c + g, c % 4 = j:  l32 * 1024 + ((2j + g) ^ (l32 % 8)) * 16
+  uint32_t vq[4];   // V read for key step tt, tt % 4 = j: key 4g + j, d = l32 (+ 32 n, + 8 (tt / 4) keys)
+  __device__ __forceinline__ void init(int wave, int lane) {
+    const int l32 = lane & 31, g = lane >> 5, x = l32 & 7;
+    ld[0] = (uint32_t)(lane ^ (wave & 7)) << 4;
+    ld[1] = (uint32_t)(lane ^ ((wave + 4) & 7)) << 4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      kq[j] = (uint32_t)l32 * 1024u + ((uint32_t)((2 * j + g) ^ x) << 4);
+      vq[j] = (uint32_t)(4 * g + j) * 1024u + ((uint32_t)((l32 >> 2) ^ (4 * g + j)) << 4) + ((uint32_t)(l32 & 3) << 2);
+    }
+  }
+};
+
+// Async copy of key tile t into LDS stage `st`: wave w copies key rows
+// w, w + W, ... (1 KB each, lane l fetching global chunk l ^ (row % 8)).
+// Missing keys past Lk re-read row Lk-1.
+template <int W>
+__device__ __forceinline__ void load_tile_f(SmemF& sm, int st, const char* kb, const char* vb, const int32_t* skb,
+                                            int64_t t, int64_t Lk, int wave, int lane, const LanesF& ln) {
+  static_assert(W == 4, "the lane patterns assume 4 waves");
+  const char* kt = kb + t * kTileBytesF;
+  const char* vt = vb + t * kTileBytesF;
+  const int64_t last = Lk - 1 - t * kBkF;  // last valid key within the tile (>= 0)
+#pragma unroll
+  for (int it = 0; it < kBkF / W; ++it) {
+    const int kk = wave + W * it;
+    const uint32_t src = (uint32_t)(kk <= last ? kk : (int)last) * 1024u;
+    g2lds16(kt + src + ln.ld[it & 1], (lds_void*)(sm.k[st] + kk * 1024));
+    g2lds16(vt + src + ln.ld[it & 1], (lds_void*)(sm.v[st] + kk * 1024));
+  }
+  if (skb != nullptr && wave == W - 1 && lane < kBkF) {
+    const int64_t key = min(t * kBkF + lane, Lk - 1);
+    g2lds4(skb + key, (lds_void*)sm.segk[st]);
+  }
+}
+
+template <int W>
+__global__ __launch_bounds__(W * 64) void fwd_f32_kernel(FwdParams p) {
+  __shared__ SmemF sm;
+  const Work w = decode_work(p);
+  const int wave = wave_id(), lane = lane_id();
+  const int l32 = lane & 31, g = lane >> 5;
+  const int h = w.h0 + wave % p.hpc;
+  const int64_t pw = w.p0 + (int64_t)(wave / p.hpc) * kRowsPerWave;
+  const int64_t row = pw + l32;
+  const int64_t row_c = min(row, p.Lq - 1);
+
+  const int64_t p_end = min(w.p0 + (int64_t)p.ppc, p.Lq);
+  const int64_t kv_end = p.causal ? min(p.Lk, p.q_offset + p_end) : p.Lk;
+  const int n_tiles = (int)((kv_end + kBkF - 1) / kBkF);
+
+  const bool seg = p.seg_q != nullptr;
+  const bool use_bits = seg && n_tiles <= kMaxSegTiles;
+  if (use_bits) seg_scan<W, kBkF>(sm.bits, p, w, n_tiles);
+
+  const int64_t kv_head = (int64_t)w.b * p.Hkv + w.kvh;
+  const char* kb = (const char*)p.k + kv_head * p.Lk * kD * 4;
+  const char* vb = (const char*)p.v + kv_head * p.Lk * kD * 4;
+  const int32_t* skb = seg ? p.seg_k + (int64_t)w.b * p.Lk : nullptr;
+  const int sq = seg ? p.seg_q[(int64_t)w.b * p.Lq + row_c] : 0;
+
+  // Q in registers: lane holds Q[row][8c + 4g + e], e = 0..3.
+  f32x4 qf[32];
+  const int64_t hq = ((int64_t)w.b * p.Hq + h) * p.Lq;
+  {
+    const f32x4* qr = (const f32x4*)((const char*)p.q + (hq + row_c) * kD * 4);
+#pragma unroll
+    for (int c = 0; c < 32; ++c) qf[c] = qr[2 * c + g];
+  }
+
+  f32x16 acc[8];
+#pragma unroll
+  for (int n = 0; n < 8; ++n) acc[n] = f32x16{};
+  float m_run = -INFINITY, l_part = 0.f;
+  const float sl2 = p.scale_log2;
+
+  int t = use_bits ? seg_next(sm.bits, 0, n_tiles) : 0;
+  int st = 0;
+  LanesF ln;
+  ln.init(wave, lane);
+  if (t < n_tiles) load_tile_f<W>(sm, 0, kb, vb, skb, t, p.Lk, wave, lane, ln);
+  while (t < n_tiles) {
+    const int tn = use_bits ? seg_next(sm.bits, t + 1, n_tiles) : t + 1;
+    wait_vm0();
+    __syncthreads();
+    if (tn < n_tiles) load_tile_f<W>(sm, st ^ 1, kb, vb, skb, tn, p.Lk, wave, lane, ln);
+    const int64_t k0 = (int64_t)t * kBkF;
+    if (!(p.causal && k0 > p.q_offset + pw + 31)) {
+      const bool seg_full = !seg || (use_bits && ((sm.bits.full[t >> 5] >> (t & 31)) & 1u));
+      const bool need_mask = !seg_full || k0 + kBkF > p.Lk || (p.causal && k0 + kBkF - 1 > p.q_offset + pw);
+      const char* Ks = sm.k[st];
+      const char* Vs = sm.v[st];
+
+      // S^T = K Q^T: MFMA (c, e) contracts d = 8c + e (lanes 0-31) and 8c + 4 + e (lanes 32-63).
+      // K fragments are read two steps ahead of their MFMAs.
+      f32x16 s = {};
+      f32x4 kf0 = *(const f32x4*)(Ks + ln.kq[0]);
+      f32x4 kf1 = *(const f32x4*)(Ks + ln.kq[1]);
+#pragma unroll
+      for (int c = 0; c < 32; ++c) {
+        const f32x4 a = kf0;
+        kf0 = kf1;
+        if (c + 2 < 32) kf1 = *(const f32x4*)(Ks + ln.kq[(c + 2) & 3] + ((c + 2) >> 2) * 128);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], qf[c][e], s, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // lane holds keys k0 + 8(r/4) + 4g + r%4 of its row
+      if (need_mask) {
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int kk = 8 * r4 + 4 * g;
+          int4 ids = {0, 0, 0, 0};
+          if (!seg_full) ids = *(const int4*)(sm.segk[st] + kk);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int64_t key = k0 + kk + e;
+            bool vis = key < p.Lk;
+            if (p.causal) vis = vis && key <= p.q_offset + row;
+            const int id = e == 0 ? ids.x : e == 1 ? ids.y : e == 2 ? ids.z : ids.w;
+            if (!seg_full) vis = vis && id == sq;
+            s[4 * r4 + e] = vis ? s[4 * r4 + e] : -INFINITY;
+          }
+        }
+      }
+      float mx = s[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+      mx = xor32_max(mx);
+      const float mxs = mx * sl2;
+      if (__builtin_amdgcn_ballot_w64(mxs > m_run + kLazyF)) {
+        const float m_new = fmaxf(m_run, mxs);
+        const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
+#pragma unroll
+        for (int n = 0; n < 8; ++n) acc[n] *= alpha;
+        l_part *= alpha;
+        m_run = m_new;
+      }
+      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+      float pr[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        pr[r] = fast_exp2(fmaf(s[r], sl2, -m_use));
+        l_part += pr[r];
+      }
+      // O^T += V^T P^T: MFMA tt contracts key 8(tt/4) + 4g + tt%4 (P register tt).
+      // The 8 V values of key step tt (one per d block) are read one step ahead.
+      float vcur[8], vnxt[8];
+#pragma unroll
+      for (int n = 0; n < 8; ++n) vcur[n] = *(const float*)(Vs + ln.vq[0] + n * 128);
+#pragma unroll
+      for (int tt = 0; tt < 16; ++tt) {
+        if (tt + 1 < 16) {
+          const int u = tt + 1;
+#pragma unroll
+          for (int n = 0; n < 8; ++n) vnxt[n] = *(const float*)(Vs + ln.vq[u & 3] + (u >> 2) * 8192 + n * 128);
+        }
+#pragma unroll
+        for (int n = 0; n < 8; ++n) acc[n] = __builtin_amdgcn_mfma_f32_32x32x2f32(vcur[n], pr[tt], acc[n], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int n = 0; n < 8; ++n) vcur[n] = vnxt[n];
+      }
+    }
+    t = tn;
+    st ^= 1;
+  }
+
+  const float l_tot = xor32_sum(l_part);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (row < p.Lq) {
+    float* op = (float*)p.o + (hq + row) * kD;
+#pragma unroll
+    for (int n = 0; n < 8; ++n)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d0 = 32 * n + 8 * r4 + 4 * g;
+        *(f32x4*)(op + d0) = f32x4{acc[n][4 * r4] * inv, acc[n][4 * r4 + 1] * inv, acc[n][4 * r4 + 2] * inv,
+                                   acc[n][4 * r4 + 3] * inv};
+      }
+    if (g == 0) {
+      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+      p.lse[hq + row] = l_tot > 0.f ? (m_use + log2f(l_tot)) * 0.69314718055994530942f : -INFINITY;
+    }
+  }
+}
+
+}  // namespace gqa

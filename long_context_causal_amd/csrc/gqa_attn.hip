@@ -1,0 +1,118 @@
+// gqa_attn.hip -- host side of libgqa_attn.so: argument checks, launch plan
+// and kernel launches behind the C ABI declared in include/gqa_attn.h.
+#include "gqa_attn.h"
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "common.hpp"
+#include "fwd_bf16.hpp"
+#include "fwd_f32.hpp"
+#include "merge.hpp"
+
+namespace {
+
+constexpr int kWavesBf16 = 4;  // 256 threads, one wave per SIMD
+constexpr int kWavesF32 = 4;   // 256 threads, one wave per SIMD
+
+bool misaligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) != 0; }
+
+// [lo, lo + n) and [lo2, lo2 + n2) overlap?
+bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + (uintptr_t)nb && y < x + (uintptr_t)na;
+}
+
+bool is_pow2_rep(int64_t r) { return r == 1 || r == 2 || r == 4 || r == 8 || r == 16; }
+
+}  // namespace
+
+extern "C" int gqa_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
+                            int64_t q_offset, const int32_t* seg_q, const int32_t* seg_k,
+                            int causal, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse) return GQA_ERR_NULL;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Lq <= 0 || Lk <= 0 || D <= 0) return GQA_ERR_SHAPE;
+  if (Hq % Hkv != 0 || q_offset < 0 || q_offset > ((int64_t)1 << 62)) return GQA_ERR_SHAPE;
+  if ((seg_q == nullptr) != (seg_k == nullptr)) return GQA_ERR_SHAPE;
+  if (D != gqa::kD || (dtype != GQA_F32 && dtype != GQA_BF16)) return GQA_ERR_UNSUPPORTED;
+  const int64_t n_rep = Hq / Hkv;
+  if (!is_pow2_rep(n_rep) || Lq >= ((int64_t)1 << 31) || Lk >= ((int64_t)1 << 31) || B * Hkv >= ((int64_t)1 << 24))
+    return GQA_ERR_UNSUPPORTED;
+  if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16) || misaligned(lse, 4) ||
+      misaligned(seg_q, 4) || misaligned(seg_k, 4))
+    return GQA_ERR_ALIGN;
+  const int64_t es = dtype == GQA_F32 ? 4 : 2;
+  const int64_t qo_bytes = B * Hq * Lq * D * es, kv_bytes = B * Hkv * Lk * D * es, lse_bytes = B * Hq * Lq * 4;
+  if (overlap(o, qo_bytes, q, qo_bytes) || overlap(o, qo_bytes, k, kv_bytes) || overlap(o, qo_bytes, v, kv_bytes) ||
+      overlap(lse, lse_bytes, o, qo_bytes) || overlap(lse, lse_bytes, q, qo_bytes) ||
+      overlap(lse, lse_bytes, k, kv_bytes) || overlap(lse, lse_bytes, v, kv_bytes))
+    return GQA_ERR_ALIAS;
+
+  const int W = dtype == GQA_F32 ? kWavesF32 : kWavesBf16;
+  gqa::FwdParams p;
+  p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
+  p.seg_q = seg_q; p.seg_k = seg_k;
+  p.Lq = Lq; p.Lk = Lk; p.q_offset = q_offset;
+  p.Hq = (int)Hq; p.Hkv = (int)Hkv; p.n_rep = (int)n_rep;
+  p.hpc = (int)(n_rep < W ? n_rep : W);
+  p.ppc = (W / p.hpc) * (dtype == GQA_F32 ? gqa::kRowsPerWave : 32 * gqa::kBlocksB);
+  const int64_t n_qb = (Lq + p.ppc - 1) / p.ppc;
+  const int64_t G = B * Hkv * (n_rep / p.hpc);
+  if (n_qb * G >= ((int64_t)1 << 31)) return GQA_ERR_UNSUPPORTED;
+  p.n_qb = (int)n_qb;
+  p.G = (int)G;
+  p.causal = causal ? 1 : 0;
+  p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
+
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
+  const dim3 grid((unsigned)(n_qb * G));
+  if (dtype == GQA_F32)
+    hipLaunchKernelGGL(gqa::fwd_f32_kernel<kWavesF32>, grid, dim3(kWavesF32 * 64), 0, s, p);
+  else
+    hipLaunchKernelGGL((gqa::fwd_bf16_kernel<kWavesBf16, gqa::kBlocksB>), grid, dim3(kWavesBf16 * 64), 0, s, p);
+  return hipGetLastError() == hipSuccess ? GQA_OK : GQA_ERR_LAUNCH;
+}
+
+extern "C" int gqa_attn_merge(const void* o1, const float* lse1, const void* o2, const float* lse2,
+                              void* o, float* lse, int64_t rows, int64_t D, int dtype, void* stream) {
+  if (!o1 || !lse1 || !o2 || !lse2 || !o || !lse) return GQA_ERR_NULL;
+  if (rows <= 0 || D <= 0) return GQA_ERR_SHAPE;
+  if (D % 8 != 0 || (dtype != GQA_F32 && dtype != GQA_BF16) || rows >= ((int64_t)1 << 33)) return GQA_ERR_UNSUPPORTED;
+  if (misaligned(o1, 16) || misaligned(o2, 16) || misaligned(o, 16) || misaligned(lse1, 4) ||
+      misaligned(lse2, 4) || misaligned(lse, 4))
+    return GQA_ERR_ALIGN;
+  const int64_t ob = rows * D * (dtype == GQA_F32 ? 4 : 2), lb = rows * 4;
+  // outputs may be exactly an input (in place) but must not partially overlap one
+  if ((o != o1 && overlap(o, ob, o1, ob)) || (o != o2 && overlap(o, ob, o2, ob)) ||
+      (lse != lse1 && overlap(lse, lb, lse1, lb)) || (lse != lse2 && overlap(lse, lb, lse2, lb)) ||
+      overlap(o, ob, lse, lb) || overlap(o, ob, lse1, lb) || overlap(o, ob, lse2, lb))
+    return GQA_ERR_ALIAS;
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
+  const dim3 grid((unsigned)((rows + 3) / 4));
+  if (dtype == GQA_F32)
+    hipLaunchKernelGGL(gqa::merge_kernel<float>, grid, dim3(256), 0, s, (const float*)o1, lse1, (const float*)o2,
+                       lse2, (float*)o, lse, rows, D);
+  else
+    hipLaunchKernelGGL(gqa::merge_kernel<__bf16>, grid, dim3(256), 0, s, (const __bf16*)o1, lse1,
+                       (const __bf16*)o2, lse2, (__bf16*)o, lse, rows, D);
+  return hipGetLastError() == hipSuccess ? GQA_OK : GQA_ERR_LAUNCH;
+}
+
+extern "C" const char* gqa_attn_strerror(int code) {
+  switch (code) {
+    case GQA_OK: return "success";
+    case GQA_ERR_NULL: return "a required pointer is NULL";
+    case GQA_ERR_SHAPE: return "invalid shape: non-positive extent, Hq not a multiple of Hkv, negative q_offset, or only one segment-id array";
+    case GQA_ERR_UNSUPPORTED: return "unsupported: D must be 256, dtype F32 or BF16, Hq/Hkv in {1,2,4,8,16}, lengths below 2^31";
+    case GQA_ERR_ALIGN: return "misaligned pointer: tensors need 16-byte alignment, lse and segment ids 4-byte";
+    case GQA_ERR_LAUNCH: return "kernel launch failed";
+    case GQA_ERR_ALIAS: return "output overlaps an input";
+    default: return "unknown status code";
+  }
+}
+
+extern "C" int gqa_attn_version(void) { return (1 << 16) | 0; }

@@ -1,0 +1,77 @@
+// merge.hpp -- log-sum-exp merge of two attention results over disjoint key
+// sets of the same rows (the prefix part and the causal suffix part of a
+// shared-prefix branch). Memory-bound: one wave per row, 16-byte accesses.
+// Each row's lse pair is read by every lane before lane 0 writes the merged
+// lse, so lse may be updated in place; o may be o1 or o2 (each element is read
+// and written by the same lane).
+#pragma once
+#include "common.hpp"
+
+namespace gqa {
+
+template <typename T>
+__device__ __forceinline__ void load8(const T* src, float* x);
+template <>
+__device__ __forceinline__ void load8<float>(const float* src, float* x) {
+  const f32x4 a = *(const f32x4*)src, b = *(const f32x4*)(src + 4);
+  x[0] = a[0]; x[1] = a[1]; x[2] = a[2]; x[3] = a[3];
+  x[4] = b[0]; x[5] = b[1]; x[6] = b[2]; x[7] = b[3];
+}
+template <>
+__device__ __forceinline__ void load8<__bf16>(const __bf16* src, float* x) {
+  const u32x4 u = *(const u32x4*)src;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(u[i] << 16);
+    x[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+  }
+}
+template <typename T>
+__device__ __forceinline__ void store8(T* dst, const float* x);
+template <>
+__device__ __forceinline__ void store8<float>(float* dst, const float* x) {
+  *(f32x4*)dst = f32x4{x[0], x[1], x[2], x[3]};
+  *(f32x4*)(dst + 4) = f32x4{x[4], x[5], x[6], x[7]};
+}
+template <>
+__device__ __forceinline__ void store8<__bf16>(__bf16* dst, const float* x) {
+  u32x4 u;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    typedef __attribute__((ext_vector_type(2))) __bf16 b2;
+    b2 r;
+    r[0] = (__bf16)x[2 * i];
+    r[1] = (__bf16)x[2 * i + 1];
+    u[i] = __builtin_bit_cast(unsigned, r);
+  }
+  *(u32x4*)dst = u;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void merge_kernel(const T* o1, const float* lse1, const T* o2, const float* lse2,
+                                                    T* o, float* lse, int64_t rows, int64_t D) {
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (r >= rows) return;
+  const float a = lse1[r], b = lse2[r];
+  const float M = fmaxf(a, b);
+  float w1 = 0.f, w2 = 0.f, inv = 0.f, out_lse = -INFINITY;
+  if (M != -INFINITY) {
+    w1 = expf(a - M);
+    w2 = expf(b - M);
+    inv = 1.f / (w1 + w2);
+    out_lse = M + logf(w1 + w2);
+  }
+  for (int64_t d = (int64_t)lane * 8; d < D; d += 512) {
+    float x[8], y[8], z[8];
+    load8<T>(o1 + r * D + d, x);
+    load8<T>(o2 + r * D + d, y);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) z[i] = (w1 * x[i] + w2 * y[i]) * inv;
+    store8<T>(o + r * D + d, z);
+  }
+  // every lane of the wave read lse1[r], lse2[r] above, in program order
+  if (lane == 0) lse[r] = out_lse;
+}
+
+}  // namespace gqa

@@ -1,0 +1,91 @@
+"""The C-ABI library on the host: it loads, exports every entry point the header
+declares, and rejects invalid arguments before any HIP call (CPU only; no call
+here reaches a kernel launch)."""
+import os
+import re
+import subprocess
+
+import pytest
+
+import long_context_causal_amd as gqa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gqa_attn.h")
+
+# fake, well-separated, 256-byte-aligned device addresses: never dereferenced
+Q, K, V, O, LSE, SQ, SK = (n << 40 for n in range(1, 8))
+GOOD = dict(q=Q, k=K, v=V, o=O, lse=LSE, B=1, Hq=16, Hkv=4, Lq=512, Lk=512, D=256, q_offset=0,
+            seg_q=None, seg_k=None, causal=1, dtype=gqa.GQA_F32, stream=None)
+
+
+def call(**over):
+    a = dict(GOOD)
+    a.update(over)
+    return gqa.fwd_raw(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["Lq"], a["Lk"],
+                       a["D"], a["q_offset"], a["seg_q"], a["seg_k"], a["causal"], a["dtype"], a["stream"])
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:int|const char\s*\*)\s*(gqa_attn_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert set(names) == set(gqa.EXPORTS)
+    lib = gqa.load_library()
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", gqa.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\sT\s(gqa_attn_\w+)", out))
+    assert set(names) <= exported
+
+
+def test_version_and_strerror():
+    assert gqa.version() == (1, 0)
+    msgs = [gqa.strerror(c) for c in range(7)]
+    assert len(set(msgs)) == 7 and msgs[0] == "success"
+    assert "unknown" in gqa.strerror(99)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(o=None), 1), (dict(lse=None), 1),
+    (dict(B=0), 2), (dict(Hq=0), 2), (dict(Hkv=0), 2), (dict(Lq=0), 2), (dict(Lk=-1), 2), (dict(D=0), 2),
+    (dict(Hq=16, Hkv=3), 2), (dict(q_offset=-1), 2), (dict(seg_q=SQ), 2), (dict(seg_k=SK), 2),
+    (dict(D=128), 3), (dict(dtype=2), 3), (dict(Hq=12, Hkv=4), 3), (dict(Hq=32, Hkv=1), 3),
+    (dict(Lq=1 << 31), 3), (dict(Lk=1 << 31), 3),
+    (dict(q=Q + 2), 4), (dict(k=K + 8), 4), (dict(v=V + 4), 4), (dict(o=O + 2), 4), (dict(lse=LSE + 2), 4),
+    (dict(seg_q=SQ + 2, seg_k=SK), 4),
+    (dict(o=Q + 4096), 6), (dict(o=K), 6), (dict(lse=O + 64), 6), (dict(lse=V), 6),
+])
+def test_fwd_rejects_before_launch(over, code):
+    assert call(**over) == code
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(o1=None), 1), (dict(lse=None), 1), (dict(rows=0), 2), (dict(D=0), 2), (dict(D=12), 3),
+    (dict(dtype=5), 3), (dict(o1=O + 8), 4), (dict(lse2=LSE + 2), 4), (dict(o=Q + 16), 6),
+    (dict(lse=SQ + 4), 6), (dict(o=K + 512), 6),
+])
+def test_merge_rejects_before_launch(over, code):
+    a = dict(o1=Q, lse1=SQ, o2=K, lse2=SK, o=O, lse=LSE, rows=100, D=256, dtype=gqa.GQA_F32, stream=None)
+    a.update(over)
+    assert gqa.merge_raw(a["o1"], a["lse1"], a["o2"], a["lse2"], a["o"], a["lse"], a["rows"], a["D"],
+                         a["dtype"], a["stream"]) == code
+
+
+def test_python_binding_rejects_host_tensors():
+    import torch
+    q = torch.zeros(1, 16, 8, 256)
+    k = torch.zeros(1, 4, 8, 256)
+    with pytest.raises(ValueError):
+        gqa.fwd(q, k, k)
+
+
+def test_product_path_does_not_import_the_oracle():
+    pkg = os.path.join(ROOT, "long_context_causal_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "oracle_attn" not in text, f

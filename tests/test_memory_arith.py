@@ -50,3 +50,19 @@ def test_visible_pair_count_closed_forms():
     lens = [3, 10, 6]
     seg = np.repeat(np.arange(3), lens)
     assert oracle.visible_pairs(19, 19, seg_q=seg, seg_k=seg) == sum(n * (n + 1) // 2 for n in lens)
+
+
+def test_product_pair_count_matches_the_oracle_definition():
+    """The benchmark's FLOP accounting (package-side, fast) agrees with the
+    oracle's dense-mask count on small cases."""
+    from long_context_causal_amd import work
+    rng = np.random.default_rng(3)
+    cases = [dict(Lq=37, Lk=37), dict(Lq=20, Lk=50, q_offset=30), dict(Lq=25, Lk=40, causal=False)]
+    seg = np.sort(rng.integers(0, 4, size=60)).astype(np.int32)
+    cases.append(dict(Lq=60, Lk=60, seg_q=seg, seg_k=seg))
+    cases.append(dict(Lq=60, Lk=60, seg_q=rng.integers(0, 3, 60), seg_k=rng.integers(0, 3, 60), causal=False))
+    cases.append(dict(Lq=60, Lk=70, q_offset=10, seg_q=rng.integers(0, 3, 60), seg_k=rng.integers(0, 3, 70)))
+    for c in cases:
+        c2 = dict(c)
+        Lq, Lk = c2.pop("Lq"), c2.pop("Lk")
+        assert work.visible_pairs(Lq, Lk, **c2) == oracle.visible_pairs(Lq, Lk, **c2), c
