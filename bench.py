@@ -64,8 +64,10 @@ def run_fwd_workload(name, x, steps, warmup, torch, gqa, work, seg=None):
     o = torch.empty_like(q)
     B, Hq, Lq, Dh = q.shape
     lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device)
-    free0, _ = torch.cuda.mem_get_info()
     fn = lambda: gqa.fwd(q, k, v, causal=x.causal, q_offset=x.q_offset, seg_q=sq, seg_k=sk, out=o, lse=lse)
+    fn()  # first launch loads the code object; device memory is compared after it
+    torch.cuda.synchronize()
+    free0, _ = torch.cuda.mem_get_info()
     wall_ms, ev_ms, ev_min, ev_max = time_calls(fn, steps, warmup, torch)
     free1, _ = torch.cuda.mem_get_info()
     peak = torch.cuda.max_memory_allocated() - base
@@ -145,6 +147,68 @@ def cpu_baseline(x, target_s=15.0):
                        "all their visible keys; %.1f s" % (n, L, L, dt))
 
 
+def kernel_source_hash() -> str:
+    """Hash of the HIP sources, so stored counter readings are only used for the
+    kernel build they were taken on."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "long_context_causal_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        h.update(f.encode())
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def pmc_means(db_path):
+    """Mean per-dispatch counter value by (kernel name, counter) from a rocprofv3 database."""
+    import sqlite3
+    from collections import defaultdict
+    con = sqlite3.connect(db_path)
+    acc = defaultdict(list)
+    for name, cname, val in con.execute("select name, counter_name, counter_value from pmc_events"):
+        acc[(name, cname)].append(float(val))
+    return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
+
+
+def pmc_report(fetch_db, write_db, kernel_substr, workload, out_path):
+    """HBM traffic per dispatch of the attention kernel from FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch), each scaled by what the same counter reports
+    for a plain device copy of 1 GiB read + 1 GiB written in the same process."""
+    f, w = pmc_means(fetch_db), pmc_means(write_db)
+
+    def pick(m, sub, counter):
+        hits = [(k, v) for k, v in m.items() if sub in k[0] and k[1] == counter]
+        assert len(hits) == 1, (sub, counter, list(m))
+        return hits[0][1][0], hits[0][0][0]
+
+    fk, kname = pick(f, kernel_substr, "FETCH_SIZE")
+    wk, _ = pick(w, kernel_substr, "WRITE_SIZE")
+    fc, _ = pick(f, "copyBuffer", "FETCH_SIZE")
+    wc, _ = pick(w, "copyBuffer", "WRITE_SIZE")
+    gib = float(1 << 30)
+    fetch_scale, write_scale = gib / (fc * 1024.0), gib / (wc * 1024.0)
+    rec = {"workload": workload, "kernel": kname, "kernel_src_sha": kernel_source_hash(),
+           "fetch_kib_per_dispatch": fk, "write_kib_per_dispatch": wk,
+           "copy_fetch_kib": fc, "copy_write_kib": wc, "fetch_scale": fetch_scale, "write_scale": write_scale,
+           "traffic_bytes": fk * 1024.0 * fetch_scale + wk * 1024.0 * write_scale}
+    with open(out_path, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec))
+
+
+def stored_traffic(workload):
+    """Counter-derived HBM bytes per launch for `workload`, or None if absent or
+    taken on different kernel sources."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    recs = json.load(open(p))
+    rec = recs.get(workload)
+    if rec is None or rec.get("kernel_src_sha") != kernel_source_hash():
+        return None
+    return rec["traffic_bytes"]
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -152,8 +216,24 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--quick", action="store_true", help="primary workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", default=None, help="run one workload: f32-30468, f32-60926, bf16-60926, ...")
+    ap.add_argument("--only", default=None, help="run one workload: f32-15231, f32-30468, f32-60926, bf16-60926")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 1 GiB device copy (3 times) to calibrate HBM byte counters")
+    ap.add_argument("--pmc-report", nargs=4, metavar=("FETCH_DB", "WRITE_DB", "KERNEL_SUBSTR", "WORKLOAD"),
+                    help="turn two rocprofv3 --pmc databases (FETCH_SIZE, WRITE_SIZE) into HBM bytes per "
+                         "dispatch and store them in profiles/traffic.json under WORKLOAD")
     args = ap.parse_args()
+    if args.pmc_report:
+        fdb, wdb, sub, wl = args.pmc_report
+        tmp = os.path.join(ROOT, "profiles", ".traffic_one.json")
+        pmc_report(fdb, wdb, sub, wl, tmp)
+        p = os.path.join(ROOT, "profiles", "traffic.json")
+        recs = json.load(open(p)) if os.path.exists(p) else {}
+        recs[wl] = json.load(open(tmp))
+        os.remove(tmp)
+        with open(p, "w") as fh:
+            json.dump(recs, fh, indent=1, sort_keys=True)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the forward is not sharded across GPUs "
               "(run with --gpus 1)", file=sys.stderr)
@@ -226,11 +306,21 @@ def main():
         "math_path_gib": round(math_gib, 2),
         "library_alloc_bytes": prim["library_alloc_bytes"],
         "roofline": {"bound": "mfma", "achieved": round(prim["kernel_tflops"], 3), "peak": peak_t,
-                     "unit": "TFLOP/s", "frac": round(prim["kernel_tflops"] / peak_t, 4), "traffic": None,
-                     "kernel_ms": round(prim["kernel_ms"], 4)},
+                     "unit": "TFLOP/s", "frac": round(prim["kernel_tflops"] / peak_t, 4),
+                     "traffic": stored_traffic(name), "kernel_ms": round(prim["kernel_ms"], 4),
+                     "algorithmic_bytes": prim["bytes"]},
     }
     if secondary:
         out["secondary"] = [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()} for r in secondary]
+    if args.copy_probe:
+        n = 1 << 28  # 2^28 fp32 = 1 GiB read + 1 GiB written per copy
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_probe_bytes"] = {"read": 4 * n, "written": 4 * n}
+        del src, dst
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(x)
     print(json.dumps(out), flush=True)
