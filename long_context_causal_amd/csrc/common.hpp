@@ -88,13 +88,24 @@ __device__ __forceinline__ int wave_max_i(int x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Async 16-byte (or 4-byte) global -> LDS copy: lane l's bytes land at
-// lds_base + l * size. lds_base must be the same in every lane of the wave.
-__device__ __forceinline__ void g2lds16(const void* src, lds_void* lds_base) {
-  __builtin_amdgcn_global_load_lds(src, lds_base, 16, 0, 0);
+// Async global -> LDS copies (global_load_lds): lane l's 16 (or 4) bytes from
+// gbase + voff land at LDS byte lds + 16 l (or 4 l); gbase and lds must be the
+// same in every lane of the wave. They are issued through inline asm on
+// purpose: the compiler then does not treat them as LDS stores whose
+// completion every later LDS read must wait for, which would serialise the
+// prefetch ring. Completion is ensured by the explicit s_waitcnt vmcnt waits
+// and workgroup barriers of the kernels. The instruction writes no VGPR;
+// M0 (the LDS base) is set in the same asm block, one wait state ahead.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
 }
-__device__ __forceinline__ void g2lds4(const void* src, lds_void* lds_base) {
-  __builtin_amdgcn_global_load_lds(src, lds_base, 4, 0, 0);
+__device__ __forceinline__ void g2lds16(const char* gbase, uint32_t voff, const void* lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(lds_addr(lds)), "v"(voff), "s"(gbase) : "memory");
+}
+__device__ __forceinline__ void g2lds4(const char* gbase, uint32_t voff, const void* lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+               :: "s"(lds_addr(lds)), "v"(voff), "s"(gbase) : "memory");
 }
 __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 

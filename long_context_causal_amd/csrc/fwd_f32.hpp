@@ -73,12 +73,11 @@ __device__ __forceinline__ void load_tile_f(SmemF& sm, int st, const char* kb, c
   for (int it = 0; it < kBkF / W; ++it) {
     const int kk = wave + W * it;
     const uint32_t src = (uint32_t)(kk <= last ? kk : (int)last) * 1024u;
-    g2lds16(kt + src + ln.ld[it & 1], (lds_void*)(sm.k[st] + kk * 1024));
-    g2lds16(vt + src + ln.ld[it & 1], (lds_void*)(sm.v[st] + kk * 1024));
+    g2lds16(kt, src + ln.ld[it & 1], sm.k[st] + kk * 1024);
+    g2lds16(vt, src + ln.ld[it & 1], sm.v[st] + kk * 1024);
   }
   if (skb != nullptr && wave == W - 1 && lane < kBkF) {
-    const int64_t key = min(t * kBkF + lane, Lk - 1);
-    g2lds4(skb + key, (lds_void*)sm.segk[st]);
+    g2lds4((const char*)(skb + t * kBkF), (uint32_t)min((int64_t)lane, last) * 4u, sm.segk[st]);
   }
 }
 

@@ -57,7 +57,7 @@ extern "C" int gqa_attn_fwd(const void* q, const void* k, const void* v, void* o
   p.Lq = Lq; p.Lk = Lk; p.q_offset = q_offset;
   p.Hq = (int)Hq; p.Hkv = (int)Hkv; p.n_rep = (int)n_rep;
   p.hpc = (int)(n_rep < W ? n_rep : W);
-  p.ppc = (W / p.hpc) * (dtype == GQA_F32 ? gqa::kRowsPerWave : 32 * gqa::kBlocksB);
+  p.ppc = (W / p.hpc) * gqa::kRowsPerWave;
   const int64_t n_qb = (Lq + p.ppc - 1) / p.ppc;
   const int64_t G = B * Hkv * (n_rep / p.hpc);
   if (n_qb * G >= ((int64_t)1 << 31)) return GQA_ERR_UNSUPPORTED;
@@ -72,7 +72,7 @@ extern "C" int gqa_attn_fwd(const void* q, const void* k, const void* v, void* o
   if (dtype == GQA_F32)
     hipLaunchKernelGGL(gqa::fwd_f32_kernel<kWavesF32>, grid, dim3(kWavesF32 * 64), 0, s, p);
   else
-    hipLaunchKernelGGL((gqa::fwd_bf16_kernel<kWavesBf16, gqa::kBlocksB>), grid, dim3(kWavesBf16 * 64), 0, s, p);
+    hipLaunchKernelGGL((gqa::fwd_bf16_kernel<kWavesBf16>), grid, dim3(kWavesBf16 * 64), 0, s, p);
   return hipGetLastError() == hipSuccess ? GQA_OK : GQA_ERR_LAUNCH;
 }
 
