@@ -1,23 +1,26 @@
 // fwd_bf16.hpp -- causal grouped-query attention forward, bf16 inputs, fp32
-// accumulation, on gfx950 bf16 MFMA (v_mfma_f32_32x32x16_bf16).
+// accumulation, on gfx950 bf16 MFMA (v_mfma_f32_16x16x32_bf16).
 //
-// One workgroup = 4 waves (one per SIMD). For Hq/Hkv = 4 the workgroup owns
-// the 4 query heads of one KV head x 32 positions; each wave owns one head and
-// 32 query rows. Key tiles of 32 keys flow HBM -> LDS through a 4-stage ring
-// (async global_load_lds, two tiles in flight ahead of use), each tile read by
-// all 4 waves, so every K/V byte fetched serves each query head of the group;
-// K/V are never repeated per head.
+// One workgroup = 8 waves, two per SIMD, so one wave's softmax (VALU) runs
+// while the other wave's products occupy the matrix core. For Hq/Hkv = 4 the
+// workgroup owns the 4 query heads of one KV head x 32 positions; each wave
+// owns one head and 16 query rows (16-row MFMA tiles keep a wave's registers,
+// O^T 64 + Q 32 per lane, within the 256 that two waves per SIMD allow). Key
+// tiles of 32 keys flow HBM -> LDS through a 4-stage ring (async
+// global_load_lds, two tiles in flight ahead of use), each tile read by all 8
+// waves, so every K/V byte fetched serves each query head of the group; K/V
+// are never repeated per head.
 //
-// Per wave and key tile j, software-pipelined:
-//   row max of tile j (one exchange between lanes l and l ^ 32) and the lazy
+// Per wave and key tile j:
+//   row max of tile j (exchanges between lanes l, l ^ 16, l ^ 32) and the lazy
 //      rescale of the running max (it moves only when a row's maximum grows
 //      by more than 8 in log2 units, so O and l are rescaled rarely and
 //      p <= 2^8);
-//   A: S^T(j+1) = K(j+1) Q^T on the matrix core (A operand = K from LDS,
-//      B operand = Q kept in registers; a lane holds one query row, lane % 32,
-//      and 16 of the 32 keys) while the VALU computes P = exp2(...) of tile j
-//      rounded to bf16 (RNE), l from the unrounded p (for lse) and lr from the
-//      rounded P (for O, so O is an exact convex combination of V rows);
+//   A: S^T(j+1) = K(j+1) Q^T (A operand = K from LDS, B operand = Q kept in
+//      registers; a lane holds one query row, lane % 16, and 8 of the 32 keys)
+//      interleaved with P = exp2(...) of tile j rounded to bf16 (RNE), l from
+//      the unrounded p (for lse) and lr from the rounded P (for O, so O is an
+//      exact convex combination of V rows);
 //   B: O^T += V^T P^T (A operand = V^T through the transposing LDS read
 //      ds_read_b64_tr_b16, B operand = P straight from the S^T registers).
 // Masks (diagonal, ragged tail, segment boundaries) are applied only to the
@@ -28,23 +31,25 @@
 
 namespace gqa {
 
-constexpr int kBkB = 32;                    // keys per LDS tile (one MFMA block)
+constexpr int kWavesB = 8;                  // waves per workgroup
+constexpr int kRowsB = 16;                  // query rows per wave
+constexpr int kBkB = 32;                    // keys per LDS tile
 constexpr int kStagesB = 4;                 // LDS ring depth
 constexpr int kTileBytesB = kBkB * kD * 2;  // 16 KB per K or V tile
-constexpr int kLoadsB = 2 * (kTileBytesB / 1024) / 4;  // 16-byte-per-lane copies per wave per tile (4 waves)
 constexpr float kLazy = 8.0f;               // lazy-rescale threshold (log2 units)
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 
 // LDS image of a bf16 tile: 512-byte key rows of 32 16-byte chunks; chunk c of
-// key k is stored at chunk c ^ swz16(k). LDS has 64 banks of 4 bytes; a
-// 16-byte read is served 16 lanes per clock and the transposing 8-byte read 32
-// lanes per clock. swz16 maps any 16 consecutive keys to 16 different values,
-// so the K reads (16 consecutive keys, one column) hit 16 different 16-byte
-// bank groups; within any 4 consecutive keys its top two bits differ, so the
-// transposing V reads (4 keys x 4 chunks per 32 lanes) hit 16 different groups
-// too. Both access patterns are conflict-free.
-__device__ __forceinline__ int swz16(int key) { return ((key & 3) << 2) | ((key >> 2) & 3); }
+// key k is stored at chunk c ^ swz_k(k) in K tiles and c ^ swz_v(k) in V tiles.
+// LDS has 64 banks of 4 bytes. The K reads (16 consecutive keys at one chunk,
+// lanes 16G..16G+15 at chunk 4c + G) are conflict-free with an XOR by k % 16;
+// the transposing V reads (8 keys x one aligned pair of chunks per 32 lanes)
+// are conflict-free with swz_v = 2 (k % 8) + (k / 8) % 2, which sends 8
+// consecutive keys to 8 different chunk pairs. Both swizzles were checked with
+// the SQ_LDS_BANK_CONFLICT counter on gfx950.
+__device__ __forceinline__ int swz_k(int key) { return key & 15; }
+__device__ __forceinline__ int swz_v(int key) { return ((key & 7) << 1) | ((key >> 3) & 1); }
 
 struct SmemB {
   __attribute__((aligned(16))) char k[kStagesB][kTileBytesB];
@@ -63,115 +68,118 @@ __device__ __forceinline__ unsigned pack_bf16(float a, float b) {
 // Per-lane parts of the tile-copy and LDS-read addresses; the rest of each
 // address is uniform or a compile-time immediate.
 struct LanesB {
-  uint32_t ld[2];  // copy: lane's chunk in 1 KB block (2 key rows); block b = wave + 4 it uses ld[it & 1]
-  uint32_t k[8];   // K read of chunk 2c + g, c % 8 = j, key l32: + 256 (c / 8)
-  uint32_t v[8];   // V transposing read, d block n % 4 = j (v[j]) and the keys 8 higher (v[4 + j]): + 256 (n / 4)
+  uint32_t ldk;    // copy: this lane's 16 bytes within a 1 KB block of 2 key rows (K tile)
+  uint32_t ldv;    // the same for the V tile
+  uint32_t k[4];   // K read, d chunk c (32 d each), c % 4 = j, keys 16 b + l16: + 256 (c / 4) + 8192 b
+  uint32_t v[16];  // V read, d block n (16 d), n % 8 = j: v[j] (keys 4G..) and v[8 + j] (keys 16 + 4G..): + 256 (n / 8)
   __device__ __forceinline__ void init(int wave, int lane) {
-    const int l32 = lane & 31, g = lane >> 5, G16 = lane >> 4, i16 = lane & 15;
+    const int l16 = lane & 15, G = lane >> 4, g = lane >> 5;
+    ldk = (uint32_t)g * 512u + ((uint32_t)((lane & 31) ^ swz_k(2 * wave + g)) << 4);
+    ldv = (uint32_t)g * 512u + ((uint32_t)((lane & 31) ^ swz_v(2 * wave + g)) << 4);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int kk = 2 * wave + 8 * j + g;  // key row of this lane's copy (mod 16 is what matters)
-      ld[j] = (uint32_t)g * 512u + ((uint32_t)((lane & 31) ^ swz16(kk)) << 4);
-    }
+    for (int j = 0; j < 4; ++j) k[j] = (uint32_t)l16 * 512u + ((uint32_t)((4 * j + G) ^ swz_k(l16)) << 4);
+    const int kr = 4 * G + (l16 >> 2);               // key of this lane's copy within a 16-key block
+    const int h = (l16 & 3) >> 1;                     // 16-byte chunk within the 32 bytes of a d block
+    const uint32_t in = (uint32_t)(l16 & 1) << 3;     // 8-byte half of the chunk
 #pragma unroll
-    for (int j = 0; j < 8; ++j) k[j] = (uint32_t)l32 * 512u + ((uint32_t)((2 * j + g) ^ swz16(l32)) << 4);
-    const int kk0 = 4 * (G16 >> 1) + (i16 >> 2);           // key within a 16-key chunk (0..7)
-    const int z = 2 * (G16 & 1) + ((i16 & 3) >> 1);         // 16-byte chunk within a 32-d block (0..3)
-    const uint32_t in = (uint32_t)(i16 & 1) << 3;           // 8-byte half of the chunk
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      v[j] = (uint32_t)kk0 * 512u + ((uint32_t)((4 * j + z) ^ swz16(kk0)) << 4) + in;
-      v[4 + j] = (uint32_t)(kk0 + 8) * 512u + ((uint32_t)((4 * j + z) ^ swz16(kk0 + 8)) << 4) + in;
+    for (int j = 0; j < 8; ++j) {
+      v[j] = (uint32_t)kr * 512u + ((uint32_t)((2 * j + h) ^ swz_v(kr)) << 4) + in;
+      v[8 + j] = (uint32_t)(kr + 16) * 512u + ((uint32_t)((2 * j + h) ^ swz_v(kr + 16)) << 4) + in;
     }
   }
 };
 
 // Async copy of key tile t (keys 32t .. 32t+31) of K, V and the key segment
-// ids into LDS stage `st`. Wave w copies the 1 KB blocks w, w+4, w+8, w+12
-// (2 key rows each) of K and of V. Keys past Lk re-read row Lk-1 (finite data
-// that the mask removes), so no read leaves the tensors.
+// ids into LDS stage `st`. Wave w copies the 1 KB blocks w and w + 8 (2 key
+// rows each) of K and of V. Keys past Lk re-read row Lk-1 (finite data that
+// the mask removes), so no read leaves the tensors.
 __device__ __forceinline__ void load_tile_b(SmemB& sm, int st, const char* kb, const char* vb, const int32_t* skb,
                                             int64_t t, int64_t Lk, int wave, int lane, const LanesB& ln) {
   const char* kt = kb + t * kTileBytesB;
   const char* vt = vb + t * kTileBytesB;
-  if ((t + 1) * kBkB <= Lk) {
+  const int last = (int)min((int64_t)(kBkB - 1), Lk - 1 - t * kBkB);  // last valid key within the tile
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int blk = wave + 4 * it;
-      const uint32_t off = ln.ld[it & 1] + (uint32_t)blk * 1024u;
-      g2lds16(kt, off, sm.k[st] + blk * 1024);
-      g2lds16(vt, off, sm.v[st] + blk * 1024);
+  for (int it = 0; it < 2; ++it) {
+    const int blk = wave + kWavesB * it;
+    uint32_t offk = ln.ldk + (uint32_t)blk * 1024u, offv = ln.ldv + (uint32_t)blk * 1024u;
+    if (last < kBkB - 1) {
+      const int kk = (int)(offk >> 9);  // the same key row for both
+      if (kk > last) {
+        offk = ((uint32_t)last << 9) | (offk & 511u);
+        offv = ((uint32_t)last << 9) | (offv & 511u);
+      }
     }
-  } else {
-    const int last = (int)(Lk - 1 - t * kBkB);  // last valid key within the tile
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int blk = wave + 4 * it;
-      const uint32_t off = ln.ld[it & 1] + (uint32_t)blk * 1024u;
-      const int kk = (int)(off >> 9);
-      const uint32_t src = kk <= last ? off : ((uint32_t)last << 9) | (off & 511u);
-      g2lds16(kt, src, sm.k[st] + blk * 1024);
-      g2lds16(vt, src, sm.v[st] + blk * 1024);
-    }
+    g2lds16(kt, offk, sm.k[st] + blk * 1024);
+    g2lds16(vt, offv, sm.v[st] + blk * 1024);
   }
-  if (skb != nullptr && wave == 3 && lane < kBkB) {
-    const int64_t last = Lk - 1 - t * kBkB;
-    g2lds4((const char*)(skb + t * kBkB), (uint32_t)min((int64_t)lane, last) * 4u, sm.segk[st]);
+  if (skb != nullptr && wave == kWavesB - 1 && lane < kBkB)
+    g2lds4((const char*)(skb + t * kBkB), (uint32_t)min(lane, last) * 4u, sm.segk[st]);
+}
+
+// S^T = K Q^T for the tile in LDS at Ks: two 16-key blocks, each 8 MFMAs over
+// D = 256; K fragments read three MFMAs ahead.
+__device__ __forceinline__ void qk_tile(const char* Ks, const bf16x8* qf, const LanesB& ln, f32x4* s) {
+  s[0] = f32x4{};
+  s[1] = f32x4{};
+  bf16x8 kf[3];
+#pragma unroll
+  for (int m = 0; m < 3; ++m) kf[m] = *(const bf16x8*)(Ks + (m >> 3) * 8192 + ln.k[m & 3] + ((m & 7) >> 2) * 256);
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {  // m = 8 b + c
+    s[m >> 3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[m % 3], qf[m & 7], s[m >> 3], 0, 0, 0);
+    const int u = m + 3;
+    if (u < 16) kf[m % 3] = *(const bf16x8*)(Ks + (u >> 3) * 8192 + ln.k[u & 3] + ((u & 7) >> 2) * 256);
   }
 }
 
-// S^T = K Q^T for the tile in LDS at Ks (32 keys x 256 d), K fragments read
-// four MFMAs ahead.
-__device__ __forceinline__ f32x16 qk_tile(const char* Ks, const bf16x8* qf, const LanesB& ln) {
-  f32x16 s = {};
-  bf16x8 kf[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) kf[c] = *(const bf16x8*)(Ks + ln.k[c & 7] + (c >> 3) * 256);
-#pragma unroll
-  for (int c = 0; c < 16; ++c) {
-    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[c & 3], qf[c], s, 0, 0, 0);
-    if (c + 4 < 16) kf[c & 3] = *(const bf16x8*)(Ks + ln.k[(c + 4) & 7] + ((c + 4) >> 3) * 256);
-  }
-  return s;
-}
-
-// Element mask of one tile: lane holds keys key0 + 8(r/4) + 4g + r%4 of row `row`.
-__device__ __forceinline__ void mask_tile(f32x16& s, int64_t key0, int g, int64_t Lk, int causal, int64_t lim,
+// Element mask of one tile: lane holds keys key0 + 16 b + 4G + r (s[b][r]) of row `row`.
+__device__ __forceinline__ void mask_tile(f32x4* s, int64_t key0, int G, int64_t Lk, int causal, int64_t lim,
                                           bool seg_elem, const int* segk, int sq) {
 #pragma unroll
-  for (int r4 = 0; r4 < 4; ++r4) {
-    const int kk = 8 * r4 + 4 * g;
+  for (int b = 0; b < 2; ++b) {
+    const int kk = 16 * b + 4 * G;
     int4 ids = {0, 0, 0, 0};
     if (seg_elem) ids = *(const int4*)(segk + kk);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int64_t key = key0 + kk + e;
+    for (int r = 0; r < 4; ++r) {
+      const int64_t key = key0 + kk + r;
       bool vis = key < Lk;
       if (causal) vis = vis && key <= lim;
-      const int id = e == 0 ? ids.x : e == 1 ? ids.y : e == 2 ? ids.z : ids.w;
+      const int id = r == 0 ? ids.x : r == 1 ? ids.y : r == 2 ? ids.z : ids.w;
       if (seg_elem) vis = vis && id == sq;
-      s[4 * r4 + e] = vis ? s[4 * r4 + e] : -INFINITY;
+      s[b][r] = vis ? s[b][r] : -INFINITY;
     }
   }
 }
 
-// Online-softmax state of the wave's 32 rows (per lane: its row). l sums the
+// max over the 4 lanes l, l ^ 16, l ^ 32, l ^ 48 that share a query row
+__device__ __forceinline__ float row_max4(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return xor32_max(x);
+}
+__device__ __forceinline__ float row_sum4(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  return xor32_sum(x);
+}
+
+// Online-softmax state of the wave's rows (per lane: its row). l sums the
 // unrounded p (for lse), lr the bf16-rounded P that the PV product uses.
 struct RowState {
   float m;   // running max, base-2 scaled domain (-inf before any visible key)
-  float l;   // this lane's partial sum of p (its 16 of every 32 keys)
+  float l;   // this lane's partial sum of p (its 8 of every 32 keys)
   float lr;  // the same over the rounded P
 };
 
-// Softmax, first part: row max (one exchange between lanes l and l ^ 32) and
-// the lazy update of the running max. Returns the per-lane rescale factor
-// alpha (1 where the lane's max did not move) and sets m_use for the exps.
-__device__ __forceinline__ float softmax_max(const f32x16& s, RowState& rs, float sl2, float& m_use) {
-  float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);
-#pragma unroll
-  for (int r = 3; r < 15; r += 2) mx = fmaxf(fmaxf(mx, s[r]), s[r + 1]);
-  mx = fmaxf(mx, s[15]);
-  mx = xor32_max(mx);
+// Softmax, first part: row max and the lazy update of the running max.
+// Returns the per-lane rescale factor alpha (1 where the max did not move).
+__device__ __forceinline__ float softmax_max(const f32x4* s, RowState& rs, float sl2, float& m_use) {
+  float mx = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
+  mx = fmaxf(fmaxf(mx, s[0][3]), s[1][0]);
+  mx = fmaxf(fmaxf(mx, s[1][1]), s[1][2]);
+  mx = fmaxf(mx, s[1][3]);
+  mx = row_max4(mx);
   const float mxs = mx * sl2;
   const bool need = mxs > rs.m + kLazy;
   const float m_new = need ? mxs : rs.m;
@@ -181,16 +189,16 @@ __device__ __forceinline__ float softmax_max(const f32x16& s, RowState& rs, floa
   return alpha;
 }
 
-// Softmax, second part (no branches): P = exp2(s * scale - m) rounded to bf16
-// pairs, and the row sums of the unrounded and of the rounded values.
-__device__ __forceinline__ void softmax_exp(const f32x16& s, RowState& rs, unsigned* pk, float sl2, float m_use,
+// Softmax, second part: P = exp2(s * scale - m) as bf16 pairs in the order of
+// the PV B operand (keys 4G..4G+3 of block 0, then of block 1) and the row sums.
+__device__ __forceinline__ void softmax_exp(const f32x4* s, RowState& rs, unsigned* pk, float sl2, float m_use,
                                             float alpha) {
   float lsum = 0.f, lrsum = 0.f;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float a = fast_exp2(fmaf(s[2 * i], sl2, -m_use));
-    const float b = fast_exp2(fmaf(s[2 * i + 1], sl2, -m_use));
+  for (int i = 0; i < 4; ++i) {
+    const float a = fast_exp2(fmaf(s[i >> 1][2 * (i & 1)], sl2, -m_use));
+    const float b = fast_exp2(fmaf(s[i >> 1][2 * (i & 1) + 1], sl2, -m_use));
     pk[i] = pack_bf16(a, b);
     lsum += a + b;
     lrsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[i]), ones, lrsum, false);
@@ -199,59 +207,55 @@ __device__ __forceinline__ void softmax_exp(const f32x16& s, RowState& rs, unsig
   rs.lr = fmaf(rs.lr, alpha, lrsum);
 }
 
-// V^T fragment m of a tile (16-key chunk m / 8, d block m % 8): two
-// transposing reads of 4 bf16 each.
-__device__ __forceinline__ bf16x8 v_frag(const char* Vs, int m, const LanesB& ln) {
-  const char* Vc = Vs + 16 * (m >> 3) * 512;
-  const int n = m & 7;
+// V^T fragment for d block n (16 d): keys 4G..4G+3 and 16+4G..16+4G+3.
+__device__ __forceinline__ bf16x8 v_frag(const char* Vs, int n, const LanesB& ln) {
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4*)(Vc + ln.v[n & 3] + (n >> 2) * 256));
+      (__attribute__((address_space(3))) s16x4*)(Vs + ln.v[n & 7] + (n >> 3) * 256));
   const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4*)(Vc + ln.v[4 + (n & 3)] + (n >> 2) * 256));
+      (__attribute__((address_space(3))) s16x4*)(Vs + ln.v[8 + (n & 7)] + (n >> 3) * 256));
   const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
   return __builtin_bit_cast(bf16x8, u32x4{lo2[0], lo2[1], hi2[0], hi2[1]});
 }
 
-// O^T += V^T P^T for the tile in LDS at Vs, V fragments read three MFMAs ahead.
-__device__ __forceinline__ void pv_tile(f32x16* acc, const char* Vs, const unsigned* pk, const LanesB& ln) {
-  const bf16x8 pf0 = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
-  const bf16x8 pf1 = __builtin_bit_cast(bf16x8, u32x4{pk[4], pk[5], pk[6], pk[7]});
+// O^T += V^T P^T for the tile in LDS at Vs: 16 d blocks, V fragments read
+// three MFMAs ahead.
+__device__ __forceinline__ void pv_tile(f32x4* acc, const char* Vs, const unsigned* pk, const LanesB& ln) {
+  const bf16x8 pf = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
   bf16x8 vf[3];
 #pragma unroll
-  for (int m = 0; m < 3; ++m) vf[m] = v_frag(Vs, m, ln);
+  for (int n = 0; n < 3; ++n) vf[n] = v_frag(Vs, n, ln);
 #pragma unroll
-  for (int m = 0; m < 16; ++m) {
-    acc[m & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[m % 3], m < 8 ? pf0 : pf1, acc[m & 7], 0, 0, 0);
-    if (m + 3 < 16) vf[m % 3] = v_frag(Vs, m + 3, ln);
+  for (int n = 0; n < 16; ++n) {
+    acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[n % 3], pf, acc[n], 0, 0, 0);
+    if (n + 3 < 16) vf[n % 3] = v_frag(Vs, n + 3, ln);
   }
 }
 
-__device__ __forceinline__ void rescale_if_needed(f32x16* acc, float alpha) {
+__device__ __forceinline__ void rescale_if_needed(f32x4* acc, float alpha) {
   if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
 #pragma unroll
-    for (int n = 0; n < 8; ++n) acc[n] *= alpha;
+    for (int n = 0; n < 16; ++n) acc[n] *= alpha;
   }
 }
 
-// Wait until at most `n` of this wave's async copies are outstanding (copies
-// complete in issue order); n is 0, 1 or 2 tiles' worth.
+// Wait until at most `n` tiles' worth (4 copies per wave per tile) of this
+// wave's async copies are outstanding (copies complete in issue order).
 __device__ __forceinline__ void wait_tiles(int tiles_outstanding) {
-  if (tiles_outstanding >= 2) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-  else if (tiles_outstanding == 1) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  if (tiles_outstanding >= 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else if (tiles_outstanding == 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
   else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
-static_assert(kLoadsB == 8, "wait_tiles assumes 8 copies per wave per tile");
 
 template <int W>
 __global__ __launch_bounds__(W * 64) void fwd_bf16_kernel(FwdParams p) {
-  static_assert(W == 4, "the copy pattern assumes 4 waves");
+  static_assert(W == kWavesB, "the copy pattern assumes 8 waves");
   __shared__ SmemB sm;
   const Work w = decode_work(p);
   const int wave = wave_id(), lane = lane_id();
-  const int l32 = lane & 31, g = lane >> 5;
+  const int l16 = lane & 15, G = lane >> 4;
   const int h = w.h0 + wave % p.hpc;
-  const int64_t pw = w.p0 + (int64_t)(wave / p.hpc) * kRowsPerWave;  // first row of this wave
-  const int64_t row = pw + l32;
+  const int64_t pw = w.p0 + (int64_t)(wave / p.hpc) * kRowsB;  // first row of this wave
+  const int64_t row = pw + l16;
   const int64_t row_c = min(row, p.Lq - 1);
 
   const int64_t p_end = min(w.p0 + (int64_t)p.ppc, p.Lq);
@@ -269,38 +273,34 @@ __global__ __launch_bounds__(W * 64) void fwd_bf16_kernel(FwdParams p) {
   const int sq = seg ? p.seg_q[(int64_t)w.b * p.Lq + row_c] : 0;
   const int64_t lim = p.q_offset + row;  // last key this row may see (causal)
 
-  // Q in registers, B-operand layout: lane holds Q[row][16c + 8g .. 16c + 8g + 7].
+  // Q in registers, B-operand layout: lane holds Q[row][32c + 8G .. 32c + 8G + 7].
   const int64_t hq = ((int64_t)w.b * p.Hq + h) * p.Lq;
-  bf16x8 qf[16];
+  bf16x8 qf[8];
   {
     const bf16x8* qr = (const bf16x8*)((const char*)p.q + (hq + row_c) * kD * 2);
 #pragma unroll
-    for (int c = 0; c < 16; ++c) qf[c] = qr[2 * c + g];
+    for (int c = 0; c < 8; ++c) qf[c] = qr[4 * c + G];
   }
 
-  f32x16 acc[8];
+  f32x4 acc[16];
 #pragma unroll
-  for (int n = 0; n < 8; ++n) acc[n] = f32x16{};
+  for (int n = 0; n < 16; ++n) acc[n] = f32x4{};
   RowState rs = {-INFINITY, 0.f, 0.f};
   const float sl2 = p.scale_log2;
   LanesB ln;
   ln.init(wave, lane);
 
-  // which tiles of this wave's rows need an element mask
+  auto full_bit = [&](int t) -> bool { return use_bits && ((sm.bits.full[t >> 5] >> (t & 31)) & 1u); };
   auto needs_mask = [&](int t) -> bool {
     const int64_t k0 = (int64_t)t * kBkB;
-    const bool seg_full = !seg || (use_bits && ((sm.bits.full[t >> 5] >> (t & 31)) & 1u));
-    return !seg_full || k0 + kBkB > p.Lk || (p.causal && k0 + kBkB - 1 > p.q_offset + pw);
-  };
-  auto seg_elem = [&](int t) -> bool {
-    return seg && !(use_bits && ((sm.bits.full[t >> 5] >> (t & 31)) & 1u));
+    return (seg && !full_bit(t)) || k0 + kBkB > p.Lk || (p.causal && k0 + kBkB - 1 > p.q_offset + pw);
   };
   auto next_tile = [&](int t) -> int {
     if (t >= n_tiles) return n_tiles;
     return use_bits ? seg_next(sm.bits, t + 1, n_tiles) : t + 1;
   };
 
-  // visible tiles in order: cur (being finished), nxt (QK this iteration), nn, n3 (in flight)
+  // visible tiles in order: cur (being finished), nxt (QK this iteration), nn and n3 (in flight)
   int cur = use_bits ? seg_next(sm.bits, 0, n_tiles) : 0;
   if (cur < n_tiles) {
     int nxt = next_tile(cur), nn = next_tile(nxt);
@@ -309,8 +309,9 @@ __global__ __launch_bounds__(W * 64) void fwd_bf16_kernel(FwdParams p) {
     if (nn < n_tiles) load_tile_b(sm, 2, kb, vb, skb, nn, p.Lk, wave, lane, ln);
     wait_tiles((nxt < n_tiles) + (nn < n_tiles));
     __syncthreads();
-    f32x16 s_cur = qk_tile(sm.k[0], qf, ln);
-    if (needs_mask(cur)) mask_tile(s_cur, (int64_t)cur * kBkB, g, p.Lk, p.causal, lim, seg_elem(cur), sm.segk[0], sq);
+    f32x4 s_cur[2];
+    qk_tile(sm.k[0], qf, ln, s_cur);
+    if (needs_mask(cur)) mask_tile(s_cur, (int64_t)cur * kBkB, G, p.Lk, p.causal, lim, seg && !full_bit(cur), sm.segk[0], sq);
     int i = 0;  // ring position of `cur`
     while (nxt < n_tiles) {
       wait_tiles(nn < n_tiles);  // tile nxt has landed (nn may still be in flight)
@@ -318,25 +319,20 @@ __global__ __launch_bounds__(W * 64) void fwd_bf16_kernel(FwdParams p) {
       const int n3 = next_tile(nn);
       if (n3 < n_tiles) load_tile_b(sm, (i + 3) & 3, kb, vb, skb, n3, p.Lk, wave, lane, ln);
       const int s1 = (i + 1) & 3;
-      // softmax max of this tile and the (rare) rescale of O, ahead of the overlapped block
       float m_use;
       const float alpha = softmax_max(s_cur, rs, sl2, m_use);
       rescale_if_needed(acc, alpha);
-      // A: QK of the next tile on the matrix core while the VALU runs this tile's exps
-      unsigned pk[8];
-      f32x16 s_nxt = qk_tile(sm.k[s1], qf, ln);
+      // A: QK of the next tile interleaved with this tile's exps
+      unsigned pk[4];
+      f32x4 s_nxt[2];
+      qk_tile(sm.k[s1], qf, ln, s_nxt);
       softmax_exp(s_cur, rs, pk, sl2, m_use, alpha);
-#pragma unroll
-      for (int c = 0; c < 16; ++c) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // 4 VALU
-      }
       // B: PV of this tile
       pv_tile(acc, sm.v[i & 3], pk, ln);
       if (needs_mask(nxt))
-        mask_tile(s_nxt, (int64_t)nxt * kBkB, g, p.Lk, p.causal, lim, seg_elem(nxt), sm.segk[s1], sq);
-      s_cur = s_nxt;
+        mask_tile(s_nxt, (int64_t)nxt * kBkB, G, p.Lk, p.causal, lim, seg && !full_bit(nxt), sm.segk[s1], sq);
+      s_cur[0] = s_nxt[0];
+      s_cur[1] = s_nxt[1];
       cur = nxt;
       nxt = nn;
       nn = n3;
@@ -345,33 +341,26 @@ __global__ __launch_bounds__(W * 64) void fwd_bf16_kernel(FwdParams p) {
     float m_use;
     const float alpha = softmax_max(s_cur, rs, sl2, m_use);
     rescale_if_needed(acc, alpha);
-    unsigned pk[8];
+    unsigned pk[4];
     softmax_exp(s_cur, rs, pk, sl2, m_use, alpha);
     pv_tile(acc, sm.v[i & 3], pk, ln);
   }
 
-  // epilogue: O = acc / lr (bf16), lse = ln2 (m + log2 l)
+  // epilogue: O = acc / lr (bf16), lse = ln2 (m + log2 l); lane holds O[row][16 n + 4G + r]
+  const float l_tot = row_sum4(rs.l);
+  const float lr_tot = row_sum4(rs.lr);
   if (row < p.Lq) {
-    const float l_tot = xor32_sum(rs.l);
-    const float lr_tot = xor32_sum(rs.lr);
     const float inv = lr_tot > 0.f ? 1.f / lr_tot : 0.f;
     char* op = (char*)p.o + (hq + row) * kD * 2;
 #pragma unroll
-    for (int n = 0; n < 8; ++n)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int d0 = 32 * n + 8 * r4 + 4 * g;
-        const u32x2 val = {pack_bf16(acc[n][4 * r4] * inv, acc[n][4 * r4 + 1] * inv),
-                           pack_bf16(acc[n][4 * r4 + 2] * inv, acc[n][4 * r4 + 3] * inv)};
-        *(u32x2*)(op + d0 * 2) = val;
-      }
-    if (g == 0) {
+    for (int n = 0; n < 16; ++n) {
+      const u32x2 val = {pack_bf16(acc[n][0] * inv, acc[n][1] * inv), pack_bf16(acc[n][2] * inv, acc[n][3] * inv)};
+      *(u32x2*)(op + (16 * n + 4 * G) * 2) = val;
+    }
+    if (G == 0) {
       const float m_use = (rs.m == -INFINITY) ? 0.f : rs.m;
       p.lse[hq + row] = l_tot > 0.f ? (m_use + log2f(l_tot)) * 0.69314718055994530942f : -INFINITY;
     }
-  } else {
-    // keep the exchange lockstep for lanes past Lq (their values are unused)
-    (void)xor32_sum(rs.l);
   }
 }
 

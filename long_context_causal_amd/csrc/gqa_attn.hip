@@ -13,7 +13,7 @@
 
 namespace {
 
-constexpr int kWavesBf16 = 4;  // 256 threads, one wave per SIMD
+constexpr int kWavesBf16 = gqa::kWavesB;  // 512 threads, two waves per SIMD
 constexpr int kWavesF32 = 4;   // 256 threads, one wave per SIMD
 
 bool misaligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) != 0; }
@@ -57,7 +57,7 @@ extern "C" int gqa_attn_fwd(const void* q, const void* k, const void* v, void* o
   p.Lq = Lq; p.Lk = Lk; p.q_offset = q_offset;
   p.Hq = (int)Hq; p.Hkv = (int)Hkv; p.n_rep = (int)n_rep;
   p.hpc = (int)(n_rep < W ? n_rep : W);
-  p.ppc = (W / p.hpc) * gqa::kRowsPerWave;
+  p.ppc = (W / p.hpc) * (dtype == GQA_F32 ? gqa::kRowsPerWave : gqa::kRowsB);
   const int64_t n_qb = (Lq + p.ppc - 1) / p.ppc;
   const int64_t G = B * Hkv * (n_rep / p.hpc);
   if (n_qb * G >= ((int64_t)1 << 31)) return GQA_ERR_UNSUPPORTED;
