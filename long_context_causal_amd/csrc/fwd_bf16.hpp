@@ -67,24 +67,28 @@ __device__ __forceinline__ unsigned pack_bf16(float a, float b) {
 
 // Per-lane parts of the tile-copy and LDS-read addresses; the rest of each
 // address is uniform or a compile-time immediate.
+typedef __attribute__((address_space(3))) const char lds_cchar;
+
 struct LanesB {
   uint32_t ldk;    // copy: this lane's 16 bytes within a 1 KB block of 2 key rows (K tile)
   uint32_t ldv;    // the same for the V tile
-  uint32_t k[4];   // K read, d chunk c (32 d each), c % 4 = j, keys 16 b + l16: + 256 (c / 4) + 8192 b
-  uint32_t v[16];  // V read, d block n (16 d), n % 8 = j: v[j] (keys 4G..) and v[8 + j] (keys 16 + 4G..): + 256 (n / 8)
-  __device__ __forceinline__ void init(int wave, int lane) {
+  lds_cchar* k[4];   // K read, d chunk c (32 d each), c % 4 = j, keys 16 b + l16: + 256 (c / 4) + 8192 b
+  lds_cchar* v[8];   // V read, d block n (16 d), n % 8 = j, keys 4G..: + 256 (n / 8); keys 16 + 4G..: + 8192 more
+                     // (swz_v(k + 16) = swz_v(k))
+  // kbase/vbase: LDS byte addresses of the K and V ring regions (folded in, so a
+  // read is one of these VGPRs plus a compile-time immediate)
+  __device__ __forceinline__ void init(int wave, int lane, lds_cchar* kbase, lds_cchar* vbase) {
     const int l16 = lane & 15, G = lane >> 4, g = lane >> 5;
     ldk = (uint32_t)g * 512u + ((uint32_t)((lane & 31) ^ swz_k(2 * wave + g)) << 4);
     ldv = (uint32_t)g * 512u + ((uint32_t)((lane & 31) ^ swz_v(2 * wave + g)) << 4);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) k[j] = (uint32_t)l16 * 512u + ((uint32_t)((4 * j + G) ^ swz_k(l16)) << 4);
+    for (int j = 0; j < 4; ++j) k[j] = kbase + l16 * 512 + (((4 * j + G) ^ swz_k(l16)) << 4);
     const int kr = 4 * G + (l16 >> 2);               // key of this lane's copy within a 16-key block
     const int h = (l16 & 3) >> 1;                     // 16-byte chunk within the 32 bytes of a d block
-    const uint32_t in = (uint32_t)(l16 & 1) << 3;     // 8-byte half of the chunk
+    const int in = (l16 & 1) << 3;                    // 8-byte half of the chunk
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      v[j] = (uint32_t)kr * 512u + ((uint32_t)((2 * j + h) ^ swz_v(kr)) << 4) + in;
-      v[8 + j] = (uint32_t)(kr + 16) * 512u + ((uint32_t)((2 * j + h) ^ swz_v(kr + 16)) << 4) + in;
+      v[j] = vbase + kr * 512 + (((2 * j + h) ^ swz_v(kr)) << 4) + in;
     }
   }
 };
@@ -98,55 +102,77 @@ __device__ __forceinline__ void load_tile_b(SmemB& sm, int st, const char* kb, c
   const char* kt = kb + t * kTileBytesB;
   const char* vt = vb + t * kTileBytesB;
   const int last = (int)min((int64_t)(kBkB - 1), Lk - 1 - t * kBkB);  // last valid key within the tile
+  if (last == kBkB - 1) {
 #pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int blk = wave + kWavesB * it;
-    uint32_t offk = ln.ldk + (uint32_t)blk * 1024u, offv = ln.ldv + (uint32_t)blk * 1024u;
-    if (last < kBkB - 1) {
+    for (int it = 0; it < 2; ++it) {
+      const int blk = wave + kWavesB * it;
+      g2lds16(kt, ln.ldk + (uint32_t)blk * 1024u, sm.k[st] + blk * 1024);
+      g2lds16(vt, ln.ldv + (uint32_t)blk * 1024u, sm.v[st] + blk * 1024);
+    }
+  } else {
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int blk = wave + kWavesB * it;
+      uint32_t offk = ln.ldk + (uint32_t)blk * 1024u, offv = ln.ldv + (uint32_t)blk * 1024u;
       const int kk = (int)(offk >> 9);  // the same key row for both
       if (kk > last) {
         offk = ((uint32_t)last << 9) | (offk & 511u);
         offv = ((uint32_t)last << 9) | (offv & 511u);
       }
+      g2lds16(kt, offk, sm.k[st] + blk * 1024);
+      g2lds16(vt, offv, sm.v[st] + blk * 1024);
     }
-    g2lds16(kt, offk, sm.k[st] + blk * 1024);
-    g2lds16(vt, offv, sm.v[st] + blk * 1024);
   }
   if (skb != nullptr && wave == kWavesB - 1 && lane < kBkB)
     g2lds4((const char*)(skb + t * kBkB), (uint32_t)min(lane, last) * 4u, sm.segk[st]);
 }
 
-// S^T = K Q^T for the tile in LDS at Ks: two 16-key blocks, each 8 MFMAs over
-// D = 256; K fragments read three MFMAs ahead.
-__device__ __forceinline__ void qk_tile(const char* Ks, const bf16x8* qf, const LanesB& ln, f32x4* s) {
+typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// K fragment u = 2 c + b (16-key block b, 32-d chunk c) of a tile whose
+// per-lane read bases (LanesB::k plus the stage offset) are kb[].
+__device__ __forceinline__ bf16x8 k_frag(int u, lds_cchar* const* kb) {
+  const int b = u & 1, c = u >> 1;
+  return *(lds_bf16x8*)(kb[c & 3] + (b * 8192 + (c >> 2) * 256));
+}
+
+// S^T = K Q^T for the tile in ring stage st: two 16-key blocks, each 8 MFMAs
+// over D = 256, alternating between the blocks; K fragments read three MFMAs ahead.
+__device__ __forceinline__ void qk_tile(int st, const bf16x8* qf, const LanesB& ln, f32x4* s) {
+  lds_cchar* kb[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) kb[j] = ln.k[j] + st * kTileBytesB;
   s[0] = f32x4{};
   s[1] = f32x4{};
   bf16x8 kf[3];
 #pragma unroll
-  for (int m = 0; m < 3; ++m) kf[m] = *(const bf16x8*)(Ks + (m >> 3) * 8192 + ln.k[m & 3] + ((m & 7) >> 2) * 256);
+  for (int u = 0; u < 3; ++u) kf[u] = k_frag(u, kb);
 #pragma unroll
-  for (int m = 0; m < 16; ++m) {  // m = 8 b + c
-    s[m >> 3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[m % 3], qf[m & 7], s[m >> 3], 0, 0, 0);
-    const int u = m + 3;
-    if (u < 16) kf[m % 3] = *(const bf16x8*)(Ks + (u >> 3) * 8192 + ln.k[u & 3] + ((u & 7) >> 2) * 256);
+  for (int u = 0; u < 16; ++u) {
+    s[u & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[u % 3], qf[u >> 1], s[u & 1], 0, 0, 0);
+    if (u + 3 < 16) kf[u % 3] = k_frag(u + 3, kb);
   }
 }
 
-// Element mask of one tile: lane holds keys key0 + 16 b + 4G + r (s[b][r]) of row `row`.
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+typedef __attribute__((address_space(3))) const i32x4 lds_i32x4;
+
+// Element mask of one tile: lane holds keys key0 + 16 b + 4G + r (s[b][r]) of
+// row `row`. segk_lane points at this lane's 4 key ids (keys 4G..) in the stage.
 __device__ __forceinline__ void mask_tile(f32x4* s, int64_t key0, int G, int64_t Lk, int causal, int64_t lim,
-                                          bool seg_elem, const int* segk, int sq) {
+                                          bool seg_elem, lds_cchar* segk_lane, int sq) {
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
     const int kk = 16 * b + 4 * G;
-    int4 ids = {0, 0, 0, 0};
-    if (seg_elem) ids = *(const int4*)(segk + kk);
+    i32x4 ids = {0, 0, 0, 0};
+    if (seg_elem) ids = *(lds_i32x4*)(segk_lane + 64 * b);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int64_t key = key0 + kk + r;
       bool vis = key < Lk;
       if (causal) vis = vis && key <= lim;
-      const int id = r == 0 ? ids.x : r == 1 ? ids.y : r == 2 ? ids.z : ids.w;
-      if (seg_elem) vis = vis && id == sq;
+      if (seg_elem) vis = vis && ids[r] == sq;
       s[b][r] = vis ? s[b][r] : -INFINITY;
     }
   }
@@ -207,27 +233,29 @@ __device__ __forceinline__ void softmax_exp(const f32x4* s, RowState& rs, unsign
   rs.lr = fmaf(rs.lr, alpha, lrsum);
 }
 
-// V^T fragment for d block n (16 d): keys 4G..4G+3 and 16+4G..16+4G+3.
-__device__ __forceinline__ bf16x8 v_frag(const char* Vs, int n, const LanesB& ln) {
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4*)(Vs + ln.v[n & 7] + (n >> 3) * 256));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4*)(Vs + ln.v[8 + (n & 7)] + (n >> 3) * 256));
+// V^T fragment for d block n (16 d) of a tile with per-lane read bases vb[]:
+// keys 4G..4G+3 and 16+4G..16+4G+3.
+__device__ __forceinline__ bf16x8 v_frag(int n, lds_cchar* const* vb) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb[n & 7] + ((n >> 3) * 256)));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb[n & 7] + (8192 + (n >> 3) * 256)));
   const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
   return __builtin_bit_cast(bf16x8, u32x4{lo2[0], lo2[1], hi2[0], hi2[1]});
 }
 
-// O^T += V^T P^T for the tile in LDS at Vs: 16 d blocks, V fragments read
+// O^T += V^T P^T for the tile in ring stage st: 16 d blocks, V fragments read
 // three MFMAs ahead.
-__device__ __forceinline__ void pv_tile(f32x4* acc, const char* Vs, const unsigned* pk, const LanesB& ln) {
+__device__ __forceinline__ void pv_tile(int st, f32x4* acc, const unsigned* pk, const LanesB& ln) {
+  lds_cchar* vb[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) vb[j] = ln.v[j] + st * kTileBytesB;
   const bf16x8 pf = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
   bf16x8 vf[3];
 #pragma unroll
-  for (int n = 0; n < 3; ++n) vf[n] = v_frag(Vs, n, ln);
+  for (int n = 0; n < 3; ++n) vf[n] = v_frag(n, vb);
 #pragma unroll
   for (int n = 0; n < 16; ++n) {
     acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[n % 3], pf, acc[n], 0, 0, 0);
-    if (n + 3 < 16) vf[n % 3] = v_frag(Vs, n + 3, ln);
+    if (n + 3 < 16) vf[n % 3] = v_frag(n + 3, vb);
   }
 }
 
@@ -288,19 +316,22 @@ __global__ __launch_bounds__(W * 64) void fwd_bf16_kernel(FwdParams p) {
   RowState rs = {-INFINITY, 0.f, 0.f};
   const float sl2 = p.scale_log2;
   LanesB ln;
-  ln.init(wave, lane);
+  ln.init(wave, lane, (lds_cchar*)sm.k[0], (lds_cchar*)sm.v[0]);
 
   auto full_bit = [&](int t) -> bool { return use_bits && ((sm.bits.full[t >> 5] >> (t & 31)) & 1u); };
-  auto needs_mask = [&](int t) -> bool {
-    const int64_t k0 = (int64_t)t * kBkB;
-    return (seg && !full_bit(t)) || k0 + kBkB > p.Lk || (p.causal && k0 + kBkB - 1 > p.q_offset + pw);
-  };
   auto next_tile = [&](int t) -> int {
     if (t >= n_tiles) return n_tiles;
     return use_bits ? seg_next(sm.bits, t + 1, n_tiles) : t + 1;
   };
+  lds_cchar* segk_lane = (lds_cchar*)sm.segk[0] + 16 * G;
+  auto mask_if_needed = [&](f32x4* s, int t, int st) {
+    const int64_t k0 = (int64_t)t * kBkB;
+    const bool seg_elem = seg && !full_bit(t);
+    if (seg_elem || k0 + kBkB > p.Lk || (p.causal && k0 + kBkB - 1 > p.q_offset + pw))
+      mask_tile(s, k0, G, p.Lk, p.causal, lim, seg_elem, segk_lane + st * (kBkB * 4), sq);
+  };
 
-  // visible tiles in order: cur (being finished), nxt (QK this iteration), nn and n3 (in flight)
+  // visible tiles in order: cur (being finished), nxt (QK this step), nn and n3 (in flight)
   int cur = use_bits ? seg_next(sm.bits, 0, n_tiles) : 0;
   if (cur < n_tiles) {
     int nxt = next_tile(cur), nn = next_tile(nxt);
@@ -310,9 +341,9 @@ __global__ __launch_bounds__(W * 64) void fwd_bf16_kernel(FwdParams p) {
     wait_tiles((nxt < n_tiles) + (nn < n_tiles));
     __syncthreads();
     f32x4 s_cur[2];
-    qk_tile(sm.k[0], qf, ln, s_cur);
-    if (needs_mask(cur)) mask_tile(s_cur, (int64_t)cur * kBkB, G, p.Lk, p.causal, lim, seg && !full_bit(cur), sm.segk[0], sq);
-    int i = 0;  // ring position of `cur`
+    qk_tile(0, qf, ln, s_cur);
+    mask_if_needed(s_cur, cur, 0);
+    int i = 0;  // ring stage of `cur`
     while (nxt < n_tiles) {
       wait_tiles(nn < n_tiles);  // tile nxt has landed (nn may still be in flight)
       __syncthreads();           // ... for every wave; and stage (i + 3) % 4 is free
@@ -325,25 +356,24 @@ __global__ __launch_bounds__(W * 64) void fwd_bf16_kernel(FwdParams p) {
       // A: QK of the next tile interleaved with this tile's exps
       unsigned pk[4];
       f32x4 s_nxt[2];
-      qk_tile(sm.k[s1], qf, ln, s_nxt);
+      qk_tile(s1, qf, ln, s_nxt);
       softmax_exp(s_cur, rs, pk, sl2, m_use, alpha);
       // B: PV of this tile
-      pv_tile(acc, sm.v[i & 3], pk, ln);
-      if (needs_mask(nxt))
-        mask_tile(s_nxt, (int64_t)nxt * kBkB, G, p.Lk, p.causal, lim, seg && !full_bit(nxt), sm.segk[s1], sq);
+      pv_tile(i, acc, pk, ln);
+      mask_if_needed(s_nxt, nxt, s1);
       s_cur[0] = s_nxt[0];
       s_cur[1] = s_nxt[1];
       cur = nxt;
       nxt = nn;
       nn = n3;
-      i = (i + 1) & 3;
+      i = s1;
     }
     float m_use;
     const float alpha = softmax_max(s_cur, rs, sl2, m_use);
     rescale_if_needed(acc, alpha);
     unsigned pk[4];
     softmax_exp(s_cur, rs, pk, sl2, m_use, alpha);
-    pv_tile(acc, sm.v[i & 3], pk, ln);
+    pv_tile(i, acc, pk, ln);
   }
 
   // epilogue: O = acc / lr (bf16), lse = ln2 (m + log2 l); lane holds O[row][16 n + 4G + r]
