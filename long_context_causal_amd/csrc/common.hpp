@@ -125,7 +125,7 @@ struct SegBits {
 
 template <int W, int BK>
 __device__ void seg_scan(SegBits& sb, const FwdParams& p, const Work& w, int n_tiles) {
-  constexpr int KPL = 32;          // consecutive keys each lane reduces per round
+  constexpr int KPL = 32;          // consecutive keys each lane reduces per pass
   constexpr int LPT = BK / KPL;    // lanes that share one tile
   static_assert(BK % KPL == 0, "tile must be a whole number of lane chunks");
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
