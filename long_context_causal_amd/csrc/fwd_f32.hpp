@@ -23,11 +23,15 @@ constexpr int kBkF = 32;                    // keys per LDS tile
 constexpr int kTileBytesF = kBkF * kD * 4;  // 32 KB per K or V tile
 constexpr float kLazyF = 8.0f;
 
-// Byte offset of (key, 16-byte chunk) in an fp32 tile: 1 KB rows, chunks
-// XOR-swizzled by key % 8.
-__device__ __forceinline__ uint32_t swz_f(int key, int chunk16) {
-  return (uint32_t)key * 1024u + ((uint32_t)(chunk16 ^ (key & 7)) << 4);
-}
+// LDS image of an fp32 tile: 1 KB key rows of 64 16-byte chunks; chunk c of key
+// k is stored at chunk c ^ swzk_f(k) in K tiles and c ^ swzv_f(k) in V tiles.
+// The K reads are 16-byte reads of 16 consecutive keys at one chunk per clock:
+// an XOR by k % 16 spreads them over all 64 banks. The V reads are 4-byte
+// reads of 32 consecutive d (8 chunks) of two keys 4 apart per clock: swzv_f
+// puts key bit 2 into chunk bit 3 so the two keys use different halves of the
+// banks (and permutes within the 8 chunks by k % 8).
+__device__ __forceinline__ int swzk_f(int key) { return key & 15; }
+__device__ __forceinline__ int swzv_f(int key) { return (((key >> 2) & 1) << 3) | (key & 7); }
 
 struct SmemF {
   __attribute__((aligned(16))) char k[2][kTileBytesF];
@@ -36,32 +40,36 @@ struct SmemF {
   SegBits bits;
 };
 
-// Async copy of key tile t into LDS stage `st`: wave w copies key rows
-// w, w + W, ... (1 KB each, lane l fetching global chunk l ^ (row % 8)).
-// Missing keys past Lk re-read row Lk-1.
 // Per-lane pieces of the swizzled LDS addresses, precomputed once so the
-// inner loops use a few VGPRs plus immediate offsets. For key row kk and
-// 16-byte chunk c the swizzled chunk is c ^ (kk % 8); all terms that do not
-// depend on the lane are folded into immediates by the callers.
+// inner loops use a few VGPRs plus immediate offsets.
 struct LanesF {
-  uint32_t ld[2];   // tile copy: (lane ^ (row % 8)) * 16 for rows w + 8i and w + 4 + 8i
-  uint32_t kq[4];   // K read for chunk 2c + g, c % 4 = j:  l32 * 1024 + ((2j + g) ^ (l32 % 8)) * 16
-  uint32_t vq[4];   // V read for key step tt, tt % 4 = j: key 4g + j, d = l32 (+ 32 n, + 8 (tt / 4) keys)
+  uint32_t ldk[4];    // K copy of key row w + 4 it, it % 4 = j: (lane ^ swzk_f(row)) * 16
+  uint32_t ldv[2];    // V copy of key row w + 4 it, it % 2 = j: (lane ^ swzv_f(row)) * 16
+  uint32_t kq[8];     // K read of chunk 2c + g, c % 8 = j, key l32: + 256 (c / 8)
+  uint32_t vq[2][4];  // V read of key step tt (tt % 4 = j), d block n: vq[n % 2][j] + 8192 (tt / 4) + 128 n
   __device__ __forceinline__ void init(int wave, int lane) {
-    const int l32 = lane & 31, g = lane >> 5, x = l32 & 7;
-    ld[0] = (uint32_t)(lane ^ (wave & 7)) << 4;
-    ld[1] = (uint32_t)(lane ^ ((wave + 4) & 7)) << 4;
+    const int l32 = lane & 31, g = lane >> 5;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ldk[j] = (uint32_t)(lane ^ swzk_f(wave + 4 * j)) << 4;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) ldv[j] = (uint32_t)(lane ^ swzv_f(wave + 4 * j)) << 4;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) kq[j] = (uint32_t)l32 * 1024u + ((uint32_t)((2 * j + g) ^ swzk_f(l32)) << 4);
+    // V key kk = 8 (tt / 4) + 4 g + j has swzv_f(kk) = 8 g + 4 g + j, so chunk
+    // (8 n + l32 / 4) ^ swzv_f(kk) = 8 (n ^ g) + ((l32 / 4) ^ (4 g + j))
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      kq[j] = (uint32_t)l32 * 1024u + ((uint32_t)((2 * j + g) ^ x) << 4);
-      vq[j] = (uint32_t)(4 * g + j) * 1024u + ((uint32_t)((l32 >> 2) ^ (4 * g + j)) << 4) + ((uint32_t)(l32 & 3) << 2);
+      const uint32_t base = (uint32_t)(4 * g + j) * 1024u + ((uint32_t)((l32 >> 2) ^ (4 * g + j)) << 4) +
+                            ((uint32_t)(l32 & 3) << 2);
+      vq[0][j] = base + 128u * (uint32_t)g;  // even n: 8 (n ^ g) = 8 n + 8 g
+      vq[1][j] = base - 128u * (uint32_t)g;  // odd n:  8 (n ^ g) = 8 n - 8 g
     }
   }
 };
 
 // Async copy of key tile t into LDS stage `st`: wave w copies key rows
-// w, w + W, ... (1 KB each, lane l fetching global chunk l ^ (row % 8)).
-// Missing keys past Lk re-read row Lk-1.
+// w, w + W, ... (1 KB each, lane l fetching the global chunk that the swizzle
+// places at its position). Missing keys past Lk re-read row Lk-1.
 template <int W>
 __device__ __forceinline__ void load_tile_f(SmemF& sm, int st, const char* kb, const char* vb, const int32_t* skb,
                                             int64_t t, int64_t Lk, int wave, int lane, const LanesF& ln) {
@@ -73,8 +81,8 @@ __device__ __forceinline__ void load_tile_f(SmemF& sm, int st, const char* kb, c
   for (int it = 0; it < kBkF / W; ++it) {
     const int kk = wave + W * it;
     const uint32_t src = (uint32_t)(kk <= last ? kk : (int)last) * 1024u;
-    g2lds16(kt, src + ln.ld[it & 1], sm.k[st] + kk * 1024);
-    g2lds16(vt, src + ln.ld[it & 1], sm.v[st] + kk * 1024);
+    g2lds16(kt, src + ln.ldk[it & 3], sm.k[st] + kk * 1024);
+    g2lds16(vt, src + ln.ldv[it & 1], sm.v[st] + kk * 1024);
   }
   if (skb != nullptr && wave == W - 1 && lane < kBkF) {
     g2lds4((const char*)(skb + t * kBkF), (uint32_t)min((int64_t)lane, last) * 4u, sm.segk[st]);
@@ -147,7 +155,7 @@ __global__ __launch_bounds__(W * 64) void fwd_f32_kernel(FwdParams p) {
       for (int c = 0; c < 32; ++c) {
         const f32x4 a = kf0;
         kf0 = kf1;
-        if (c + 2 < 32) kf1 = *(const f32x4*)(Ks + ln.kq[(c + 2) & 3] + ((c + 2) >> 2) * 128);
+        if (c + 2 < 32) kf1 = *(const f32x4*)(Ks + ln.kq[(c + 2) & 7] + ((c + 2) >> 3) * 256);
 #pragma unroll
         for (int e = 0; e < 4; ++e) s = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], qf[c][e], s, 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
@@ -194,13 +202,13 @@ __global__ __launch_bounds__(W * 64) void fwd_f32_kernel(FwdParams p) {
       // The 8 V values of key step tt (one per d block) are read one step ahead.
       float vcur[8], vnxt[8];
 #pragma unroll
-      for (int n = 0; n < 8; ++n) vcur[n] = *(const float*)(Vs + ln.vq[0] + n * 128);
+      for (int n = 0; n < 8; ++n) vcur[n] = *(const float*)(Vs + ln.vq[n & 1][0] + n * 128);
 #pragma unroll
       for (int tt = 0; tt < 16; ++tt) {
         if (tt + 1 < 16) {
           const int u = tt + 1;
 #pragma unroll
-          for (int n = 0; n < 8; ++n) vnxt[n] = *(const float*)(Vs + ln.vq[u & 3] + (u >> 2) * 8192 + n * 128);
+          for (int n = 0; n < 8; ++n) vnxt[n] = *(const float*)(Vs + ln.vq[n & 1][u & 3] + (u >> 2) * 8192 + n * 128);
         }
 #pragma unroll
         for (int n = 0; n < 8; ++n) acc[n] = __builtin_amdgcn_mfma_f32_32x32x2f32(vcur[n], pr[tt], acc[n], 0, 0, 0);
