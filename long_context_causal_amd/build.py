@@ -1,45 +1,70 @@
-"""Build libgqa_attn.so (the HIP kernels and the C ABI) in-tree for gfx950."""
+"""Build libgqa_attn.so (the HIP kernels and the C ABI) in-tree for gfx950.
+
+Each kernel is its own translation unit, compiled with the code-generation
+flags that suit it, and the objects are linked into one shared library.
+"""
 from __future__ import annotations
 
 import os
 import subprocess
 import sys
+import tempfile
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRC = os.path.join(HERE, "csrc", "gqa_attn.hip")
+CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libgqa_attn.so")
 
-HIPCC_FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+COMMON_FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # keep the compiler from forming packed-fp32 (v_pk_*_f32) instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # MFMA accumulators in the VGPR file: the O accumulator is also touched by
-    # VALU (rescale, epilogue); the AGPR form makes the compiler copy it
-    # between the two register files on every iteration
-    "-mllvm", "-amdgpu-mfma-vgpr-form",
     # no NaN inputs are produced or consumed (masked scores are -inf, guarded);
     # lets fmaxf lower to a plain v_max without canonicalising its operands
     "-fno-honor-nans",
     "-Wall", "-Wno-unused-function",
 ]
 
+# MFMA accumulators in the VGPR file: in the fp32 kernel the O accumulator is
+# also touched by VALU inside the loop (rescale) and fits the VGPR file; the
+# AGPR form made the compiler copy it between the two register files on every
+# iteration.
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 
-def build(verbose: bool = False) -> str:
-    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = OUT + ".tmp%d" % os.getpid()
-    cmd = [hipcc] + HIPCC_FLAGS + ["-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
-                                   SRC, "-o", tmp]
+# translation unit -> extra flags. The bf16 kernel keeps its O accumulator in
+# AGPRs (Q, scores and fragments fill the VGPRs).
+UNITS = {
+    "gqa_attn.hip": [],
+    "fwd_f32.hip": VGPR_FORM,
+    "fwd_bf16.hip": [],
+}
+
+# hipcc's host pass does not know the packed-fp32 target feature; that warning is expected
+_NOISE = "packed-fp32-ops' is not a recognized feature"
+
+
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
-    # hipcc's host pass does not know the packed-fp32 target feature; that warning is expected
-    noise = "packed-fp32-ops' is not a recognized feature"
-    msgs = [l for l in (res.stdout + res.stderr).splitlines() if noise not in l and l.strip()]
+    msgs = [l for l in (res.stdout + res.stderr).splitlines() if _NOISE not in l and l.strip()]
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs), file=sys.stderr)
+
+
+def build(verbose: bool = False) -> str:
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    with tempfile.TemporaryDirectory(prefix="gqa_build_") as tmpd:
+        objs = []
+        for unit, extra in UNITS.items():
+            obj = os.path.join(tmpd, unit + ".o")
+            _run([hipcc] + COMMON_FLAGS + extra + inc + ["-c", os.path.join(CSRC, unit), "-o", obj], verbose)
+            objs.append(obj)
+        tmp = OUT + ".tmp%d" % os.getpid()
+        _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", tmp], verbose)
     os.replace(tmp, OUT)
     return OUT
 

@@ -109,6 +109,28 @@ __device__ __forceinline__ void g2lds4(const char* gbase, uint32_t voff, const v
 }
 __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// The same async copy through a buffer resource (MUBUF with the LDS bit): the
+// resource bounds the read, and lanes whose offset falls at or past its size
+// read zeros, so a tile that runs past the end of a tensor needs no clamping.
+// Resource words: 48-bit base address (stride 0), size in bytes, and the
+// format word of a raw 32-bit buffer on this family.
+typedef __attribute__((ext_vector_type(4))) int rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  return rsrc_t{(int)(uint32_t)a, (int)(uint32_t)(a >> 32), (int)bytes, 0x00020000};
+}
+// lds: LDS byte address of the wave's 1 KB (or 256 B) destination. It goes
+// through readfirstlane: it is wave-uniform, and this keeps it in an SGPR even
+// where the compiler cannot prove that.
+__device__ __forceinline__ void buf2lds16(rsrc_t rsrc, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc) : "memory");
+}
+__device__ __forceinline__ void buf2lds4(rsrc_t rsrc, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc) : "memory");
+}
+
 // ---------------------------------------------------------------------------
 // Segment scan. With segment ids, a key tile is visible to the workgroup when
 // the id range of its keys meets the id range of the workgroup's query rows; it

@@ -7,14 +7,10 @@
 #include <stdint.h>
 
 #include "common.hpp"
-#include "fwd_bf16.hpp"
-#include "fwd_f32.hpp"
+#include "launch.hpp"
 #include "merge.hpp"
 
 namespace {
-
-constexpr int kWavesBf16 = gqa::kWavesB;  // 512 threads, two waves per SIMD
-constexpr int kWavesF32 = 4;   // 256 threads, one wave per SIMD
 
 bool misaligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) != 0; }
 
@@ -50,14 +46,14 @@ extern "C" int gqa_attn_fwd(const void* q, const void* k, const void* v, void* o
       overlap(lse, lse_bytes, k, kv_bytes) || overlap(lse, lse_bytes, v, kv_bytes))
     return GQA_ERR_ALIAS;
 
-  const int W = dtype == GQA_F32 ? kWavesF32 : kWavesBf16;
+  const int W = dtype == GQA_F32 ? gqa::kWavesF32 : gqa::kWavesBf16;
   gqa::FwdParams p;
   p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
   p.seg_q = seg_q; p.seg_k = seg_k;
   p.Lq = Lq; p.Lk = Lk; p.q_offset = q_offset;
   p.Hq = (int)Hq; p.Hkv = (int)Hkv; p.n_rep = (int)n_rep;
   p.hpc = (int)(n_rep < W ? n_rep : W);
-  p.ppc = (W / p.hpc) * (dtype == GQA_F32 ? gqa::kRowsPerWave : gqa::kRowsB);
+  p.ppc = (W / p.hpc) * (dtype == GQA_F32 ? gqa::kRowsF32 : gqa::kRowsBf16);
   const int64_t n_qb = (Lq + p.ppc - 1) / p.ppc;
   const int64_t G = B * Hkv * (n_rep / p.hpc);
   if (n_qb * G >= ((int64_t)1 << 31)) return GQA_ERR_UNSUPPORTED;
@@ -68,12 +64,8 @@ extern "C" int gqa_attn_fwd(const void* q, const void* k, const void* v, void* o
 
   hipStream_t s = (hipStream_t)stream;
   (void)hipGetLastError();
-  const dim3 grid((unsigned)(n_qb * G));
-  if (dtype == GQA_F32)
-    hipLaunchKernelGGL(gqa::fwd_f32_kernel<kWavesF32>, grid, dim3(kWavesF32 * 64), 0, s, p);
-  else
-    hipLaunchKernelGGL((gqa::fwd_bf16_kernel<kWavesBf16>), grid, dim3(kWavesBf16 * 64), 0, s, p);
-  return hipGetLastError() == hipSuccess ? GQA_OK : GQA_ERR_LAUNCH;
+  const hipError_t e = dtype == GQA_F32 ? gqa::launch_fwd_f32(p, s) : gqa::launch_fwd_bf16(p, s);
+  return e == hipSuccess ? GQA_OK : GQA_ERR_LAUNCH;
 }
 
 extern "C" int gqa_attn_merge(const void* o1, const float* lse1, const void* o2, const float* lse2,

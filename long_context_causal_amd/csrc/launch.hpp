@@ -1,0 +1,20 @@
+// launch.hpp -- launchers of the forward kernels, each defined in the
+// translation unit of its kernel (fwd_f32.hip, fwd_bf16.hip) so that each
+// kernel is compiled with its own code-generation flags.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include "common.hpp"
+
+namespace gqa {
+
+// Workgroup shapes the host plan needs: waves per workgroup and query rows per wave.
+constexpr int kWavesF32 = 4, kRowsF32 = 32;
+constexpr int kWavesBf16 = 4, kRowsBf16 = 32;
+
+// Enqueue one forward launch (grid = p.n_qb * p.G workgroups); returns
+// hipGetLastError() after the launch.
+hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);
+hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream);
+
+}  // namespace gqa
