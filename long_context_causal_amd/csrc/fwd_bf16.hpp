@@ -247,13 +247,14 @@ __device__ __forceinline__ bf16x8 k_frag(int q, lds_cchar* const* kb) {
 }
 
 // Phase A: S^T(next) = K Q^T for the tile in K stage kst (32 MFMAs over
-// D = 256, two key halves) with slots 0..31 of the current tile's exps, the K
-// part (and ids) of the tile copy two ahead, and the first V fragments of
-// phase B (already resident).
+// D = 256, two key halves) with slots 0..31 of the current tile's exps, the
+// tile copies (K and ids of the tile two ahead, V of the tile one ahead: early
+// enough that they land before the next barrier), and the first V fragments
+// of phase B (already resident).
 __device__ __forceinline__ void phase_a(int kst, const bf16x8* qf, const LanesB& ln, f32x16* s_nxt,
                                         const f32x16* s_cur, float sl2, float m_use, unsigned* pk, ExpPipe& ep,
-                                        const PartCopy& kc, bool seg, int wave, int lane, lds_cchar* const* vb,
-                                        bf16x8* vf) {
+                                        const PartCopy& kc, const PartCopy& vc, bool seg, int wave, int lane,
+                                        lds_cchar* const* vb, bf16x8* vf) {
   lds_cchar* kb[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) kb[j] = ln.k[j] + kst * kTileBytesB;
@@ -267,7 +268,8 @@ __device__ __forceinline__ void phase_a(int kst, const bf16x8* qf, const LanesB&
     if (q + 3 < 32) kf[q % 3] = k_frag(q + 3, kb);
     ep.slot(q, s_cur, sl2, m_use, pk);
     if ((q & 3) == 1) kc.rows(ln.ldk, q >> 2, wave);
-    if (q == 3 && seg) kc.ids(wave, lane);
+    if ((q & 3) == 3) vc.rows(ln.ldv, q >> 2, wave);
+    if (q == 2 && seg) kc.ids(wave, lane);
     if (q >= 32 - kVPre) vf[q - (32 - kVPre)] = v_frag(q - (32 - kVPre), 0, vb);
     GQA_SEGMENT_END();
   }
@@ -361,9 +363,8 @@ struct Bf16Wave {
   // flight (32 MFMAs: 4 key quarters x 8 d blocks, fragments read kVPre
   // products ahead) with the last exp slots of this tile, the row max of the
   // next scores s_nxt (masked first where needed; ids in K stage kst1) spread
-  // over the products, the lazy update of the running max, and the V part of
-  // the tile copy one ahead. Returns alpha.
-  __device__ __forceinline__ float phase_b(int kst1, f32x16* s_nxt, unsigned* pk, ExpPipe& ep, const PartCopy& vc,
+  // over the products, and the lazy update of the running max. Returns alpha.
+  __device__ __forceinline__ float phase_b(int kst1, f32x16* s_nxt, unsigned* pk, ExpPipe& ep,
                                            lds_cchar* const* vbs, bf16x8* vf) {
     const float sl2 = p.scale_log2;
     const float m_cur = rs.m_use;
@@ -382,7 +383,6 @@ struct Bf16Wave {
       }
       if (u == 19) mx = xor32_max(mx);
       if (u == 21) alpha = lazy_max_update(mx, rs, sl2);
-      if ((u & 3) == 1) vc.rows(ln.ldv, u >> 2, wave);
       GQA_SEGMENT_END();
     }
     rs.l += ep.lsum;
@@ -390,12 +390,17 @@ struct Bf16Wave {
     return alpha;
   }
 
-  // The last tile: its exps, then its PV product (V stage vst).
+  // The last tile: its exps, then its PV product (V stage vst). The scores
+  // pass through an empty asm first: the exps here and in phase A would
+  // otherwise be one common expression, which the compiler hoists above the
+  // branch between them, out of reach of the products that hide it.
   __device__ __forceinline__ void finish(int vst) {
     unsigned pk[16];
     ExpPipe ep;
+    f32x16 sc[2] = {s_cur[0], s_cur[1]};
+    asm volatile("" : "+v"(sc[0]), "+v"(sc[1]));
 #pragma unroll
-    for (int e = 0; e < 34; ++e) ep.slot(e, s_cur, p.scale_log2, rs.m_use, pk);
+    for (int e = 0; e < 34; ++e) ep.slot(e, sc, p.scale_log2, rs.m_use, pk);
     rs.l += ep.lsum;
     rs.lr += ep.lrsum;
     lds_cchar* vbs[4];
@@ -430,8 +435,8 @@ struct Bf16Wave {
 #pragma unroll
     for (int j = 0; j < 4; ++j) vbs[j] = ln.v[j] + st * kTileBytesB;
     bf16x8 vf[kVPre];
-    phase_a(st1, qf, ln, s_nxt, s_cur, p.scale_log2, rs.m_use, pk, ep, kc, SEG, wave, lane, vbs, vf);
-    const float alpha = phase_b(st1, s_nxt, pk, ep, vc, vbs, vf);
+    phase_a(st1, qf, ln, s_nxt, s_cur, p.scale_log2, rs.m_use, pk, ep, kc, vc, SEG, wave, lane, vbs, vf);
+    const float alpha = phase_b(st1, s_nxt, pk, ep, vbs, vf);
     rescale(acc, rs, alpha);
     s_cur[0] = s_nxt[0];
     s_cur[1] = s_nxt[1];
