@@ -147,15 +147,28 @@ def cpu_baseline(x, target_s=15.0):
                        "all their visible keys; %.1f s" % (n, L, L, dt))
 
 
-def kernel_source_hash() -> str:
-    """Hash of the HIP sources, so stored counter readings are only used for the
-    kernel build they were taken on."""
+# Sources and translation unit of each forward kernel.
+KERNEL_SOURCES = {"f32": (["common.hpp", "launch.hpp", "fwd_f32.hpp", "fwd_f32.hip"], "fwd_f32.hip"),
+                  "bf16": (["common.hpp", "launch.hpp", "fwd_bf16.hpp", "fwd_bf16.hip"], "fwd_bf16.hip")}
+
+
+def kernel_dtype(name: str) -> str:
+    """'bf16' or 'f32' from a kernel or workload name."""
+    return "bf16" if "bf16" in name else "f32"
+
+
+def kernel_source_hash(dtype: str) -> str:
+    """Hash of one forward kernel's sources and compile flags, so stored counter
+    readings are only used for the kernel build they were taken on."""
     import hashlib
+    from long_context_causal_amd import build as gbuild
+    files, unit = KERNEL_SOURCES[dtype]
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "long_context_causal_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in files:
         h.update(f.encode())
         h.update(open(os.path.join(csrc, f), "rb").read())
+    h.update(repr(gbuild.COMMON_FLAGS + gbuild.UNITS[unit]).encode())
     return h.hexdigest()[:16]
 
 
@@ -187,7 +200,7 @@ def pmc_report(fetch_db, write_db, kernel_substr, workload, out_path):
     wc, _ = pick(w, "copyBuffer", "WRITE_SIZE")
     gib = float(1 << 30)
     fetch_scale, write_scale = gib / (fc * 1024.0), gib / (wc * 1024.0)
-    rec = {"workload": workload, "kernel": kname, "kernel_src_sha": kernel_source_hash(),
+    rec = {"workload": workload, "kernel": kname, "kernel_src_sha": kernel_source_hash(kernel_dtype(kname)),
            "fetch_kib_per_dispatch": fk, "write_kib_per_dispatch": wk,
            "copy_fetch_kib": fc, "copy_write_kib": wc, "fetch_scale": fetch_scale, "write_scale": write_scale,
            "traffic_bytes": fk * 1024.0 * fetch_scale + wk * 1024.0 * write_scale}
@@ -204,7 +217,7 @@ def stored_traffic(workload):
         return None
     recs = json.load(open(p))
     rec = recs.get(workload)
-    if rec is None or rec.get("kernel_src_sha") != kernel_source_hash():
+    if rec is None or rec.get("kernel_src_sha") != kernel_source_hash(kernel_dtype(workload)):
         return None
     return rec["traffic_bytes"]
 
