@@ -346,7 +346,7 @@ struct Bf16Wave {
     return part_copy(rb.v + (uint32_t)st * kTileBytesB, 0u, vb, nullptr, t, t < n_tiles, p.Lk);
   }
   __device__ __forceinline__ bool full_bit(int t) const {
-    return SEG && use_bits && ((sm.bits.full[t >> 5] >> (t & 31)) & 1u);
+    return SEG && use_bits && t < n_tiles && ((sm.bits.full[t >> 5] >> (t & 31)) & 1u);
   }
   __device__ __forceinline__ void mask_if_needed(f32x16* s, int t, int st) {
     const int64_t k0 = (int64_t)t * kBkB;
@@ -390,41 +390,15 @@ struct Bf16Wave {
     return alpha;
   }
 
-  // The last tile: its exps, then its PV product (V stage vst). The scores
-  // pass through an empty asm first: the exps here and in phase A would
-  // otherwise be one common expression, which the compiler hoists above the
-  // branch between them, out of reach of the products that hide it.
-  __device__ __forceinline__ void finish(int vst) {
-    unsigned pk[16];
-    ExpPipe ep;
-    f32x16 sc[2] = {s_cur[0], s_cur[1]};
-    asm volatile("" : "+v"(sc[0]), "+v"(sc[1]));
-#pragma unroll
-    for (int e = 0; e < 34; ++e) ep.slot(e, sc, p.scale_log2, rs.m_use, pk);
-    rs.l += ep.lsum;
-    rs.lr += ep.lrsum;
-    lds_cchar* vbs[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) vbs[j] = ln.v[j] + vst * kTileBytesB;
-#pragma unroll
-    for (int u = 0; u < 32; ++u) {
-      const int n = u & 7, h = u >> 3;
-      const bf16x8 ph = __builtin_bit_cast(bf16x8, u32x4{pk[4 * h], pk[4 * h + 1], pk[4 * h + 2], pk[4 * h + 3]});
-      acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_frag(n, h, vbs), ph, acc[n], 0, 0, 0);
-    }
-  }
-
-  // One step with tile `cur` in stages (K, V) = i % 2: returns false after
-  // finishing the last tile (whose V, too, was copied in the step before, so
-  // the wait and the barrier come first).
-  __device__ __forceinline__ bool step(int i) {
+  // One step with tile `cur` in stages (K, V) = i % 2. The step of the last
+  // tile runs like the others: its "next" tile is past the end, copied as
+  // zeros and fully masked (-inf scores leave the running max, and with it O,
+  // unchanged), which costs one tile's QK products per workgroup and keeps a
+  // single loop body.
+  __device__ __forceinline__ void step(int i) {
     const int st = i & 1, st1 = st ^ 1;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // K(nxt) and V(cur), copied last step, have landed
     __syncthreads();                                    // ... for every wave; K stage st and V stage st1 are free
-    if (nxt >= n_tiles) {
-      finish(st);
-      return false;
-    }
     const int n3 = next_tile(nn);
     const PartCopy kc = k_copy(st, nn);   // K(#i+2) into K(#i)'s stage
     const PartCopy vc = v_copy(st1, nxt);  // V(#i+1) into V(#i-1)'s stage
@@ -443,7 +417,6 @@ struct Bf16Wave {
     cur = nxt;
     nxt = nn;
     nn = n3;
-    return true;
   }
 };
 
@@ -512,8 +485,7 @@ __global__ __launch_bounds__(kWavesB * 64) void fwd_bf16_kernel(FwdParams p) {
     qk_only(0, wv.qf, wv.ln, wv.s_cur);
     wv.mask_if_needed(wv.s_cur, wv.cur, 0);
     (void)softmax_max(wv.s_cur, wv.rs, p.scale_log2);  // nothing accumulated yet: no rescale
-    for (int i = 0; wv.step(i); ++i) {
-    }
+    for (int i = 0; wv.cur < wv.n_tiles; ++i) wv.step(i);
   }
 
   // epilogue: O = acc / lr (bf16), lse = ln2 (m + log2 l); lane holds
