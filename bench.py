@@ -31,7 +31,8 @@ def dev_inputs(x, torch):
     dev = "cuda:0"
     if x.dtype == "f32":
         return tuple(torch.from_numpy(a).to(dev) for a in (x.q, x.k, x.v))
-    return tuple(torch.from_numpy(b.view(np.int16)).to(dev).view(torch.bfloat16) for b in (x.q_bits, x.k_bits, x.v_bits))
+    tdt = torch.bfloat16 if x.dtype == "bf16" else torch.float16
+    return tuple(torch.from_numpy(b.view(np.int16)).to(dev).view(tdt) for b in (x.q_bits, x.k_bits, x.v_bits))
 
 
 def time_calls(fn, steps, warmup, torch):
@@ -149,12 +150,18 @@ def cpu_baseline(x, target_s=15.0):
 
 # Sources and translation unit of each forward kernel.
 KERNEL_SOURCES = {"f32": (["common.hpp", "launch.hpp", "fwd_f32.hpp", "fwd_f32.hip"], "fwd_f32.hip"),
-                  "bf16": (["common.hpp", "launch.hpp", "fwd_bf16.hpp", "fwd_bf16.hip"], "fwd_bf16.hip")}
+                  "bf16": (["common.hpp", "launch.hpp", "fwd_h16.hpp", "fwd_h16.hip"], "fwd_h16.hip"),
+                  "f16": (["common.hpp", "launch.hpp", "fwd_h16.hpp", "fwd_h16.hip"], "fwd_h16.hip")}
 
 
 def kernel_dtype(name: str) -> str:
-    """'bf16' or 'f32' from a kernel or workload name."""
-    return "bf16" if "bf16" in name else "f32"
+    """'bf16', 'f16' or 'f32' from a kernel or workload name; kernel names may be
+    mangled (DF16b is __bf16, DF16_ is _Float16)."""
+    if "bf16" in name or "DF16b" in name:
+        return "bf16"
+    if "fp16" in name or "_Float16" in name or "DF16_" in name or name.startswith("f16"):
+        return "f16"
+    return "f32"
 
 
 def kernel_source_hash(dtype: str) -> str:
@@ -229,7 +236,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--quick", action="store_true", help="primary workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", default=None, help="run one workload: f32-15231, f32-30468, f32-60926, bf16-60926")
+    ap.add_argument("--only", default=None,
+                    help="run one workload: f32-15231, f32-30468, f32-60926, bf16-60926, f16-60926")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (3 times) to calibrate HBM byte counters")
     ap.add_argument("--pmc-report", nargs=4, metavar=("FETCH_DB", "WRITE_DB", "KERNEL_SUBSTR", "WORKLOAD"),
@@ -266,6 +274,7 @@ def main():
         "f32-30468": ("causal GQA fwd fp32 B=1 Hq=16 Hkv=4 D=256 L=30468", 30468, "f32"),
         "f32-60926": ("causal GQA fwd fp32 B=1 Hq=16 Hkv=4 D=256 L=60926", 60926, "f32"),
         "bf16-60926": ("causal GQA fwd bf16 B=1 Hq=16 Hkv=4 D=256 L=60926", 60926, "bf16"),
+        "f16-60926": ("causal GQA fwd fp16 B=1 Hq=16 Hkv=4 D=256 L=60926", 60926, "f16"),
     }
     primary_key = args.only or "f32-30468"
     name, L, dt = workloads[primary_key]
@@ -275,7 +284,7 @@ def main():
 
     secondary = []
     if not args.quick and args.only is None:
-        for key in ("f32-15231", "f32-60926", "bf16-60926"):
+        for key in ("f32-15231", "f32-60926", "bf16-60926", "f16-60926"):
             nm, Ls, dts = workloads[key]
             xs = synth.gqa(1, HQ, HKV, Ls, seed=0, dtype=dts)
             r = run_fwd_workload(nm, xs, max(3, args.steps // 2), 2, torch, gqa, work)
@@ -295,7 +304,7 @@ def main():
         secondary.append(r)
         del xs
     for r in [prim] + secondary:
-        dts = "bf16" if "bf16" in r["workload"] else "f32"
+        dts = "bf16" if "bf16" in r["workload"] else "f16" if "fp16" in r["workload"] else "f32"
         r["pct_mfma_peak"] = 100.0 * r["kernel_tflops"] / work.PEAK_TFLOPS[dts]
 
     math_gib = work.score_matrix_bytes(HQ, L, L, 4) / 2 ** 30

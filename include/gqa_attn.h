@@ -28,8 +28,11 @@
  *   lse   [B, Hq,  Lq]      fp32, natural log
  *   seg_q [B, Lq], seg_k [B, Lk]  int32 (any values; sorted ids skip more work)
  * All pointers are device pointers on the current HIP device. Accumulation is
- * fp32; bf16 outputs are rounded to nearest even. fp32 inputs use full-fp32
- * matrix instructions (no reduced-precision products).
+ * fp32; bf16 and fp16 outputs are rounded to nearest even, and so are the
+ * softmax weights that enter the P V product in those types. fp32 inputs use
+ * full-fp32 matrix instructions (no reduced-precision products). fp16 is the
+ * other half-width input type that the same fast path serves (kev pull request
+ * 202, "The change": bf16 and fp16 calls keep the fused kernels).
  *
  * Ownership and threading. The caller allocates every buffer. The library
  * allocates no device memory, keeps no pointer after returning and never
@@ -51,13 +54,13 @@
 extern "C" {
 #endif
 
-enum gqa_dtype { GQA_F32 = 0, GQA_BF16 = 1 };
+enum gqa_dtype { GQA_F32 = 0, GQA_BF16 = 1, GQA_F16 = 2 };
 
 enum gqa_status {
   GQA_OK = 0,
   GQA_ERR_NULL = 1,        /* q, k, v, o or lse is NULL */
   GQA_ERR_SHAPE = 2,       /* an extent <= 0, Hq % Hkv != 0, q_offset < 0, or exactly one segment pointer NULL */
-  GQA_ERR_UNSUPPORTED = 3, /* D != 256, dtype not F32/BF16, Hq/Hkv not in {1,2,4,8,16}, or Lq/Lk >= 2^31 */
+  GQA_ERR_UNSUPPORTED = 3, /* D != 256, dtype not F32/BF16/F16, Hq/Hkv not in {1,2,4,8,16}, or Lq/Lk >= 2^31 */
   GQA_ERR_ALIGN = 4,       /* q, k, v, o not 16-byte aligned, or lse/seg not 4-byte aligned */
   GQA_ERR_LAUNCH = 5,      /* the HIP runtime reported an error at launch */
   GQA_ERR_ALIAS = 6        /* o overlaps q, k or v (or, for merge, partially overlaps an input) */

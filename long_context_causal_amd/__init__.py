@@ -14,7 +14,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgqa_attn.so")
 
-GQA_F32, GQA_BF16 = 0, 1
+GQA_F32, GQA_BF16, GQA_F16 = 0, 1, 2
 STATUS = {0: "GQA_OK", 1: "GQA_ERR_NULL", 2: "GQA_ERR_SHAPE", 3: "GQA_ERR_UNSUPPORTED",
           4: "GQA_ERR_ALIGN", 5: "GQA_ERR_LAUNCH", 6: "GQA_ERR_ALIAS"}
 EXPORTS = ("gqa_attn_fwd", "gqa_attn_merge", "gqa_attn_strerror", "gqa_attn_version")
@@ -75,7 +75,9 @@ def _dtype_code(t):
         return GQA_F32
     if t.dtype == torch.bfloat16:
         return GQA_BF16
-    raise TypeError("tensors must be float32 or bfloat16, got %s" % t.dtype)
+    if t.dtype == torch.float16:
+        return GQA_F16
+    raise TypeError("tensors must be float32, bfloat16 or float16, got %s" % t.dtype)
 
 
 def _check_dev(*ts):
@@ -95,7 +97,7 @@ def _stream_ptr(stream):
 
 
 def fwd(q, k, v, *, causal=True, q_offset=0, seg_q=None, seg_k=None, out=None, lse=None, stream=None):
-    """Attention forward: q [B,Hq,Lq,D], k/v [B,Hkv,Lk,D] (fp32 or bf16, same dtype),
+    """Attention forward: q [B,Hq,Lq,D], k/v [B,Hkv,Lk,D] (fp32, bf16 or fp16, same dtype),
     optional int32 segment ids seg_q [B,Lq] / seg_k [B,Lk]. Returns (o, lse) with
     o like q and lse [B,Hq,Lq] fp32. Work is enqueued on `stream` (default: the
     current stream)."""

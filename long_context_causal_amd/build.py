@@ -23,6 +23,8 @@ COMMON_FLAGS = [
     # lets fmaxf lower to a plain v_max without canonicalising its operands
     "-fno-honor-nans",
     "-Wall", "-Wno-unused-function",
+    # only the C ABI is exported (gqa_attn.hip marks it); kernels and helpers stay internal
+    "-fvisibility=hidden",
 ]
 
 # MFMA accumulators in the VGPR file: in the fp32 kernel the O accumulator is
@@ -31,12 +33,12 @@ COMMON_FLAGS = [
 # iteration.
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 
-# translation unit -> extra flags. The bf16 kernel keeps its O accumulator in
-# AGPRs (Q, scores and fragments fill the VGPRs).
+# translation unit -> extra flags. The 16-bit-input (bf16, fp16) kernel keeps
+# its O accumulator in AGPRs (Q, scores and fragments fill the VGPRs).
 UNITS = {
     "gqa_attn.hip": [],
     "fwd_f32.hip": VGPR_FORM,
-    "fwd_bf16.hip": [],
+    "fwd_h16.hip": [],
 }
 
 # hipcc's host pass does not know the packed-fp32 target feature; that warning is expected

@@ -1,5 +1,7 @@
-// fwd_bf16.hpp -- causal grouped-query attention forward, bf16 inputs, fp32
-// accumulation, on gfx950 bf16 MFMA (v_mfma_f32_32x32x16_bf16).
+// fwd_h16.hpp -- causal grouped-query attention forward for 16-bit inputs
+// (bf16 or fp16), fp32 accumulation, on gfx950 MFMA (v_mfma_f32_32x32x16_bf16
+// / _f16). The element type only changes the products' opcode and the
+// conversions to it (round to nearest even); the layouts are the same.
 //
 // One workgroup = 4 waves, one per SIMD. For Hq/Hkv = 4 the workgroup owns the
 // 4 query heads of one KV head x 32 positions; each wave owns one head and 32
@@ -47,6 +49,48 @@ constexpr float kLazy = 8.0f;               // lazy-rescale threshold (log2 unit
 constexpr int kVPre = 6;                    // V fragments in flight in phase B (the first read in phase A)
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+
+// The two 16-bit element types: the 8-element operand vector of a 32x32x16
+// product, the product itself, a pair packed with round-to-nearest-even, and
+// the rounded pair's sum accumulated (v_dot2 with ones).
+template <typename E>
+struct Elem;
+template <>
+struct Elem<__bf16> {
+  typedef bf16x8 v8;
+  static __device__ __forceinline__ f32x16 mfma(v8 a, v8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ unsigned pack(float a, float b) {
+    bf16x2 r;
+    r[0] = (__bf16)a;
+    r[1] = (__bf16)b;
+    return __builtin_bit_cast(unsigned, r);
+  }
+  static __device__ __forceinline__ float sum2(unsigned pair, float acc) {
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), ones, acc, false);
+  }
+};
+template <>
+struct Elem<_Float16> {
+  typedef f16x8 v8;
+  static __device__ __forceinline__ f32x16 mfma(v8 a, v8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ unsigned pack(float a, float b) {
+    f16x2 r;
+    r[0] = (_Float16)a;
+    r[1] = (_Float16)b;
+    return __builtin_bit_cast(unsigned, r);
+  }
+  static __device__ __forceinline__ float sum2(unsigned pair, float acc) {
+    const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pair), ones, acc, false);
+  }
+};
 
 // LDS image of a bf16 tile: 512-byte key rows of 32 16-byte chunks; chunk c of
 // key k is stored at chunk c ^ swz_k(k) in K tiles and c ^ swz_v(k) in V tiles.
@@ -65,15 +109,7 @@ struct SmemB {
   SegBits bits;
 };
 
-__device__ __forceinline__ unsigned pack_bf16(float a, float b) {
-  bf16x2 r;
-  r[0] = (__bf16)a;
-  r[1] = (__bf16)b;
-  return __builtin_bit_cast(unsigned, r);
-}
-
 typedef __attribute__((address_space(3))) const char lds_cchar;
-typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((ext_vector_type(4))) int i32x4;
 typedef __attribute__((address_space(3))) const i32x4 lds_i32x4;
@@ -150,12 +186,13 @@ __device__ __forceinline__ PartCopy part_copy(uint32_t lds, uint32_t s_lds, cons
 // V^T fragment for d block n (32 d) and key quarter h (16 keys) of a stage
 // whose read bases are vb[]: keys 16 h + 4 g + 0..3 then 16 h + 8 + 4 g + 0..3
 // (g = lane / 32), d 32 n + lane % 32.
-__device__ __forceinline__ bf16x8 v_frag(int n, int h, lds_cchar* const* vb) {
+template <typename V8>
+__device__ __forceinline__ V8 v_frag(int n, int h, lds_cchar* const* vb) {
   lds_cchar* a = vb[n & 3] + ((n >> 2) * 256 + h * 8192);
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)a);
   const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a + 4096));
   const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
-  return __builtin_bit_cast(bf16x8, u32x4{lo2[0], lo2[1], hi2[0], hi2[1]});
+  return __builtin_bit_cast(V8, u32x4{lo2[0], lo2[1], hi2[0], hi2[1]});
 }
 
 // Online-softmax state of the wave's rows (per lane: its row). l sums the
@@ -215,6 +252,7 @@ __device__ __forceinline__ float softmax_max(const f32x16* s, RowState& rs, floa
 // issues in order, and an exp result takes several cycles); slots 32 and 33
 // drain the pipeline. Score e is s[e / 16][e % 16]; P pair f / 2 goes to pk,
 // and key quarter h of the PV product takes pk[4 h .. 4 h + 3].
+template <typename E>
 struct ExpPipe {
   float t[32], x[32];
   float lsum = 0.f, lrsum = 0.f;
@@ -225,9 +263,8 @@ struct ExpPipe {
       const int f = e - 2;
       lsum += x[f];
       if (f & 1) {
-        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-        pk[f >> 1] = pack_bf16(x[f - 1], x[f]);
-        lrsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[f >> 1]), ones, lrsum, false);
+        pk[f >> 1] = Elem<E>::pack(x[f - 1], x[f]);
+        lrsum = Elem<E>::sum2(pk[f >> 1], lrsum);
       }
     }
   }
@@ -241,9 +278,11 @@ struct ExpPipe {
 // QK product q (0..31) of a tile: key half q % 2, d chunk q / 2 (16 d); the
 // two halves are independent chains, interleaved. K fragments are read three
 // products ahead from a stage whose read bases are kb[].
-__device__ __forceinline__ bf16x8 k_frag(int q, lds_cchar* const* kb) {
+template <typename V8>
+__device__ __forceinline__ V8 k_frag(int q, lds_cchar* const* kb) {
+  typedef __attribute__((address_space(3))) const V8 lds_v8;
   const int j = q & 1, c = q >> 1;
-  return *(lds_bf16x8*)(kb[c & 7] + ((c >> 3) * 256 + j * 16384));
+  return *(lds_v8*)(kb[c & 7] + ((c >> 3) * 256 + j * 16384));
 }
 
 // Phase A: S^T(next) = K Q^T for the tile in K stage kst (32 MFMAs over
@@ -251,26 +290,28 @@ __device__ __forceinline__ bf16x8 k_frag(int q, lds_cchar* const* kb) {
 // tile copies (K and ids of the tile two ahead, V of the tile one ahead: early
 // enough that they land before the next barrier), and the first V fragments
 // of phase B (already resident).
-__device__ __forceinline__ void phase_a(int kst, const bf16x8* qf, const LanesB& ln, f32x16* s_nxt,
-                                        const f32x16* s_cur, float sl2, float m_use, unsigned* pk, ExpPipe& ep,
+template <typename E>
+__device__ __forceinline__ void phase_a(int kst, const typename Elem<E>::v8* qf, const LanesB& ln, f32x16* s_nxt,
+                                        const f32x16* s_cur, float sl2, float m_use, unsigned* pk, ExpPipe<E>& ep,
                                         const PartCopy& kc, const PartCopy& vc, bool seg, int wave, int lane,
-                                        lds_cchar* const* vb, bf16x8* vf) {
+                                        lds_cchar* const* vb, typename Elem<E>::v8* vf) {
+  typedef typename Elem<E>::v8 V8;
   lds_cchar* kb[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) kb[j] = ln.k[j] + kst * kTileBytesB;
-  bf16x8 kf[3];
+  V8 kf[3];
 #pragma unroll
-  for (int q = 0; q < 3; ++q) kf[q] = k_frag(q, kb);
+  for (int q = 0; q < 3; ++q) kf[q] = k_frag<V8>(q, kb);
 #pragma unroll
   for (int q = 0; q < 32; ++q) {
     const int j = q & 1, c = q >> 1;
-    s_nxt[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[q % 3], qf[c], c == 0 ? f32x16{} : s_nxt[j], 0, 0, 0);
-    if (q + 3 < 32) kf[q % 3] = k_frag(q + 3, kb);
+    s_nxt[j] = Elem<E>::mfma(kf[q % 3], qf[c], c == 0 ? f32x16{} : s_nxt[j]);
+    if (q + 3 < 32) kf[q % 3] = k_frag<V8>(q + 3, kb);
     ep.slot(q, s_cur, sl2, m_use, pk);
     if ((q & 3) == 1) kc.rows(ln.ldk, q >> 2, wave);
     if ((q & 3) == 3) vc.rows(ln.ldv, q >> 2, wave);
     if (q == 2 && seg) kc.ids(wave, lane);
-    if (q >= 32 - kVPre) vf[q - (32 - kVPre)] = v_frag(q - (32 - kVPre), 0, vb);
+    if (q >= 32 - kVPre) vf[q - (32 - kVPre)] = v_frag<V8>(q - (32 - kVPre), 0, vb);
     GQA_SEGMENT_END();
   }
   // Anchor the slot results in this block: their users lie past the mask
@@ -281,18 +322,20 @@ __device__ __forceinline__ void phase_a(int kst, const bf16x8* qf, const LanesB&
 }
 
 // QK alone (the first tile of a row block).
-__device__ __forceinline__ void qk_only(int kst, const bf16x8* qf, const LanesB& ln, f32x16* s) {
+template <typename E>
+__device__ __forceinline__ void qk_only(int kst, const typename Elem<E>::v8* qf, const LanesB& ln, f32x16* s) {
+  typedef typename Elem<E>::v8 V8;
   lds_cchar* kb[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) kb[j] = ln.k[j] + kst * kTileBytesB;
-  bf16x8 kf[3];
+  V8 kf[3];
 #pragma unroll
-  for (int q = 0; q < 3; ++q) kf[q] = k_frag(q, kb);
+  for (int q = 0; q < 3; ++q) kf[q] = k_frag<V8>(q, kb);
 #pragma unroll
   for (int q = 0; q < 32; ++q) {
     const int j = q & 1, c = q >> 1;
-    s[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[q % 3], qf[c], c == 0 ? f32x16{} : s[j], 0, 0, 0);
-    if (q + 3 < 32) kf[q % 3] = k_frag(q + 3, kb);
+    s[j] = Elem<E>::mfma(kf[q % 3], qf[c], c == 0 ? f32x16{} : s[j]);
+    if (q + 3 < 32) kf[q % 3] = k_frag<V8>(q + 3, kb);
   }
 }
 
@@ -313,13 +356,14 @@ __device__ __forceinline__ void rescale(f32x16* acc, RowState& rs, float alpha) 
 }
 
 // Everything one workgroup's wave needs inside the tile loop.
-template <bool SEG>
-struct Bf16Wave {
+template <typename E, bool SEG>
+struct H16Wave {
+  typedef typename Elem<E>::v8 V8;
   const FwdParams& p;
   SmemB& sm;
   LanesB ln;
   RingBase rb;
-  bf16x8 qf[16];
+  V8 qf[16];
   f32x16 acc[8];
   f32x16 s_cur[2];
   RowState rs;
@@ -331,7 +375,7 @@ struct Bf16Wave {
   bool use_bits;
   int cur, nxt, nn;  // visible tiles: being finished, QK this step, next after that
 
-  __device__ __forceinline__ Bf16Wave(const FwdParams& p_, SmemB& sm_) : p(p_), sm(sm_) {}
+  __device__ __forceinline__ H16Wave(const FwdParams& p_, SmemB& sm_) : p(p_), sm(sm_) {}
 
   __device__ __forceinline__ int next_tile(int t) const {
     if (t >= n_tiles) return n_tiles;
@@ -364,8 +408,8 @@ struct Bf16Wave {
   // products ahead) with the last exp slots of this tile, the row max of the
   // next scores s_nxt (masked first where needed; ids in K stage kst1) spread
   // over the products, and the lazy update of the running max. Returns alpha.
-  __device__ __forceinline__ float phase_b(int kst1, f32x16* s_nxt, unsigned* pk, ExpPipe& ep,
-                                           lds_cchar* const* vbs, bf16x8* vf) {
+  __device__ __forceinline__ float phase_b(int kst1, f32x16* s_nxt, unsigned* pk, ExpPipe<E>& ep,
+                                           lds_cchar* const* vbs, V8* vf) {
     const float sl2 = p.scale_log2;
     const float m_cur = rs.m_use;
     mask_if_needed(s_nxt, nxt, kst1);
@@ -373,9 +417,9 @@ struct Bf16Wave {
 #pragma unroll
     for (int u = 0; u < 32; ++u) {
       const int n = u & 7, h = u >> 3;
-      const bf16x8 ph = __builtin_bit_cast(bf16x8, u32x4{pk[4 * h], pk[4 * h + 1], pk[4 * h + 2], pk[4 * h + 3]});
-      acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[u % kVPre], ph, acc[n], 0, 0, 0);
-      if (u + kVPre < 32) vf[u % kVPre] = v_frag((u + kVPre) & 7, (u + kVPre) >> 3, vbs);
+      const V8 ph = __builtin_bit_cast(V8, u32x4{pk[4 * h], pk[4 * h + 1], pk[4 * h + 2], pk[4 * h + 3]});
+      acc[n] = Elem<E>::mfma(vf[u % kVPre], ph, acc[n]);
+      if (u + kVPre < 32) vf[u % kVPre] = v_frag<V8>((u + kVPre) & 7, (u + kVPre) >> 3, vbs);
       if (u < 2) ep.slot(32 + u, s_cur, sl2, m_cur, pk);
       if (u >= 2 && u < 18) {
         const int r = u - 2;
@@ -403,13 +447,13 @@ struct Bf16Wave {
     const PartCopy kc = k_copy(st, nn);   // K(#i+2) into K(#i)'s stage
     const PartCopy vc = v_copy(st1, nxt);  // V(#i+1) into V(#i-1)'s stage
     unsigned pk[16];
-    ExpPipe ep;
+    ExpPipe<E> ep;
     f32x16 s_nxt[2];
     lds_cchar* vbs[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) vbs[j] = ln.v[j] + st * kTileBytesB;
-    bf16x8 vf[kVPre];
-    phase_a(st1, qf, ln, s_nxt, s_cur, p.scale_log2, rs.m_use, pk, ep, kc, vc, SEG, wave, lane, vbs, vf);
+    V8 vf[kVPre];
+    phase_a<E>(st1, qf, ln, s_nxt, s_cur, p.scale_log2, rs.m_use, pk, ep, kc, vc, SEG, wave, lane, vbs, vf);
     const float alpha = phase_b(st1, s_nxt, pk, ep, vbs, vf);
     rescale(acc, rs, alpha);
     s_cur[0] = s_nxt[0];
@@ -420,10 +464,11 @@ struct Bf16Wave {
   }
 };
 
-template <bool SEG>
-__global__ __launch_bounds__(kWavesB * 64) void fwd_bf16_kernel(FwdParams p) {
+template <typename E, bool SEG>
+__global__ __launch_bounds__(kWavesB * 64) void fwd_h16_kernel(FwdParams p) {
+  typedef typename Elem<E>::v8 V8;
   __shared__ SmemB sm;
-  Bf16Wave<SEG> wv(p, sm);
+  H16Wave<E, SEG> wv(p, sm);
   const Work w = decode_work(p);
   wv.wave = wave_id();
   wv.lane = lane_id();
@@ -451,7 +496,7 @@ __global__ __launch_bounds__(kWavesB * 64) void fwd_bf16_kernel(FwdParams p) {
   // Q in registers, B-operand layout: lane holds Q[row][16 c + 8 g .. + 7].
   const int64_t hq = ((int64_t)w.b * p.Hq + h) * p.Lq;
   {
-    const bf16x8* qr = (const bf16x8*)((const char*)p.q + (hq + row_c) * kD * 2);
+    const V8* qr = (const V8*)((const char*)p.q + (hq + row_c) * kD * 2);
 #pragma unroll
     for (int c = 0; c < 16; ++c) wv.qf[c] = qr[2 * c + wv.g];
   }
@@ -482,13 +527,13 @@ __global__ __launch_bounds__(kWavesB * 64) void fwd_bf16_kernel(FwdParams p) {
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    qk_only(0, wv.qf, wv.ln, wv.s_cur);
+    qk_only<E>(0, wv.qf, wv.ln, wv.s_cur);
     wv.mask_if_needed(wv.s_cur, wv.cur, 0);
     (void)softmax_max(wv.s_cur, wv.rs, p.scale_log2);  // nothing accumulated yet: no rescale
     for (int i = 0; wv.cur < wv.n_tiles; ++i) wv.step(i);
   }
 
-  // epilogue: O = acc / lr (bf16), lse = ln2 (m + log2 l); lane holds
+  // epilogue: O = acc / lr (in E), lse = ln2 (m + log2 l); lane holds
   // O[row][32 n + 8 j + 4 g + i] in acc[n][4 j + i]
 #pragma unroll
   for (int n = 0; n < 8; ++n) asm volatile("" : "+a"(wv.acc[n]));
@@ -501,8 +546,8 @@ __global__ __launch_bounds__(kWavesB * 64) void fwd_bf16_kernel(FwdParams p) {
     for (int n = 0; n < 8; ++n)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const u32x2 val = {pack_bf16(wv.acc[n][4 * j] * inv, wv.acc[n][4 * j + 1] * inv),
-                           pack_bf16(wv.acc[n][4 * j + 2] * inv, wv.acc[n][4 * j + 3] * inv)};
+        const u32x2 val = {Elem<E>::pack(wv.acc[n][4 * j] * inv, wv.acc[n][4 * j + 1] * inv),
+                           Elem<E>::pack(wv.acc[n][4 * j + 2] * inv, wv.acc[n][4 * j + 3] * inv)};
         *(u32x2*)(op + (32 * n + 8 * j + 4 * wv.g) * 2) = val;
       }
     if (wv.g == 0)

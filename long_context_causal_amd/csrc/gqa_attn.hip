@@ -24,7 +24,10 @@ bool is_pow2_rep(int64_t r) { return r == 1 || r == 2 || r == 4 || r == 8 || r =
 
 }  // namespace
 
-extern "C" int gqa_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+// The library is built with hidden visibility; these are its only exports.
+#define GQA_API extern "C" __attribute__((visibility("default")))
+
+GQA_API int gqa_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                             int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
                             int64_t q_offset, const int32_t* seg_q, const int32_t* seg_k,
                             int causal, int dtype, void* stream) {
@@ -32,7 +35,7 @@ extern "C" int gqa_attn_fwd(const void* q, const void* k, const void* v, void* o
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Lq <= 0 || Lk <= 0 || D <= 0) return GQA_ERR_SHAPE;
   if (Hq % Hkv != 0 || q_offset < 0 || q_offset > ((int64_t)1 << 62)) return GQA_ERR_SHAPE;
   if ((seg_q == nullptr) != (seg_k == nullptr)) return GQA_ERR_SHAPE;
-  if (D != gqa::kD || (dtype != GQA_F32 && dtype != GQA_BF16)) return GQA_ERR_UNSUPPORTED;
+  if (D != gqa::kD || (dtype != GQA_F32 && dtype != GQA_BF16 && dtype != GQA_F16)) return GQA_ERR_UNSUPPORTED;
   const int64_t n_rep = Hq / Hkv;
   if (!is_pow2_rep(n_rep) || Lq >= ((int64_t)1 << 31) || Lk >= ((int64_t)1 << 31) || B * Hkv >= ((int64_t)1 << 24))
     return GQA_ERR_UNSUPPORTED;
@@ -46,14 +49,14 @@ extern "C" int gqa_attn_fwd(const void* q, const void* k, const void* v, void* o
       overlap(lse, lse_bytes, k, kv_bytes) || overlap(lse, lse_bytes, v, kv_bytes))
     return GQA_ERR_ALIAS;
 
-  const int W = dtype == GQA_F32 ? gqa::kWavesF32 : gqa::kWavesBf16;
+  const int W = dtype == GQA_F32 ? gqa::kWavesF32 : gqa::kWavesH16;
   gqa::FwdParams p;
   p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
   p.seg_q = seg_q; p.seg_k = seg_k;
   p.Lq = Lq; p.Lk = Lk; p.q_offset = q_offset;
   p.Hq = (int)Hq; p.Hkv = (int)Hkv; p.n_rep = (int)n_rep;
   p.hpc = (int)(n_rep < W ? n_rep : W);
-  p.ppc = (W / p.hpc) * (dtype == GQA_F32 ? gqa::kRowsF32 : gqa::kRowsBf16);
+  p.ppc = (W / p.hpc) * (dtype == GQA_F32 ? gqa::kRowsF32 : gqa::kRowsH16);
   const int64_t n_qb = (Lq + p.ppc - 1) / p.ppc;
   const int64_t G = B * Hkv * (n_rep / p.hpc);
   if (n_qb * G >= ((int64_t)1 << 31)) return GQA_ERR_UNSUPPORTED;
@@ -64,15 +67,18 @@ extern "C" int gqa_attn_fwd(const void* q, const void* k, const void* v, void* o
 
   hipStream_t s = (hipStream_t)stream;
   (void)hipGetLastError();
-  const hipError_t e = dtype == GQA_F32 ? gqa::launch_fwd_f32(p, s) : gqa::launch_fwd_bf16(p, s);
+  const hipError_t e = dtype == GQA_F32    ? gqa::launch_fwd_f32(p, s)
+                       : dtype == GQA_BF16 ? gqa::launch_fwd_bf16(p, s)
+                                           : gqa::launch_fwd_f16(p, s);
   return e == hipSuccess ? GQA_OK : GQA_ERR_LAUNCH;
 }
 
-extern "C" int gqa_attn_merge(const void* o1, const float* lse1, const void* o2, const float* lse2,
+GQA_API int gqa_attn_merge(const void* o1, const float* lse1, const void* o2, const float* lse2,
                               void* o, float* lse, int64_t rows, int64_t D, int dtype, void* stream) {
   if (!o1 || !lse1 || !o2 || !lse2 || !o || !lse) return GQA_ERR_NULL;
   if (rows <= 0 || D <= 0) return GQA_ERR_SHAPE;
-  if (D % 8 != 0 || (dtype != GQA_F32 && dtype != GQA_BF16) || rows >= ((int64_t)1 << 33)) return GQA_ERR_UNSUPPORTED;
+  if (D % 8 != 0 || (dtype != GQA_F32 && dtype != GQA_BF16 && dtype != GQA_F16) || rows >= ((int64_t)1 << 33))
+    return GQA_ERR_UNSUPPORTED;
   if (misaligned(o1, 16) || misaligned(o2, 16) || misaligned(o, 16) || misaligned(lse1, 4) ||
       misaligned(lse2, 4) || misaligned(lse, 4))
     return GQA_ERR_ALIGN;
@@ -88,18 +94,21 @@ extern "C" int gqa_attn_merge(const void* o1, const float* lse1, const void* o2,
   if (dtype == GQA_F32)
     hipLaunchKernelGGL(gqa::merge_kernel<float>, grid, dim3(256), 0, s, (const float*)o1, lse1, (const float*)o2,
                        lse2, (float*)o, lse, rows, D);
-  else
+  else if (dtype == GQA_BF16)
     hipLaunchKernelGGL(gqa::merge_kernel<__bf16>, grid, dim3(256), 0, s, (const __bf16*)o1, lse1,
                        (const __bf16*)o2, lse2, (__bf16*)o, lse, rows, D);
+  else
+    hipLaunchKernelGGL(gqa::merge_kernel<_Float16>, grid, dim3(256), 0, s, (const _Float16*)o1, lse1,
+                       (const _Float16*)o2, lse2, (_Float16*)o, lse, rows, D);
   return hipGetLastError() == hipSuccess ? GQA_OK : GQA_ERR_LAUNCH;
 }
 
-extern "C" const char* gqa_attn_strerror(int code) {
+GQA_API const char* gqa_attn_strerror(int code) {
   switch (code) {
     case GQA_OK: return "success";
     case GQA_ERR_NULL: return "a required pointer is NULL";
     case GQA_ERR_SHAPE: return "invalid shape: non-positive extent, Hq not a multiple of Hkv, negative q_offset, or only one segment-id array";
-    case GQA_ERR_UNSUPPORTED: return "unsupported: D must be 256, dtype F32 or BF16, Hq/Hkv in {1,2,4,8,16}, lengths below 2^31";
+    case GQA_ERR_UNSUPPORTED: return "unsupported: D must be 256, dtype F32, BF16 or F16, Hq/Hkv in {1,2,4,8,16}, lengths below 2^31";
     case GQA_ERR_ALIGN: return "misaligned pointer: tensors need 16-byte alignment, lse and segment ids 4-byte";
     case GQA_ERR_LAUNCH: return "kernel launch failed";
     case GQA_ERR_ALIAS: return "output overlaps an input";
@@ -107,4 +116,4 @@ extern "C" const char* gqa_attn_strerror(int code) {
   }
 }
 
-extern "C" int gqa_attn_version(void) { return (1 << 16) | 0; }
+GQA_API int gqa_attn_version(void) { return (1 << 16) | 1; }

@@ -1,5 +1,5 @@
 // launch.hpp -- launchers of the forward kernels, each defined in the
-// translation unit of its kernel (fwd_f32.hip, fwd_bf16.hip) so that each
+// translation unit of its kernel (fwd_f32.hip, fwd_h16.hip) so that each
 // kernel is compiled with its own code-generation flags.
 #pragma once
 #include <hip/hip_runtime.h>
@@ -10,11 +10,12 @@ namespace gqa {
 
 // Workgroup shapes the host plan needs: waves per workgroup and query rows per wave.
 constexpr int kWavesF32 = 4, kRowsF32 = 32;
-constexpr int kWavesBf16 = 4, kRowsBf16 = 32;
+constexpr int kWavesH16 = 4, kRowsH16 = 32;  // bf16 and fp16
 
 // Enqueue one forward launch (grid = p.n_qb * p.G workgroups); returns
 // hipGetLastError() after the launch.
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream);
+hipError_t launch_fwd_f16(const FwdParams& p, hipStream_t stream);
 
 }  // namespace gqa

@@ -26,6 +26,13 @@ __device__ __forceinline__ void load8<__bf16>(const __bf16* src, float* x) {
     x[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
   }
 }
+template <>
+__device__ __forceinline__ void load8<_Float16>(const _Float16* src, float* x) {
+  typedef __attribute__((ext_vector_type(8))) _Float16 h8;
+  const h8 u = *(const h8*)src;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = (float)u[i];
+}
 template <typename T>
 __device__ __forceinline__ void store8(T* dst, const float* x);
 template <>
@@ -45,6 +52,14 @@ __device__ __forceinline__ void store8<__bf16>(__bf16* dst, const float* x) {
     u[i] = __builtin_bit_cast(unsigned, r);
   }
   *(u32x4*)dst = u;
+}
+template <>
+__device__ __forceinline__ void store8<_Float16>(_Float16* dst, const float* x) {
+  typedef __attribute__((ext_vector_type(8))) _Float16 h8;
+  h8 u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) u[i] = (_Float16)x[i];
+  *(h8*)dst = u;
 }
 
 template <typename T>

@@ -52,5 +52,5 @@ def score_matrix_bytes(Hq: int, Lq: int, Lk: int, elem_bytes: int = 4) -> int:
 
 
 # MI355X published peaks (dense): bf16 MFMA 2.5 PFLOP/s, fp32 157.3 TFLOP/s, HBM 8 TB/s
-PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6}
+PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6, "f16": 2516.6}
 PEAK_HBM_GBS = 8000.0

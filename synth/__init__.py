@@ -1,7 +1,8 @@
 """Seeded synthetic inputs shared by the tests, the smoke check and the benchmark.
 
 This module holds no attention arithmetic: it only draws random tensors, rounds
-fp32 draws to bf16 bit patterns, lays out segment ids and picks sample rows.
+fp32 draws to bf16 or fp16 bit patterns, lays out segment ids and picks sample
+rows.
 Both the HIP path and the CPU oracle receive exactly the bytes made here.
 
 Workload shapes stand in for the pages' inputs (post-RoPE activations of Kev
@@ -29,24 +30,40 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
+def f32_to_f16_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp32 values to fp16 bit patterns, round-to-nearest-even (numpy's
+    conversion; values stay well inside the fp16 range here)."""
+    return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def f16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Widen fp16 bit patterns to fp32 (exact)."""
+    return np.ascontiguousarray(b, dtype=np.uint16).view(np.float16).astype(np.float32)
+
+
+_ROUND = {"bf16": (f32_to_bf16_bits, bf16_bits_to_f32), "f16": (f32_to_f16_bits, f16_bits_to_f32)}
+
+
 class Inputs:
-    """q [B,Hq,Lq,D], k/v [B,Hkv,Lk,D] as fp32 values (already bf16-exact when
-    dtype is bf16) plus, for bf16, the raw bit patterns the device receives."""
+    """q [B,Hq,Lq,D], k/v [B,Hkv,Lk,D] as fp32 values (already exact in the
+    16-bit type when dtype is bf16 or f16) plus, for those, the raw bit patterns
+    the device receives."""
 
     def __init__(self, q, k, v, dtype, seg_q=None, seg_k=None, q_offset=0, causal=True):
         self.q, self.k, self.v = q, k, v
         self.dtype = dtype
         self.seg_q, self.seg_k = seg_q, seg_k
         self.q_offset, self.causal = q_offset, causal
-        if dtype == "bf16":
-            self.q_bits = f32_to_bf16_bits(q)
-            self.k_bits = f32_to_bf16_bits(k)
-            self.v_bits = f32_to_bf16_bits(v)
-            self.q = bf16_bits_to_f32(self.q_bits)
-            self.k = bf16_bits_to_f32(self.k_bits)
-            self.v = bf16_bits_to_f32(self.v_bits)
+        if dtype in _ROUND:
+            to_bits, to_f32 = _ROUND[dtype]
+            self.q_bits = to_bits(q)
+            self.k_bits = to_bits(k)
+            self.v_bits = to_bits(v)
+            self.q = to_f32(self.q_bits)
+            self.k = to_f32(self.k_bits)
+            self.v = to_f32(self.v_bits)
         elif dtype != "f32":
-            raise ValueError("dtype must be 'f32' or 'bf16'")
+            raise ValueError("dtype must be 'f32', 'bf16' or 'f16'")
 
 
 def gqa(B=1, Hq=HQ, Hkv=HKV, Lq=512, Lk=None, Dh=D, *, seed=0, scale=1.0, dtype="f32",

@@ -39,10 +39,13 @@ def test_library_exports_every_declared_function():
     out = subprocess.run(["nm", "-D", "--defined-only", gqa.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\sT\s(gqa_attn_\w+)", out))
     assert set(names) <= exported
+    # and nothing else: the kernels, launchers and helpers stay internal
+    functions = set(re.findall(r"\s[TW]\s(\S+)", out))
+    assert functions == exported, sorted(functions - exported)[:5]
 
 
 def test_version_and_strerror():
-    assert gqa.version() == (1, 0)
+    assert gqa.version() == (1, 1)
     msgs = [gqa.strerror(c) for c in range(7)]
     assert len(set(msgs)) == 7 and msgs[0] == "success"
     assert "unknown" in gqa.strerror(99)
@@ -52,7 +55,7 @@ def test_version_and_strerror():
     (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(o=None), 1), (dict(lse=None), 1),
     (dict(B=0), 2), (dict(Hq=0), 2), (dict(Hkv=0), 2), (dict(Lq=0), 2), (dict(Lk=-1), 2), (dict(D=0), 2),
     (dict(Hq=16, Hkv=3), 2), (dict(q_offset=-1), 2), (dict(seg_q=SQ), 2), (dict(seg_k=SK), 2),
-    (dict(D=128), 3), (dict(dtype=2), 3), (dict(Hq=12, Hkv=4), 3), (dict(Hq=32, Hkv=1), 3),
+    (dict(D=128), 3), (dict(dtype=3), 3), (dict(dtype=-1), 3), (dict(Hq=12, Hkv=4), 3), (dict(Hq=32, Hkv=1), 3),
     (dict(Lq=1 << 31), 3), (dict(Lk=1 << 31), 3),
     (dict(q=Q + 2), 4), (dict(k=K + 8), 4), (dict(v=V + 4), 4), (dict(o=O + 2), 4), (dict(lse=LSE + 2), 4),
     (dict(seg_q=SQ + 2, seg_k=SK), 4),
