@@ -60,7 +60,8 @@ enum gqa_status {
   GQA_OK = 0,
   GQA_ERR_NULL = 1,        /* q, k, v, o or lse is NULL */
   GQA_ERR_SHAPE = 2,       /* an extent <= 0, Hq % Hkv != 0, q_offset < 0, or exactly one segment pointer NULL */
-  GQA_ERR_UNSUPPORTED = 3, /* D != 256, dtype not F32/BF16/F16, Hq/Hkv not in {1,2,4,8,16}, or Lq/Lk >= 2^31 */
+  GQA_ERR_UNSUPPORTED = 3, /* D != 256, dtype not F32/BF16/F16, Hq/Hkv not in {1,2,4,8,16}, or Lq/Lk >= 2^31
+                              (backward: Lq/Lk > 2^21, or a dtype its kernels do not cover) */
   GQA_ERR_ALIGN = 4,       /* q, k, v, o not 16-byte aligned, or lse/seg not 4-byte aligned */
   GQA_ERR_LAUNCH = 5,      /* the HIP runtime reported an error at launch */
   GQA_ERR_ALIAS = 6        /* o overlaps q, k or v (or, for merge, partially overlaps an input) */
@@ -89,6 +90,42 @@ int gqa_attn_fwd(const void* q, const void* k, const void* v, void* o, float* ls
  */
 int gqa_attn_merge(const void* o1, const float* lse1, const void* o2, const float* lse2,
                    void* o, float* lse, int64_t rows, int64_t D, int dtype, void* stream);
+
+/*
+ * Attention backward: the gradients of a scalar loss with respect to q, k and
+ * v, given its gradient `dout` with respect to o. The pages train at these
+ * lengths (kev pull request 202, the title of the change: states of 64k tokens
+ * are trained and served; system1-omni issue 27, "The closest planned or
+ * implemented model": the model trains end to end), so this is the chain rule
+ * through the forward above. With p_ij = exp(s_ij - lse_i) over the visible
+ * keys:
+ *     delta_i = sum_d dout[i,d] o[i,d]          (= sum_j p_ij dp_ij)
+ *     dp_ij   = dout_i . v_j,   ds_ij = p_ij (dp_ij - delta_i)
+ *     dq_i    = (1/sqrt(D)) sum_j ds_ij k_j
+ *     dk_j    = (1/sqrt(D)) sum_{h,i} ds_ij q_i,   dv_j = sum_{h,i} p_ij dout_i
+ * where the dk/dv sums run over every query head h of the key/value head's
+ * group (grouped-query attention reduces the gradient over the heads that share
+ * a key/value head) and over the rows i that see key j.
+ *
+ * Inputs: q, k, v as for the forward; o and lse are the forward's outputs for
+ * the same arguments (or, for a key set split into parts, the merged o and lse
+ * of the whole: each part's call then yields that part's dk, dv and its share
+ * of dq, and the dq of the parts add up); dout [B,Hq,Lq,D] in `dtype`.
+ * Outputs: dq [B,Hq,Lq,D], dk and dv [B,Hkv,Lk,D] in `dtype`, and
+ * delta [B,Hq,Lq] fp32 (written, then read by the second kernel; a caller
+ * buffer so that the library allocates nothing). Every element of the outputs
+ * is written (rows with no visible key get dq = 0; keys no row sees get
+ * dk = dv = 0). Outputs must not overlap any input or each other.
+ * Same shape rules as the forward, plus Lq, Lk <= 2^21. Accumulation is fp32.
+ * Deterministic: no atomics; dq comes from one kernel over query blocks, dk and
+ * dv from one over key blocks. Returns a gqa_status; GQA_ERR_NULL when any
+ * pointer but the segment ids is NULL.
+ */
+int gqa_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                 const void* dout, void* dq, void* dk, void* dv, float* delta,
+                 int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
+                 int64_t q_offset, const int32_t* seg_q, const int32_t* seg_k,
+                 int causal, int dtype, void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* gqa_attn_strerror(int code);

@@ -1,4 +1,5 @@
-"""MI355X (gfx950) exact causal grouped-query attention forward, memory linear in L.
+"""MI355X (gfx950) exact causal grouped-query attention, memory linear in L:
+the forward, the lse merge of split key sets, and the backward.
 
 A thin ctypes binding over ``libgqa_attn.so`` (C ABI in ``include/gqa_attn.h``).
 Every step of the computation runs in the library's HIP kernels; this module
@@ -17,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libgqa_attn.so")
 GQA_F32, GQA_BF16, GQA_F16 = 0, 1, 2
 STATUS = {0: "GQA_OK", 1: "GQA_ERR_NULL", 2: "GQA_ERR_SHAPE", 3: "GQA_ERR_UNSUPPORTED",
           4: "GQA_ERR_ALIGN", 5: "GQA_ERR_LAUNCH", 6: "GQA_ERR_ALIAS"}
-EXPORTS = ("gqa_attn_fwd", "gqa_attn_merge", "gqa_attn_strerror", "gqa_attn_version")
+EXPORTS = ("gqa_attn_fwd", "gqa_attn_merge", "gqa_attn_bwd", "gqa_attn_strerror", "gqa_attn_version")
 
 _lib = None
 
@@ -41,6 +42,8 @@ def load_library():
         lib.gqa_attn_fwd.restype = c_int
         lib.gqa_attn_merge.argtypes = [p, p, p, p, p, p, i64, i64, c_int, p]
         lib.gqa_attn_merge.restype = c_int
+        lib.gqa_attn_bwd.argtypes = [p] * 10 + [i64] * 7 + [p, p, c_int, c_int, p]
+        lib.gqa_attn_bwd.restype = c_int
         lib.gqa_attn_strerror.argtypes = [c_int]
         lib.gqa_attn_strerror.restype = ctypes.c_char_p
         lib.gqa_attn_version.argtypes = []
@@ -62,6 +65,13 @@ def fwd_raw(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, D, q_offset, seg_q, seg_k, caus
     """Direct call of gqa_attn_fwd with integer pointers; returns the status code."""
     return load_library().gqa_attn_fwd(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, D, q_offset, seg_q, seg_k,
                                        int(causal), int(dtype), stream)
+
+
+def bwd_raw(q, k, v, o, lse, dout, dq, dk, dv, delta, B, Hq, Hkv, Lq, Lk, D, q_offset, seg_q, seg_k,
+            causal, dtype, stream) -> int:
+    """Direct call of gqa_attn_bwd with integer pointers; returns the status code."""
+    return load_library().gqa_attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, Hq, Hkv, Lq, Lk, D,
+                                       q_offset, seg_q, seg_k, int(causal), int(dtype), stream)
 
 
 def merge_raw(o1, lse1, o2, lse2, o, lse, rows, D, dtype, stream) -> int:
@@ -151,3 +161,47 @@ def merge(o1, lse1, o2, lse2, *, out=None, out_lse=None, stream=None):
     if rc != 0:
         raise GqaError(rc, strerror(rc))
     return out, out_lse
+
+
+def bwd(q, k, v, o, lse, dout, *, causal=True, q_offset=0, seg_q=None, seg_k=None, dq=None, dk=None, dv=None,
+        delta=None, stream=None):
+    """Attention backward: gradients with respect to q, k and v of a loss whose
+    gradient with respect to the forward output o is `dout` (like q). o and lse
+    are the forward's outputs for the same arguments (or the merged ones of a
+    split key set). Returns (dq, dk, dv, delta): dq like q, dk and dv like k,
+    delta [B,Hq,Lq] float32 (the row dot products dout . o)."""
+    import torch
+    _check_dev(q, k, v, o, lse, dout, seg_q, seg_k, dq, dk, dv, delta)
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape or o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("q, o, dout must be [B,Hq,Lq,D] and k, v [B,Hkv,Lk,D]")
+    if any(t.dtype != q.dtype for t in (k, v, o, dout)):
+        raise TypeError("q, k, v, o and dout must share a dtype")
+    B, Hq, Lq, D = q.shape
+    Hkv, Lk = k.shape[1], k.shape[2]
+    if k.shape[0] != B or k.shape[3] != D:
+        raise ValueError("q and k/v disagree in batch or head size")
+    if lse.shape != (B, Hq, Lq) or lse.dtype != torch.float32:
+        raise ValueError("lse must be [B,Hq,Lq] float32")
+    if (seg_q is None) != (seg_k is None):
+        raise ValueError("give both segment-id tensors or neither")
+    if seg_q is not None:
+        if seg_q.dtype != torch.int32 or seg_k.dtype != torch.int32:
+            raise TypeError("segment ids must be int32")
+        if seg_q.numel() != B * Lq or seg_k.numel() != B * Lk:
+            raise ValueError("segment ids must be [B,Lq] and [B,Lk]")
+    dt = _dtype_code(q)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    delta = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device) if delta is None else delta
+    if dq.shape != q.shape or dk.shape != k.shape or dv.shape != k.shape or delta.shape != (B, Hq, Lq):
+        raise ValueError("gradient buffers must match q, k, v and delta [B,Hq,Lq]")
+    if any(t.dtype != q.dtype for t in (dq, dk, dv)) or delta.dtype != torch.float32:
+        raise TypeError("gradients share q's dtype; delta is float32")
+    rc = bwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                 dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, Hq, Hkv, Lq, Lk, D,
+                 int(q_offset), None if seg_q is None else seg_q.data_ptr(),
+                 None if seg_k is None else seg_k.data_ptr(), causal, dt, _stream_ptr(stream))
+    if rc != 0:
+        raise GqaError(rc, strerror(rc))
+    return dq, dk, dv, delta

@@ -17,6 +17,8 @@ typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kD = 256;             // head dimension the kernels are built for
+constexpr float kInvSqrtD = 0.0625f;  // 1/sqrt(kD), exact
+static_assert(kD == 256, "kInvSqrtD is 1/sqrt(256)");
 constexpr int kRowsPerWave = 32;    // query rows (one head, 32 positions) per wave
 constexpr int kMaxSegTiles = 16384; // key tiles a workgroup can classify for segment skipping
 
@@ -37,6 +39,18 @@ struct FwdParams {
   int G;          // B * Hkv * (n_rep / hpc): independent head groups per position block
   int causal;
   float scale_log2;  // log2(e) / sqrt(D): scores go straight to the base-2 domain
+};
+
+// Arguments of one backward launch pair (passed by value to both kernels).
+struct BwdParams {
+  FwdParams f;   // q, k, v, o, lse, ids, shape; plan (hpc, ppc, n_qb, G) of the dQ kernel
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;  // [B, Hq, Lq]: written by the dQ kernel, read by the dK/dV kernel
+  int n_kb;      // key blocks per key/value head (dK/dV kernel)
+  int BH;        // B * Hkv
 };
 
 // Which (batch, kv head, head chunk, position block) a workgroup owns.
@@ -145,23 +159,27 @@ struct SegBits {
   int qmin, qmax;
 };
 
-template <int W, int BK>
-__device__ void seg_scan(SegBits& sb, const FwdParams& p, const Work& w, int n_tiles) {
-  constexpr int KPL = 32;          // consecutive keys each lane reduces per pass
-  constexpr int LPT = BK / KPL;    // lanes that share one tile
-  static_assert(BK % KPL == 0, "tile must be a whole number of lane chunks");
+// Generic form: `own` are the ids of this workgroup's own entries [own0,
+// own0 + own_n) of a sequence of own_len (entries past the end are ignored);
+// the scanned side `other` (other_len entries) is cut into tiles of BT.
+template <int NT, int BT>
+__device__ void seg_scan_ids(SegBits& sb, const int32_t* own, int64_t own0, int own_n, int64_t own_len,
+                             const int32_t* other, int64_t other_len, int n_tiles) {
+  constexpr int W = NT / 64;
+  constexpr int KPL = BT < 32 ? BT : 32;  // consecutive entries each lane reduces per pass
+  constexpr int LPT = BT / KPL;           // lanes that share one tile
+  static_assert(BT % KPL == 0, "tile must be a whole number of lane chunks");
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
   const int words = (n_tiles + 31) >> 5;
-  for (int i = tid; i < words; i += W * 64) { sb.vis[i] = 0u; sb.full[i] = 0u; }
+  for (int i = tid; i < words; i += NT) { sb.vis[i] = 0u; sb.full[i] = 0u; }
   if (tid == 0) { sb.qmin = INT32_MAX; sb.qmax = INT32_MIN; }
   __syncthreads();
-  // query id range of this workgroup's rows
+  // id range of this workgroup's own entries
   {
-    const int32_t* sq = p.seg_q + (int64_t)w.b * p.Lq;
     int lo = INT32_MAX, hi = INT32_MIN;
-    for (int r = tid; r < p.ppc; r += W * 64) {
-      const int64_t i = w.p0 + r;
-      if (i < p.Lq) { const int s = sq[i]; lo = min(lo, s); hi = max(hi, s); }
+    for (int r = tid; r < own_n; r += NT) {
+      const int64_t i = own0 + r;
+      if (i < own_len) { const int s = own[i]; lo = min(lo, s); hi = max(hi, s); }
     }
     lo = wave_min_i(lo);
     hi = wave_max_i(hi);
@@ -169,15 +187,14 @@ __device__ void seg_scan(SegBits& sb, const FwdParams& p, const Work& w, int n_t
   }
   __syncthreads();
   const int qmin = sb.qmin, qmax = sb.qmax;
-  const int32_t* sk = p.seg_k + (int64_t)w.b * p.Lk;
-  const int64_t n_keys = (int64_t)n_tiles * BK;
-  for (int64_t base = (int64_t)wave * 64 * KPL; base < n_keys; base += (int64_t)W * 64 * KPL) {
+  const int64_t n_other = (int64_t)n_tiles * BT;
+  for (int64_t base = (int64_t)wave * 64 * KPL; base < n_other; base += (int64_t)W * 64 * KPL) {
     const int64_t k0 = base + (int64_t)lane * KPL;
     int v[KPL];
 #pragma unroll
-    for (int e = 0; e < KPL; ++e) v[e] = (k0 + e < p.Lk) ? sk[k0 + e] : qmin;
+    for (int e = 0; e < KPL; ++e) v[e] = (k0 + e < other_len) ? other[k0 + e] : qmin;
     int lo = INT32_MAX, hi = INT32_MIN;
-    const int nvalid = (int)max((int64_t)0, min((int64_t)KPL, p.Lk - k0));
+    const int nvalid = (int)max((int64_t)0, min((int64_t)KPL, other_len - k0));
 #pragma unroll
     for (int e = 0; e < KPL; ++e) {
       if (e < nvalid) { lo = min(lo, v[e]); hi = max(hi, v[e]); }
@@ -187,13 +204,20 @@ __device__ void seg_scan(SegBits& sb, const FwdParams& p, const Work& w, int n_t
       lo = min(lo, __shfl_xor(lo, s));
       hi = max(hi, __shfl_xor(hi, s));
     }
-    const int64_t t = k0 / BK;
+    const int64_t t = k0 / BT;
     if ((lane % LPT) == 0 && t < n_tiles && lo <= hi) {
       if (lo <= qmax && hi >= qmin) atomicOr(&sb.vis[t >> 5], 1u << (t & 31));
       if (lo == hi && qmin == qmax && lo == qmin) atomicOr(&sb.full[t >> 5], 1u << (t & 31));
     }
   }
   __syncthreads();
+}
+
+// The forward's use: own = the workgroup's query rows, scanned = key tiles of BK.
+template <int W, int BK>
+__device__ void seg_scan(SegBits& sb, const FwdParams& p, const Work& w, int n_tiles) {
+  seg_scan_ids<W * 64, BK>(sb, p.seg_q + (int64_t)w.b * p.Lq, w.p0, p.ppc, p.Lq, p.seg_k + (int64_t)w.b * p.Lk,
+                           p.Lk, n_tiles);
 }
 
 // First visible tile index >= t (n_tiles if none).

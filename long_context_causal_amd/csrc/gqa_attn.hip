@@ -73,6 +73,61 @@ GQA_API int gqa_attn_fwd(const void* q, const void* k, const void* v, void* o, f
   return e == hipSuccess ? GQA_OK : GQA_ERR_LAUNCH;
 }
 
+GQA_API int gqa_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                         const void* dout, void* dq, void* dk, void* dv, float* delta,
+                         int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
+                         int64_t q_offset, const int32_t* seg_q, const int32_t* seg_k,
+                         int causal, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !delta) return GQA_ERR_NULL;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Lq <= 0 || Lk <= 0 || D <= 0) return GQA_ERR_SHAPE;
+  if (Hq % Hkv != 0 || q_offset < 0 || q_offset > ((int64_t)1 << 62)) return GQA_ERR_SHAPE;
+  if ((seg_q == nullptr) != (seg_k == nullptr)) return GQA_ERR_SHAPE;
+  if (D != gqa::kD || dtype != GQA_F32) return GQA_ERR_UNSUPPORTED;
+  const int64_t n_rep = Hq / Hkv;
+  if (!is_pow2_rep(n_rep) || Lq > ((int64_t)1 << 21) || Lk > ((int64_t)1 << 21) || B * Hkv >= ((int64_t)1 << 24))
+    return GQA_ERR_UNSUPPORTED;
+  if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16) || misaligned(dout, 16) ||
+      misaligned(dq, 16) || misaligned(dk, 16) || misaligned(dv, 16) || misaligned(lse, 4) ||
+      misaligned(delta, 4) || misaligned(seg_q, 4) || misaligned(seg_k, 4))
+    return GQA_ERR_ALIGN;
+  const int64_t es = 4;
+  const int64_t qo = B * Hq * Lq * D * es, kv = B * Hkv * Lk * D * es, rl = B * Hq * Lq * 4;
+  const void* ins[6] = {q, k, v, o, lse, dout};
+  const int64_t in_n[6] = {qo, kv, kv, qo, rl, qo};
+  const void* outs[4] = {dq, dk, dv, delta};
+  const int64_t out_n[4] = {qo, kv, kv, rl};
+  for (int a = 0; a < 4; ++a) {
+    for (int i = 0; i < 6; ++i)
+      if (overlap(outs[a], out_n[a], ins[i], in_n[i])) return GQA_ERR_ALIAS;
+    for (int b2 = a + 1; b2 < 4; ++b2)
+      if (overlap(outs[a], out_n[a], outs[b2], out_n[b2])) return GQA_ERR_ALIAS;
+  }
+
+  gqa::BwdParams bp;
+  gqa::FwdParams& p = bp.f;
+  p.q = q; p.k = k; p.v = v; p.o = const_cast<void*>(o); p.lse = const_cast<float*>(lse);
+  p.seg_q = seg_q; p.seg_k = seg_k;
+  p.Lq = Lq; p.Lk = Lk; p.q_offset = q_offset;
+  p.Hq = (int)Hq; p.Hkv = (int)Hkv; p.n_rep = (int)n_rep;
+  p.hpc = (int)(n_rep < 4 ? n_rep : 4);
+  p.ppc = (gqa::kBwdWavesDQ / p.hpc) * gqa::kBwdRowsDQ;
+  const int64_t n_qb = (Lq + p.ppc - 1) / p.ppc;
+  const int64_t G = B * Hkv * (n_rep / p.hpc);
+  const int64_t n_kb = (Lk + gqa::kBwdKeysDKV - 1) / gqa::kBwdKeysDKV;
+  if (n_qb * G >= ((int64_t)1 << 31) || n_kb * B * Hkv >= ((int64_t)1 << 31)) return GQA_ERR_UNSUPPORTED;
+  p.n_qb = (int)n_qb;
+  p.G = (int)G;
+  p.causal = causal ? 1 : 0;
+  p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
+  bp.dout = dout; bp.dq = dq; bp.dk = dk; bp.dv = dv; bp.delta = delta;
+  bp.n_kb = (int)n_kb;
+  bp.BH = (int)(B * Hkv);
+
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
+  return gqa::launch_bwd_f32(bp, s) == hipSuccess ? GQA_OK : GQA_ERR_LAUNCH;
+}
+
 GQA_API int gqa_attn_merge(const void* o1, const float* lse1, const void* o2, const float* lse2,
                               void* o, float* lse, int64_t rows, int64_t D, int dtype, void* stream) {
   if (!o1 || !lse1 || !o2 || !lse2 || !o || !lse) return GQA_ERR_NULL;
@@ -108,7 +163,8 @@ GQA_API const char* gqa_attn_strerror(int code) {
     case GQA_OK: return "success";
     case GQA_ERR_NULL: return "a required pointer is NULL";
     case GQA_ERR_SHAPE: return "invalid shape: non-positive extent, Hq not a multiple of Hkv, negative q_offset, or only one segment-id array";
-    case GQA_ERR_UNSUPPORTED: return "unsupported: D must be 256, dtype F32, BF16 or F16, Hq/Hkv in {1,2,4,8,16}, lengths below 2^31";
+    case GQA_ERR_UNSUPPORTED: return "unsupported: D must be 256, dtype F32, BF16 or F16 (backward: F32), Hq/Hkv in {1,2,4,8,16}, "
+                                     "lengths below 2^31 (backward: at most 2^21)";
     case GQA_ERR_ALIGN: return "misaligned pointer: tensors need 16-byte alignment, lse and segment ids 4-byte";
     case GQA_ERR_LAUNCH: return "kernel launch failed";
     case GQA_ERR_ALIAS: return "output overlaps an input";
@@ -116,4 +172,4 @@ GQA_API const char* gqa_attn_strerror(int code) {
   }
 }
 
-GQA_API int gqa_attn_version(void) { return (1 << 16) | 1; }
+GQA_API int gqa_attn_version(void) { return (1 << 16) | 2; }

@@ -1,6 +1,6 @@
-// launch.hpp -- launchers of the forward kernels, each defined in the
-// translation unit of its kernel (fwd_f32.hip, fwd_h16.hip) so that each
-// kernel is compiled with its own code-generation flags.
+// launch.hpp -- launchers of the forward and backward kernels, each defined in
+// the translation unit of its kernel (fwd_f32.hip, fwd_h16.hip, bwd_f32.hip)
+// so that each kernel is compiled with its own code-generation flags.
 #pragma once
 #include <hip/hip_runtime.h>
 
@@ -17,5 +17,13 @@ constexpr int kWavesH16 = 4, kRowsH16 = 32;  // bf16 and fp16
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream);
 hipError_t launch_fwd_f16(const FwdParams& p, hipStream_t stream);
+
+// Backward: waves per workgroup and query rows per wave of the dQ kernel, keys
+// per workgroup of the dK/dV kernel (host plan).
+constexpr int kBwdWavesDQ = 8, kBwdRowsDQ = 16, kBwdKeysDKV = 64;
+
+// Enqueue the dQ kernel (grid p.f.n_qb * p.f.G) then the dK/dV kernel (grid
+// p.n_kb * p.BH) on `stream`; returns the first launch error.
+hipError_t launch_bwd_f32(const BwdParams& p, hipStream_t stream);
 
 }  // namespace gqa

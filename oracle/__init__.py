@@ -65,6 +65,12 @@ def open_library(path: str):
     lib.oracle_merge.argtypes = [p, p, p, p, i64, i64, p, p]
     lib.oracle_merge.restype = None
     lib.oracle_max_threads.restype = ctypes.c_int
+    lib.oracle_attn_bwd_dq.argtypes = [p, p, p, p, i64, i64, i64, i64, i64, i64, i64, p, p,
+                                       ctypes.c_int, p, i64, p, ctypes.c_int]
+    lib.oracle_attn_bwd_dq.restype = ctypes.c_int
+    lib.oracle_attn_bwd_dkdv.argtypes = [p, p, p, p, i64, i64, i64, i64, i64, i64, i64, p, p,
+                                         ctypes.c_int, p, i64, p, p, ctypes.c_int]
+    lib.oracle_attn_bwd_dkdv.restype = ctypes.c_int
     return lib
 
 
@@ -96,6 +102,22 @@ class Oracle:
 
     def merge(self, o1, lse1, o2, lse2):
         return _merge(self._l(), o1, lse1, o2, lse2)
+
+    def bwd_dq(self, q, k, v, dout, *, causal=True, q_offset=0, seg_q=None, seg_k=None, rows=None,
+               nthreads=0):
+        return _bwd_dq(self._l(), q, k, v, dout, causal=causal, q_offset=q_offset, seg_q=seg_q,
+                       seg_k=seg_k, rows=rows, nthreads=nthreads)
+
+    def bwd_dkdv(self, q, k, v, dout, *, causal=True, q_offset=0, seg_q=None, seg_k=None, keys=None,
+                 nthreads=0):
+        return _bwd_dkdv(self._l(), q, k, v, dout, causal=causal, q_offset=q_offset, seg_q=seg_q,
+                         seg_k=seg_k, keys=keys, nthreads=nthreads)
+
+    def bwd(self, q, k, v, dout, **kw):
+        """dq [B,Hq,Lq,D], dk and dv [B,Hkv,Lk,D] over all rows and keys (fp64)."""
+        dq = self.bwd_dq(q, k, v, dout, **kw)
+        dk, dv = self.bwd_dkdv(q, k, v, dout, **kw)
+        return dq, dk, dv
 
 
 
@@ -180,10 +202,59 @@ def _merge(lib, o1, lse1, o2, lse2):
     return o, lse
 
 
+def _bwd_dq(lib, q, k, v, dout, *, causal=True, q_offset=0, seg_q=None, seg_k=None, rows=None, nthreads=0):
+    """Gradient with respect to q of a loss whose gradient with respect to o is
+    `dout` [B,Hq,Lq,D], for all rows or the given query indices; fp64
+    [B,Hq,R,D]."""
+    q, k, v, dout = _f32(q), _f32(k), _f32(v), _f32(dout)
+    seg_q, seg_k = _check(q, k, v, seg_q, seg_k)
+    if dout.shape != q.shape:
+        raise ValueError("dout must have q's shape")
+    B, Hq, Lq, D = q.shape
+    rows_arr, nrows = None, Lq
+    if rows is not None:
+        rows_arr = np.ascontiguousarray(rows, dtype=np.int64)
+        nrows = rows_arr.size
+    dq = np.empty((B, Hq, nrows, D), dtype=np.float64)
+    rc = lib.oracle_attn_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), B, Hq, k.shape[1], Lq, k.shape[2], D,
+                                int(q_offset), _ptr(seg_q), _ptr(seg_k), int(bool(causal)), _ptr(rows_arr),
+                                nrows, _ptr(dq), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_attn_bwd_dq rejected its arguments")
+    return dq
+
+
+def _bwd_dkdv(lib, q, k, v, dout, *, causal=True, q_offset=0, seg_q=None, seg_k=None, keys=None, nthreads=0):
+    """Gradients with respect to k and v (summed over the query heads that share
+    each key/value head), for all keys or the given key indices; fp64
+    [B,Hkv,K,D] each."""
+    q, k, v, dout = _f32(q), _f32(k), _f32(v), _f32(dout)
+    seg_q, seg_k = _check(q, k, v, seg_q, seg_k)
+    if dout.shape != q.shape:
+        raise ValueError("dout must have q's shape")
+    B, Hq, Lq, D = q.shape
+    Hkv, Lk = k.shape[1], k.shape[2]
+    keys_arr, nkeys = None, Lk
+    if keys is not None:
+        keys_arr = np.ascontiguousarray(keys, dtype=np.int64)
+        nkeys = keys_arr.size
+    dk = np.empty((B, Hkv, nkeys, D), dtype=np.float64)
+    dv = np.empty((B, Hkv, nkeys, D), dtype=np.float64)
+    rc = lib.oracle_attn_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), B, Hq, Hkv, Lq, Lk, D,
+                                  int(q_offset), _ptr(seg_q), _ptr(seg_k), int(bool(causal)), _ptr(keys_arr),
+                                  nkeys, _ptr(dk), _ptr(dv), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_attn_bwd_dkdv rejected its arguments")
+    return dk, dv
+
+
 _default = Oracle()
 attn = _default.attn
 weights = _default.weights
 merge = _default.merge
+bwd_dq = _default.bwd_dq
+bwd_dkdv = _default.bwd_dkdv
+bwd = _default.bwd
 
 
 def max_threads() -> int:

@@ -32,6 +32,12 @@
 #include <omp.h>
 #endif
 
+/* Key/value head read by query head h: contiguous groups of Hq/Hkv heads. */
+static int64_t kv_head_of(int64_t h, int64_t Hq, int64_t Hkv) { return h / (Hq / Hkv); }
+
+/* The score scale 1/sqrt(D). */
+static double score_scale(int64_t D) { return 1.0 / sqrt((double)D); }
+
 /* Key j visible to query row i of batch b? Causal part: j <= q_offset + i.
  * Segment part: seg_q[b,i] == seg_k[b,j] when ids are given. */
 static int visible(int64_t b, int64_t i, int64_t j, int64_t Lq, int64_t Lk, int64_t q_offset,
@@ -51,8 +57,8 @@ static void one_row(const float* q, const float* k, const float* v,
                     int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
                     int64_t q_offset, const int32_t* seg_q, const int32_t* seg_k, int causal,
                     double* s, double* o_row, double* lse_out, double* w) {
-  const int64_t g = h / (Hq / Hkv);
-  const double scale = 1.0 / sqrt((double)D);
+  const int64_t g = kv_head_of(h, Hq, Hkv);
+  const double scale = score_scale(D);
   const float* qi = q + ((b * Hq + h) * Lq + i) * D;
   const float* kb = k + (b * Hkv + g) * Lk * D;
   const float* vb = v + (b * Hkv + g) * Lk * D;
@@ -164,6 +170,187 @@ void oracle_merge(const double* o1, const double* lse1, const double* o2, const 
     for (int64_t d = 0; d < D; ++d) o[r * D + d] = (w1 * o1[r * D + d] + w2 * o2[r * D + d]) / (w1 + w2);
     lse[r] = M + log(w1 + w2);
   }
+}
+
+/* ---- Backward: gradients of a scalar loss whose gradient with respect to o
+ * is dout ---------------------------------------------------------------------
+ *
+ * The pages train at these lengths (kev pull request 202, the title of the
+ * change: states of 64k tokens are trained and served; system1-omni issue 27,
+ * the model trains end to end), so the backward is the gradient of the same
+ * forward, by the chain rule through its definition. With the scores
+ * s_ij = (1/sqrt(D)) q_i.k_j over the visible keys A_i, the weights
+ * p_ij = exp(s_ij - lse_i) and o_i = sum_j p_ij v_j:
+ *   dp_ij = dout_i . v_j
+ *   ds_ij = p_ij (dp_ij - sum_{k in A_i} p_ik dp_ik)      (softmax Jacobian)
+ *   dq_i  = (1/sqrt(D)) sum_{j in A_i} ds_ij k_j
+ *   dk_j  = (1/sqrt(D)) sum_{(h,i): j in A_i} ds_ij q_i
+ *   dv_j  = sum_{(h,i): j in A_i} p_ij dout_i
+ * where the key/value sums run over every query head h that shares the key's
+ * head (the heads that repeating K/V would have copied it to). Rows with no
+ * visible key contribute nothing and get dq = 0. */
+
+/* Statistics of one row (b, h, i): lse_i (natural log; -inf when empty) and
+ * r_i = sum_j p_ij dp_ij. `s` is scratch of Lk doubles, `w` receives p_ij. */
+static void bwd_row_stats(const float* q, const float* k, const float* v, const float* dout,
+                          int64_t b, int64_t h, int64_t i,
+                          int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
+                          int64_t q_offset, const int32_t* seg_q, const int32_t* seg_k, int causal,
+                          double* s, double* orow, double* w, double* lse_out, double* r_out) {
+  one_row(q, k, v, b, h, i, Hq, Hkv, Lq, Lk, D, q_offset, seg_q, seg_k, causal, s, orow, lse_out, w);
+  const int64_t g = kv_head_of(h, Hq, Hkv);
+  const float* di = dout + ((b * Hq + h) * Lq + i) * D;
+  const float* vb = v + (b * Hkv + g) * Lk * D;
+  double r = 0.0;
+  for (int64_t j = 0; j < Lk; ++j) {
+    if (w[j] == 0.0) continue;
+    double dp = 0.0;
+    for (int64_t d = 0; d < D; ++d) dp += (double)di[d] * (double)vb[j * D + d];
+    r += w[j] * dp;
+  }
+  *r_out = r;
+}
+
+/* dq for a subset of query rows (rows == NULL: all, nrows == Lq).
+ * dq [B,Hq,nrows,D] fp64. Returns 0 or -1. */
+int oracle_attn_bwd_dq(const float* q, const float* k, const float* v, const float* dout,
+                       int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
+                       int64_t q_offset, const int32_t* seg_q, const int32_t* seg_k, int causal,
+                       const int64_t* rows, int64_t nrows, double* dq, int nthreads) {
+  if (!q || !k || !v || !dout || !dq) return -1;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Lq <= 0 || Lk <= 0 || D <= 0 || Hq % Hkv) return -1;
+  if ((seg_q == NULL) != (seg_k == NULL) || q_offset < 0 || nrows <= 0) return -1;
+  if (!rows && nrows != Lq) return -1;
+  if (rows) for (int64_t r = 0; r < nrows; ++r) if (rows[r] < 0 || rows[r] >= Lq) return -1;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#endif
+  const double scale = score_scale(D);
+  const int64_t total = B * Hq * nrows;
+  int err = 0;
+#pragma omp parallel
+  {
+    double* s = (double*)malloc((size_t)Lk * sizeof(double));
+    double* w = (double*)malloc((size_t)Lk * sizeof(double));
+    double* orow = (double*)malloc((size_t)D * sizeof(double));
+    if (!s || !w || !orow) {
+#pragma omp atomic write
+      err = 1;
+    }
+#pragma omp for schedule(dynamic, 4)
+    for (int64_t t = 0; t < total; ++t) {
+      if (!s || !w || !orow) continue;
+      const int64_t r = t % nrows, h = (t / nrows) % Hq, b = t / (nrows * Hq);
+      const int64_t i = rows ? rows[r] : r;
+      double lse, rsum;
+      bwd_row_stats(q, k, v, dout, b, h, i, Hq, Hkv, Lq, Lk, D, q_offset, seg_q, seg_k, causal,
+                    s, orow, w, &lse, &rsum);
+      const int64_t g = kv_head_of(h, Hq, Hkv);
+      const float* di = dout + ((b * Hq + h) * Lq + i) * D;
+      const float* kb = k + (b * Hkv + g) * Lk * D;
+      const float* vb = v + (b * Hkv + g) * Lk * D;
+      double* out = dq + t * D;
+      for (int64_t d = 0; d < D; ++d) out[d] = 0.0;
+      for (int64_t j = 0; j < Lk; ++j) {
+        if (w[j] == 0.0) continue;
+        double dp = 0.0;
+        for (int64_t d = 0; d < D; ++d) dp += (double)di[d] * (double)vb[j * D + d];
+        const double ds = w[j] * (dp - rsum);
+        for (int64_t d = 0; d < D; ++d) out[d] += scale * ds * (double)kb[j * D + d];
+      }
+    }
+    free(s);
+    free(w);
+    free(orow);
+  }
+  return err ? -1 : 0;
+}
+
+/* dk and dv for a subset of keys (keys == NULL: all, nkeys == Lk).
+ * dk, dv [B,Hkv,nkeys,D] fp64. The row statistics are computed only for the
+ * rows that see at least one selected key. Returns 0 or -1. */
+int oracle_attn_bwd_dkdv(const float* q, const float* k, const float* v, const float* dout,
+                         int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
+                         int64_t q_offset, const int32_t* seg_q, const int32_t* seg_k, int causal,
+                         const int64_t* keys, int64_t nkeys, double* dk, double* dv, int nthreads) {
+  if (!q || !k || !v || !dout || !dk || !dv) return -1;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Lq <= 0 || Lk <= 0 || D <= 0 || Hq % Hkv) return -1;
+  if ((seg_q == NULL) != (seg_k == NULL) || q_offset < 0 || nkeys <= 0) return -1;
+  if (!keys && nkeys != Lk) return -1;
+  if (keys) for (int64_t r = 0; r < nkeys; ++r) if (keys[r] < 0 || keys[r] >= Lk) return -1;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#endif
+  const double scale = score_scale(D);
+  /* rows (per batch) that see some selected key */
+  char* need = (char*)calloc((size_t)(B * Lq), 1);
+  double* lse = (double*)malloc((size_t)(B * Hq * Lq) * sizeof(double));
+  double* rsum = (double*)malloc((size_t)(B * Hq * Lq) * sizeof(double));
+  if (!need || !lse || !rsum) { free(need); free(lse); free(rsum); return -1; }
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int64_t t = 0; t < B * Lq; ++t) {
+    const int64_t b = t / Lq, i = t % Lq;
+    for (int64_t r = 0; r < nkeys; ++r) {
+      const int64_t j = keys ? keys[r] : r;
+      if (visible(b, i, j, Lq, Lk, q_offset, seg_q, seg_k, causal)) { need[t] = 1; break; }
+    }
+  }
+  int err = 0;
+#pragma omp parallel
+  {
+    double* s = (double*)malloc((size_t)Lk * sizeof(double));
+    double* w = (double*)malloc((size_t)Lk * sizeof(double));
+    double* orow = (double*)malloc((size_t)D * sizeof(double));
+    if (!s || !w || !orow) {
+#pragma omp atomic write
+      err = 1;
+    }
+#pragma omp for schedule(dynamic, 4)
+    for (int64_t t = 0; t < B * Hq * Lq; ++t) {
+      const int64_t i = t % Lq, h = (t / Lq) % Hq, b = t / (Lq * Hq);
+      if (!s || !w || !orow || !need[b * Lq + i]) continue;
+      bwd_row_stats(q, k, v, dout, b, h, i, Hq, Hkv, Lq, Lk, D, q_offset, seg_q, seg_k, causal,
+                    s, orow, w, &lse[t], &rsum[t]);
+    }
+    free(s);
+    free(w);
+    free(orow);
+  }
+  if (err) { free(need); free(lse); free(rsum); return -1; }
+  const int64_t n_rep = Hq / Hkv;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t t = 0; t < B * Hkv * nkeys; ++t) {
+    const int64_t r = t % nkeys, g = (t / nkeys) % Hkv, b = t / (nkeys * Hkv);
+    const int64_t j = keys ? keys[r] : r;
+    const float* kj = k + ((b * Hkv + g) * Lk + j) * D;
+    const float* vj = v + ((b * Hkv + g) * Lk + j) * D;
+    double* dkj = dk + t * D;
+    double* dvj = dv + t * D;
+    for (int64_t d = 0; d < D; ++d) { dkj[d] = 0.0; dvj[d] = 0.0; }
+    for (int64_t h = g * n_rep; h < (g + 1) * n_rep; ++h) {
+      for (int64_t i = 0; i < Lq; ++i) {
+        if (!visible(b, i, j, Lq, Lk, q_offset, seg_q, seg_k, causal)) continue;
+        const int64_t row = (b * Hq + h) * Lq + i;
+        const float* qi = q + row * D;
+        const float* di = dout + row * D;
+        double sd = 0.0, dp = 0.0;
+        for (int64_t d = 0; d < D; ++d) {
+          sd += (double)qi[d] * (double)kj[d];
+          dp += (double)di[d] * (double)vj[d];
+        }
+        const double p = exp(scale * sd - lse[row]);
+        const double ds = p * (dp - rsum[row]);
+        for (int64_t d = 0; d < D; ++d) {
+          dvj[d] += p * (double)di[d];
+          dkj[d] += scale * ds * (double)qi[d];
+        }
+      }
+    }
+  }
+  free(need);
+  free(lse);
+  free(rsum);
+  return 0;
 }
 
 int oracle_max_threads(void) {

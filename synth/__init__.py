@@ -82,6 +82,24 @@ def gqa(B=1, Hq=HQ, Hkv=HKV, Lq=512, Lk=None, Dh=D, *, seed=0, scale=1.0, dtype=
     return Inputs(q, k, v, dtype, q_offset=q_offset, causal=causal)
 
 
+class Grad:
+    """An upstream gradient dout [B,Hq,Lq,D] drawn i.i.d. N(0,1) in fp32 from
+    default_rng(seed); for bf16/f16, rounded to nearest even, with the bit
+    patterns the device receives in `bits`."""
+
+    def __init__(self, shape, seed=0, dtype="f32"):
+        d = np.random.default_rng(seed).standard_normal(shape, dtype=np.float32)
+        self.dtype = dtype
+        self.bits = None
+        if dtype in _ROUND:
+            to_bits, to_f32 = _ROUND[dtype]
+            self.bits = to_bits(d)
+            d = to_f32(self.bits)
+        elif dtype != "f32":
+            raise ValueError("dtype must be 'f32', 'bf16' or 'f16'")
+        self.values = d
+
+
 def segment_lengths(total: int, lo: int = 2048, hi: int = 32768, seed: int = 1) -> list[int]:
     """Uniform-random segment lengths in [lo, hi] from default_rng(seed), drawn
     until they cover `total`; the last one is cut to fit (it may fall below lo)."""

@@ -225,7 +225,161 @@ def pin_row_subset(orc):
     assert np.array_equal(o[:, :, rows], o2) and np.array_equal(lse[:, :, rows], lse2)
 
 
+# ---- backward ---------------------------------------------------------------
+# The backward is the gradient of the forward above (the pages train at these
+# lengths: kev pull request 202, the title of the change; system1-omni issue 27,
+# the model trains end to end). Pins: automatic differentiation of an explicit
+# math-path forward, central differences of the oracle's own forward, and exact
+# identities of the softmax gradient.
+
+BWD_CASES = [
+    # B, Hq, Hkv, Lq, Lk, D, causal, q_offset, segments, input scale
+    (1, 4, 2, 7, 7, 8, True, 0, False, 1.0),
+    (2, 8, 2, 6, 9, 4, True, 3, False, 1.5),
+    (1, 2, 2, 9, 9, 4, False, 0, False, 2.0),
+    (2, 4, 1, 10, 10, 2, True, 0, True, 1.0),
+    (1, 8, 4, 9, 12, 8, True, 3, True, 1.0),
+    (2, 4, 4, 5, 11, 4, False, 0, True, 1.0),
+]
+
+
+def _bwd_case(n):
+    B, Hq, Hkv, Lq, Lk, D, causal, off, seg, sc = BWD_CASES[n]
+    q, k, v = _case(B, Hq, Hkv, Lq, Lk, D, 300 + 7 * n, sc)
+    do = _rand((B, Hq, Lq, D), 900 + n)
+    sq = sk = None
+    if seg:
+        rng = np.random.default_rng(700 + n)
+        sq = rng.integers(0, 3, size=(B, Lq)).astype(np.int32)
+        sk = rng.integers(0, 3, size=(B, Lk)).astype(np.int32)
+        sq[:, 0] = 7  # no key has this id: an empty row when causal is off
+    return q, k, v, do, dict(causal=causal, q_offset=off, seg_q=sq, seg_k=sk)
+
+
+def _autograd_math_path(q, k, v, do, causal, q_offset, seg_q, seg_k):
+    """Gradients by torch autograd (CPU, fp64) of the math path: K/V repeated to
+    every query head by indexing, the full score matrix, an explicit boolean
+    visibility matrix and a softmax from its definition; rows with no visible
+    key output zero."""
+    import torch
+    B, Hq, Lq, D = q.shape
+    Hkv, Lk = k.shape[1], k.shape[2]
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    idx = torch.tensor([h // (Hq // Hkv) for h in range(Hq)])
+    kr, vr = tk[:, idx], tv[:, idx]
+    s = torch.matmul(tq, kr.transpose(-1, -2)) / np.sqrt(D)
+    i = torch.arange(Lq)[:, None]
+    j = torch.arange(Lk)[None, :]
+    vis = torch.ones((B, 1, Lq, Lk), dtype=torch.bool)
+    if causal:
+        vis = vis & (j <= q_offset + i)
+    if seg_q is not None:
+        vis = vis & (torch.tensor(seg_q)[:, None, :, None] == torch.tensor(seg_k)[:, None, None, :])
+    s = torch.where(vis, s, torch.tensor(-np.inf, dtype=torch.float64))
+    m = s.amax(dim=-1, keepdim=True)
+    m = torch.where(torch.isfinite(m), m, torch.zeros_like(m)).detach()
+    e = torch.where(vis, torch.exp(s - m), torch.zeros_like(s))
+    z = e.sum(dim=-1, keepdim=True)
+    p = e / torch.where(z > 0, z, torch.ones_like(z))
+    o = torch.matmul(p, vr)
+    (o * torch.tensor(do, dtype=torch.float64)).sum().backward()
+    return tq.grad.numpy(), tk.grad.numpy(), tv.grad.numpy()
+
+
+def pin_bwd_autograd(orc):
+    """dq, dk, dv within 1e-12 (relative to the largest gradient) of automatic
+    differentiation of the explicit math path, on tiny inputs covering GQA
+    ratios 1-4, causal on and off, q_offset 0 and 3, segments and empty rows."""
+    for n in range(len(BWD_CASES)):
+        q, k, v, do, kw = _bwd_case(n)
+        dq, dk, dv = orc.bwd(q, k, v, do, **kw)
+        rq, rk, rv = _autograd_math_path(q, k, v, do, **kw)
+        for name, a, r in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+            err = np.max(np.abs(a - r)) / max(1.0, np.max(np.abs(r)))
+            assert err < 1e-12, "%s differs from autograd (case %d): %g" % (name, n, err)
+
+
+def pin_bwd_finite_differences(orc):
+    """Central differences of the oracle's forward loss sum(o * dout) with
+    respect to single entries of q, k and v agree with the gradients to 1e-7
+    (relative; step 2^-12 on entries that are multiples of 2^-8, exact in fp32)."""
+    B, Hq, Hkv, Lq, Lk, D = 1, 4, 2, 8, 10, 8
+    q, k, v = (_grid(x) for x in _case(B, Hq, Hkv, Lq, Lk, D, 151))
+    do = _rand((B, Hq, Lq, D), 152)
+    kw = dict(causal=True, q_offset=2)
+    dq, dk, dv = orc.bwd(q, k, v, do, **kw)
+
+    def loss(q_, k_, v_):
+        o, _ = orc.attn(q_, k_, v_, **kw)
+        return float(np.sum(o * do.astype(np.float64)))
+
+    h = 2.0 ** -12
+    rng = np.random.default_rng(153)
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        for _ in range(6):
+            ix = tuple(int(rng.integers(0, n)) for n in x.shape)
+            xp, xm = x.copy(), x.copy()
+            xp[ix] += h
+            xm[ix] -= h
+            args_p = [q, k, v]
+            args_m = [q, k, v]
+            pos = "qkv".index(name)
+            args_p[pos], args_m[pos] = xp, xm
+            fd = (loss(*args_p) - loss(*args_m)) / (2 * h)
+            assert abs(fd - g[ix]) <= 1e-7 * max(1.0, abs(g[ix])), "d%s%s: fd %r vs %r" % (name, ix, fd, g[ix])
+
+
+def pin_bwd_sum_identities(orc):
+    """Exact identities of the softmax gradient: the ds_ij of a row sum to zero,
+    so sum_j dk_j = 0 for every key/value head; the p_ij of a non-empty row sum
+    to one, so sum_j dv_j = sum of dout over the non-empty rows of the heads that
+    share the key/value head; a row with a single visible key (causal row 0) has
+    dq = 0."""
+    q, k, v, do, kw = _bwd_case(4)
+    dq, dk, dv = orc.bwd(q, k, v, do, **kw)
+    _, lse = orc.attn(q, k, v, **kw)
+    Hq, Hkv = q.shape[1], k.shape[1]
+    rep = Hq // Hkv
+    scale = np.max(np.abs(dk))
+    assert np.max(np.abs(dk.sum(axis=2))) < 1e-13 * max(1.0, scale) * k.shape[2]
+    nonempty = np.isfinite(lse)[..., None]
+    want = (do.astype(np.float64) * nonempty).reshape(q.shape[0], Hkv, rep, q.shape[2], -1).sum(axis=(2, 3))
+    assert np.max(np.abs(dv.sum(axis=2) - want)) < 1e-12
+    q0, k0, v0 = _case(1, 4, 2, 6, 6, 8, 161)
+    do0 = _rand((1, 4, 6, 8), 162)
+    dq0 = orc.bwd_dq(q0, k0, v0, do0)
+    assert np.max(np.abs(dq0[:, :, 0])) < 1e-15
+
+
+def pin_bwd_gqa_equals_repeat(orc):
+    """The GQA gradient equals the gradient taken on K/V repeated per query head
+    with dk, dv then summed over each group of heads (1e-13); dq is identical."""
+    q, k, v = _case(1, 8, 2, 11, 11, 8, 171)
+    do = _rand(q.shape, 172)
+    dq, dk, dv = orc.bwd(q, k, v, do)
+    kr, vr = np.repeat(k, 4, axis=1), np.repeat(v, 4, axis=1)
+    dq2, dk2, dv2 = orc.bwd(q, kr, vr, do)
+    assert np.array_equal(dq, dq2)
+    assert np.max(np.abs(dk - dk2.reshape(1, 2, 4, 11, 8).sum(axis=2))) < 1e-13
+    assert np.max(np.abs(dv - dv2.reshape(1, 2, 4, 11, 8).sum(axis=2))) < 1e-13
+
+
+def pin_bwd_subsets(orc):
+    """Gradients for a subset of rows (dq) or keys (dk, dv) equal the full run
+    bitwise."""
+    q, k, v, do, kw = _bwd_case(1)
+    dq, dk, dv = orc.bwd(q, k, v, do, **kw)
+    rows, keys = np.array([5, 0, 3]), np.array([8, 2, 0, 7])
+    assert np.array_equal(orc.bwd_dq(q, k, v, do, rows=rows, **kw), dq[:, :, rows])
+    dks, dvs = orc.bwd_dkdv(q, k, v, do, keys=keys, **kw)
+    assert np.array_equal(dks, dk[:, :, keys]) and np.array_equal(dvs, dv[:, :, keys])
+
+
+BWD_PINS = [pin_bwd_autograd, pin_bwd_finite_differences, pin_bwd_sum_identities, pin_bwd_gqa_equals_repeat,
+            pin_bwd_subsets]
+
+
 ALL_PINS = [pin_brute_force, pin_rows_sum_to_one, pin_gqa_equals_repeat, pin_one_segment_equals_none,
             pin_packed_equals_per_segment, pin_prefix_branch, pin_merge_identity, pin_zero_q,
             pin_first_row, pin_two_keys, pin_constant_v, pin_key_shift, pin_linear_in_v,
-            pin_row_subset]
+            pin_row_subset] + BWD_PINS

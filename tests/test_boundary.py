@@ -45,7 +45,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_strerror():
-    assert gqa.version() == (1, 1)
+    assert gqa.version() == (1, 2)
     msgs = [gqa.strerror(c) for c in range(7)]
     assert len(set(msgs)) == 7 and msgs[0] == "success"
     assert "unknown" in gqa.strerror(99)
@@ -75,6 +75,30 @@ def test_merge_rejects_before_launch(over, code):
     a.update(over)
     assert gqa.merge_raw(a["o1"], a["lse1"], a["o2"], a["lse2"], a["o"], a["lse"], a["rows"], a["D"],
                          a["dtype"], a["stream"]) == code
+
+
+DO, DQ, DK, DV, DEL = (n << 40 for n in range(8, 13))
+BWD_GOOD = dict(q=Q, k=K, v=V, o=O, lse=LSE, dout=DO, dq=DQ, dk=DK, dv=DV, delta=DEL, B=1, Hq=16, Hkv=4,
+                Lq=512, Lk=512, D=256, q_offset=0, seg_q=None, seg_k=None, causal=1, dtype=gqa.GQA_F32,
+                stream=None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), 1), (dict(o=None), 1), (dict(lse=None), 1), (dict(dout=None), 1), (dict(dq=None), 1),
+    (dict(dk=None), 1), (dict(dv=None), 1), (dict(delta=None), 1),
+    (dict(B=0), 2), (dict(Lq=0), 2), (dict(Hq=16, Hkv=3), 2), (dict(q_offset=-1), 2), (dict(seg_q=SQ), 2),
+    (dict(D=128), 3), (dict(dtype=7), 3), (dict(Hq=12, Hkv=4), 3), (dict(Lq=(1 << 21) + 1), 3),
+    (dict(Lk=(1 << 21) + 1), 3),
+    (dict(dout=DO + 4), 4), (dict(dq=DQ + 8), 4), (dict(dk=DK + 2), 4), (dict(delta=DEL + 2), 4),
+    (dict(dq=Q), 6), (dict(dq=DO + 256), 6), (dict(dk=V), 6), (dict(dv=DK), 6), (dict(delta=LSE), 6),
+    (dict(delta=DQ + 1024), 6), (dict(dv=O + 1024), 6),
+])
+def test_bwd_rejects_before_launch(over, code):
+    a = dict(BWD_GOOD)
+    a.update(over)
+    assert gqa.bwd_raw(*(a[n] for n in ("q", "k", "v", "o", "lse", "dout", "dq", "dk", "dv", "delta", "B", "Hq",
+                                         "Hkv", "Lq", "Lk", "D", "q_offset", "seg_q", "seg_k", "causal",
+                                         "dtype", "stream"))) == code
 
 
 def test_python_binding_rejects_host_tensors():
