@@ -138,6 +138,7 @@ __global__ __launch_bounds__(kWavesDQ * 64) void bwd_dq_f32_kernel(BwdParams bp)
   }
   const float lse = p.lse[hq + row_c];
   const float lse2 = lse == -INFINITY ? 0.f : lse * 1.4426950408889634f;
+  wait_vm0_known();
   const float sl2 = p.scale_log2;
 
   f32x4 acc[16];
@@ -229,6 +230,7 @@ __global__ __launch_bounds__(kWavesDQ * 64) void bwd_dq_f32_kernel(BwdParams bp)
 // dK/dV kernel
 // ---------------------------------------------------------------------------
 struct SmemDKV {
+  __attribute__((aligned(16))) char v[kKeysBlockDKV * 1024];  // V of the block's keys, for the whole kernel
   __attribute__((aligned(16))) char q[2][kRowsDKV * 1024];
   __attribute__((aligned(16))) char d[2][kRowsDKV * 1024];
   __attribute__((aligned(16))) float lse[2][kRowsDKV];
@@ -237,14 +239,16 @@ struct SmemDKV {
   SegBits bits;
 };
 
-// Async copy of query tile (rows i0.., head h) into stage st: Q and dO rows
-// (wave w copies rows w, w + 4, w + 8, w + 12), lse, delta and row ids. Rows
-// past Lq read zeros.
-__device__ __forceinline__ void dkv_copy(SmemDKV& sm, int st, const BwdParams& bp, int b, int h, int64_t i0,
-                                         int wave, int lane) {
+// Async copy of query tile (rows i0.., head h) into stage st: the Q and dO
+// rows (wave w copies rows w, w + 4, w + 8, w + 12) and, in a separate call
+// (wave 0, lanes 0..15), the lse, delta and row ids. Rows past Lq read zeros.
+// With live == false the descriptors have size 0: the copy then takes no
+// branch and writes zeros into the idle stage.
+__device__ __forceinline__ void dkv_copy_rows(SmemDKV& sm, int st, const BwdParams& bp, int b, int h, int64_t i0,
+                                              int wave, int lane, bool live = true) {
   const FwdParams& p = bp.f;
   const int64_t hq = ((int64_t)b * p.Hq + h) * p.Lq;
-  const uint32_t nb = (uint32_t)(p.Lq * kD * 4);
+  const uint32_t nb = live ? (uint32_t)(p.Lq * kD * 4) : 0u;
   const rsrc_t rq = make_rsrc((const char*)p.q + hq * kD * 4, nb);
   const rsrc_t rd = make_rsrc((const char*)bp.dout + hq * kD * 4, nb);
 #pragma unroll
@@ -254,13 +258,17 @@ __device__ __forceinline__ void dkv_copy(SmemDKV& sm, int st, const BwdParams& b
     buf2lds16(rq, src, lds_addr(sm.q[st] + rr * 1024));
     buf2lds16(rd, src, lds_addr(sm.d[st] + rr * 1024));
   }
+}
+__device__ __forceinline__ void dkv_copy_rowdata(SmemDKV& sm, int st, const BwdParams& bp, int b, int h,
+                                                 int64_t i0, int wave, int lane) {
+  const FwdParams& p = bp.f;
   // lane l writes slot l: only the first kRowsDKV lanes take part
   if (wave == 0 && lane < kRowsDKV) {
-    const uint32_t off = (uint32_t)(i0 + lane) * 4u;
-    buf2lds4(make_rsrc(p.lse + hq, (uint32_t)(p.Lq * 4)), off, lds_addr(sm.lse[st]));
-    buf2lds4(make_rsrc(bp.delta + hq, (uint32_t)(p.Lq * 4)), off, lds_addr(sm.delta[st]));
-    if (p.seg_q != nullptr)
-      buf2lds4(make_rsrc(p.seg_q + (int64_t)b * p.Lq, (uint32_t)(p.Lq * 4)), off, lds_addr(sm.segq[st]));
+    const int64_t hq = ((int64_t)b * p.Hq + h) * p.Lq;
+    const uint32_t off = (uint32_t)(i0 + lane) * 4u, nb = (uint32_t)(p.Lq * 4);
+    buf2lds4(make_rsrc(p.lse + hq, nb), off, lds_addr(sm.lse[st]));
+    buf2lds4(make_rsrc(bp.delta + hq, nb), off, lds_addr(sm.delta[st]));
+    if (p.seg_q != nullptr) buf2lds4(make_rsrc(p.seg_q + (int64_t)b * p.Lq, nb), off, lds_addr(sm.segq[st]));
   }
 }
 
@@ -291,18 +299,23 @@ __global__ __launch_bounds__(kWavesDKV * 64) void bwd_dkv_f32_kernel(BwdParams b
                                            p.seg_q + (int64_t)b * p.Lq, p.Lq, n_rb);
   const int sk = seg ? p.seg_k[(int64_t)b * p.Lk + key_c] : 0;
 
-  // K and V of the lane's key: chunk 4 c + g (d = 16 c + 4 g + e)
+  // K of the lane's key in registers: chunk 4 c + g (d = 16 c + 4 g + e). V of
+  // the block's 64 keys in LDS (swizzled rows; keys past Lk read zeros): the
+  // registers hold K, the dK and dV accumulators and the operand rings.
   const int64_t kv_head = (int64_t)b * p.Hkv + kvh;
-  f32x4 kf[16], vf[16];
+  f32x4 kf[16];
   {
     const f32x4* kr = (const f32x4*)((const char*)p.k + (kv_head * p.Lk + key_c) * kD * 4);
-    const f32x4* vr = (const f32x4*)((const char*)p.v + (kv_head * p.Lk + key_c) * kD * 4);
 #pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      kf[c] = kr[4 * c + g];
-      vf[c] = vr[4 * c + g];
+    for (int c = 0; c < 16; ++c) kf[c] = kr[4 * c + g];
+    const rsrc_t rv = make_rsrc((const char*)p.v + kv_head * p.Lk * kD * 4, (uint32_t)(p.Lk * kD * 4));
+#pragma unroll
+    for (int it = 0; it < kKeysBlockDKV / kWavesDKV; ++it) {
+      const int kk = wave + kWavesDKV * it;
+      buf2lds16(rv, (uint32_t)(j0 + kk) * 1024u + ((uint32_t)(lane ^ (kk & 15)) << 4), lds_addr(sm.v + kk * 1024));
     }
   }
+  wait_vm0_known();
   f32x4 dka[16], dva[16];
 #pragma unroll
   for (int n = 0; n < 16; ++n) {
@@ -312,23 +325,33 @@ __global__ __launch_bounds__(kWavesDKV * 64) void bwd_dkv_f32_kernel(BwdParams b
   const float sl2 = p.scale_log2;
   const int n_rep = p.n_rep;
   const int h0 = kvh * n_rep;
+  const char* Vs = sm.v + wave * kKeysDKV * 1024;
 
   LanesB ln;
   ln.init(lane);
-  // tiles (rb, hh), hh fastest
-  int rb = use_bits ? seg_next(sm.bits, rb0, n_rb) : rb0;
+  // tiles (rb, hh), hh fastest, row blocks from the last down to rb0: every
+  // key block starts at the last rows, so the workgroups that run together on
+  // an XCD (one kv head) stream the same Q / dO tiles at about the same time
+  // and share them in that XCD's L2.
+  int rb = use_bits ? seg_prev(sm.bits, n_rb - 1, rb0) : n_rb - 1;
   int hh = 0;
   int st = 0;
-  if (rb < n_rb) dkv_copy(sm, 0, bp, b, h0, (int64_t)rb * kRowsDKV, wave, lane);
-  while (rb < n_rb) {
+  if (rb >= rb0) {
+    dkv_copy_rows(sm, 0, bp, b, h0, (int64_t)rb * kRowsDKV, wave, lane);
+    dkv_copy_rowdata(sm, 0, bp, b, h0, (int64_t)rb * kRowsDKV, wave, lane);
+  }
+  while (rb >= rb0) {
     int rbn = rb, hhn = hh + 1;
     if (hhn == n_rep) {
       hhn = 0;
-      rbn = use_bits ? seg_next(sm.bits, rb + 1, n_rb) : rb + 1;
+      rbn = use_bits ? seg_prev(sm.bits, rb - 1, rb0) : rb - 1;
     }
     wait_vm0();
     __syncthreads();
-    if (rbn < n_rb) dkv_copy(sm, st ^ 1, bp, b, h0 + hhn, (int64_t)rbn * kRowsDKV, wave, lane);
+    if (rbn >= rb0) {
+      dkv_copy_rows(sm, st ^ 1, bp, b, h0 + hhn, (int64_t)rbn * kRowsDKV, wave, lane);
+      dkv_copy_rowdata(sm, st ^ 1, bp, b, h0 + hhn, (int64_t)rbn * kRowsDKV, wave, lane);
+    }
     const int64_t i0 = (int64_t)rb * kRowsDKV;
     if (!(p.causal && kw0 > p.q_offset + i0 + kRowsDKV - 1)) {
       const bool seg_full = !seg || (use_bits && ((sm.bits.full[rb >> 5] >> (rb & 31)) & 1u));
@@ -336,54 +359,85 @@ __global__ __launch_bounds__(kWavesDKV * 64) void bwd_dkv_f32_kernel(BwdParams b
           !seg_full || i0 + kRowsDKV > p.Lq || (p.causal && kw0 + kKeysDKV - 1 > p.q_offset + i0);
       const char* Qs = sm.q[st];
       const char* Ds = sm.d[st];
-      // S = Q K^T and dP = dO V^T: lane holds row 4 g + r of its key
-      f32x4 s = {}, dp = {};
-#pragma unroll
-      for (int c = 0; c < 16; ++c) {
-        const f32x4 qa = *(const f32x4*)(Qs + ln.dcon[c & 3] + (c >> 2) * 256);
-        const f32x4 da = *(const f32x4*)(Ds + ln.dcon[c & 3] + (c >> 2) * 256);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) s = mfma16(qa[e], kf[c][e], s);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dp = mfma16(da[e], vf[c][e], dp);
-      }
+      // row data of the tile, read now so that the softmax step does not wait for it
       const f32x4 lse4 = *(const f32x4*)(&sm.lse[st][4 * g]);
       const f32x4 del4 = *(const f32x4*)(&sm.delta[st][4 * g]);
-      int4 ids = {0, 0, 0, 0};
-      if (need_mask && !seg_full) ids = *(const int4*)(&sm.segq[st][4 * g]);
+      int4 ids = {sk, sk, sk, sk};
+      if (!seg_full) ids = *(const int4*)(&sm.segq[st][4 * g]);
+      // mask limits in 32 bits: row 4 g + r of the tile sees the lane's key iff
+      // 4 g + r >= lim (causal) and 4 g + r < nrow (rows past Lq)
+      const int lim = (p.causal && need_mask) ? (int)max((int64_t)-1, min((int64_t)kRowsDKV, key - p.q_offset - i0)) : -1;
+      const int nrow = (int)min((int64_t)kRowsDKV, p.Lq - i0);
+      // S = Q K^T and dP = dO V^T: lane holds row 4 g + r of its key. With one
+      // wave per SIMD nothing else hides the LDS latency, so the operand reads
+      // run two steps ahead of their products (a ring of three).
+      f32x4 s = {}, dp = {};
+      f32x4 qa[3], da[3], va[3];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        qa[c] = *(const f32x4*)(Qs + ln.dcon[c & 3] + (c >> 2) * 256);
+        da[c] = *(const f32x4*)(Ds + ln.dcon[c & 3] + (c >> 2) * 256);
+        va[c] = *(const f32x4*)(Vs + ln.dcon[c & 3] + (c >> 2) * 256);
+      }
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+        if (c + 2 < 16) {
+          const int u = c + 2;
+          qa[u % 3] = *(const f32x4*)(Qs + ln.dcon[u & 3] + (u >> 2) * 256);
+          da[u % 3] = *(const f32x4*)(Ds + ln.dcon[u & 3] + (u >> 2) * 256);
+          va[u % 3] = *(const f32x4*)(Vs + ln.dcon[u & 3] + (u >> 2) * 256);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          s = mfma16(qa[c % 3][e], kf[c][e], s);
+          dp = mfma16(da[c % 3][e], va[c % 3][e], dp);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // the first two operand pairs of the dV / dK products, read while the
+      // last S and dP products finish
+      f32x4 qb[3], db[3];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        db[u] = *(const f32x4*)(Ds + ln.rowc[u >> 2] + (u & 3) * 256);
+        qb[u] = *(const f32x4*)(Qs + ln.rowc[u >> 2] + (u & 3) * 256);
+      }
       float pr[4], ds[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float l2 = lse4[r] == -INFINITY ? 0.f : lse4[r] * 1.4426950408889634f;
         float pv = fast_exp2(fmaf(s[r], sl2, -l2));
-        if (need_mask) {
-          const int64_t i = i0 + 4 * g + r;
-          bool vis = i < p.Lq;
-          if (p.causal) vis = vis && key <= p.q_offset + i;
-          const int id = r == 0 ? ids.x : r == 1 ? ids.y : r == 2 ? ids.z : ids.w;
-          if (!seg_full) vis = vis && id == sk;
-          pv = vis ? pv : 0.f;
-        }
+        // branch-free: lim = -1, nrow = 16 and ids = sk when no mask is needed
+        const int ri = 4 * g + r;
+        const int id = r == 0 ? ids.x : r == 1 ? ids.y : r == 2 ? ids.z : ids.w;
+        pv = (ri < nrow && ri >= lim && id == sk) ? pv : 0.f;
         pr[r] = pv;
         ds[r] = pv * (dp[r] - del4[r]);
       }
-      // dV^T += dO^T P and dK^T += Q^T dS: step r contracts row 4 g + r
+      __builtin_amdgcn_sched_barrier(0);
+      // dV^T += dO^T P and dK^T += Q^T dS: step u = 4 r + a contracts row 4 g + r
+      // for d-blocks 4 a .. 4 a + 3
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const f32x4 da = *(const f32x4*)(Ds + ln.rowc[r] + a * 256);
-          const f32x4 qa = *(const f32x4*)(Qs + ln.rowc[r] + a * 256);
-#pragma unroll
-          for (int bb = 0; bb < 4; ++bb) dva[4 * a + bb] = mfma16(da[bb], pr[r], dva[4 * a + bb]);
-#pragma unroll
-          for (int bb = 0; bb < 4; ++bb) dka[4 * a + bb] = mfma16(qa[bb], ds[r], dka[4 * a + bb]);
+      for (int u = 0; u < 16; ++u) {
+        if (u + 2 < 16) {
+          const int w2 = u + 2;
+          db[w2 % 3] = *(const f32x4*)(Ds + ln.rowc[w2 >> 2] + (w2 & 3) * 256);
+          qb[w2 % 3] = *(const f32x4*)(Qs + ln.rowc[w2 >> 2] + (w2 & 3) * 256);
         }
+        const int r = u >> 2, a = u & 3;
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+          dva[4 * a + bb] = mfma16(db[u % 3][bb], pr[r], dva[4 * a + bb]);
+          dka[4 * a + bb] = mfma16(qb[u % 3][bb], ds[r], dka[4 * a + bb]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     rb = rbn;
     hh = hhn;
     st ^= 1;
   }
+  wait_vm0();  // the V copy is still in flight when no row sees the block
 
   // lane holds dK^T[d = 64 a + 16 g + 4 r + b][key] in dka[4 a + b][r]
   if (key < p.Lk) {

@@ -122,6 +122,13 @@ __device__ __forceinline__ void g2lds4(const char* gbase, uint32_t voff, const v
                :: "s"(lds_addr(lds)), "v"(voff), "s"(gbase) : "memory");
 }
 __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// The same wait as a builtin, which the compiler's own wait insertion sees: after
+// the loads a kernel makes before its main loop (Q, K held in registers), so
+// that the compiler places no vmcnt wait for them inside the loop, where the
+// counter also counts the loop's async tile copies and such a wait would hold
+// the wave until the next tile's copies land. (gfx9 encoding: vmcnt 0,
+// expcnt 7, lgkmcnt 15.)
+__device__ __forceinline__ void wait_vm0_known() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // The same async copy through a buffer resource (MUBUF with the LDS bit): the
 // resource bounds the read, and lanes whose offset falls at or past its size
@@ -133,16 +140,28 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   const uint64_t a = (uint64_t)(uintptr_t)base;
   return rsrc_t{(int)(uint32_t)a, (int)(uint32_t)(a >> 32), (int)bytes, 0x00020000};
 }
-// lds: LDS byte address of the wave's 1 KB (or 256 B) destination. It goes
-// through readfirstlane: it is wave-uniform, and this keeps it in an SGPR even
-// where the compiler cannot prove that.
+// lds: LDS byte address of the wave's 1 KB (or 256 B) destination. It and the
+// resource words go through readfirstlane: they are wave-uniform, and this
+// keeps them in SGPRs even where the compiler cannot prove that (inside a
+// branch on the lane index, for one).
+__device__ __forceinline__ rsrc_t uniform_rsrc(rsrc_t r) {
+  return rsrc_t{__builtin_amdgcn_readfirstlane(r[0]), __builtin_amdgcn_readfirstlane(r[1]),
+                __builtin_amdgcn_readfirstlane(r[2]), __builtin_amdgcn_readfirstlane(r[3])};
+}
 __device__ __forceinline__ void buf2lds16(rsrc_t rsrc, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc) : "memory");
 }
+// The same copy without a memory clobber, for copies into a stage that no
+// code reads before the next explicit wait and barrier (those carry the
+// clobber and order the LDS accesses).
+__device__ __forceinline__ void buf2lds16_nc(rsrc_t rsrc, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc));
+}
 __device__ __forceinline__ void buf2lds4(rsrc_t rsrc, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
-               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc) : "memory");
+               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(uniform_rsrc(rsrc)) : "memory");
 }
 
 // ---------------------------------------------------------------------------
@@ -228,6 +247,19 @@ __device__ __forceinline__ int seg_next(const SegBits& sb, int t, int n_tiles) {
     t = (t | 31) + 1;
   }
   return n_tiles;
+}
+
+// Last visible tile index <= t and >= lo (lo - 1 if none).
+__device__ __forceinline__ int seg_prev(const SegBits& sb, int t, int lo) {
+  while (t >= lo) {
+    const unsigned m = sb.vis[t >> 5] << (31 - (t & 31));
+    if (m) {
+      const int r = t - __builtin_clz(m);
+      return r >= lo ? r : lo - 1;
+    }
+    t = (t & ~31) - 1;
+  }
+  return lo - 1;
 }
 
 }  // namespace gqa

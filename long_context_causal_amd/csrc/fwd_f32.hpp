@@ -122,6 +122,7 @@ __global__ __launch_bounds__(W * 64) void fwd_f32_kernel(FwdParams p) {
 #pragma unroll
     for (int c = 0; c < 32; ++c) qf[c] = qr[2 * c + g];
   }
+  wait_vm0_known();
 
   f32x16 acc[8];
 #pragma unroll
