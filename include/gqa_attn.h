@@ -61,7 +61,7 @@ enum gqa_status {
   GQA_ERR_NULL = 1,        /* q, k, v, o or lse is NULL */
   GQA_ERR_SHAPE = 2,       /* an extent <= 0, Hq % Hkv != 0, q_offset < 0, or exactly one segment pointer NULL */
   GQA_ERR_UNSUPPORTED = 3, /* D != 256, dtype not F32/BF16/F16, Hq/Hkv not in {1,2,4,8,16}, or Lq/Lk >= 2^31
-                              (backward: Lq/Lk > 2^21, or a dtype its kernels do not cover) */
+                              (backward: Lq/Lk > 2^21) */
   GQA_ERR_ALIGN = 4,       /* q, k, v, o not 16-byte aligned, or lse/seg not 4-byte aligned */
   GQA_ERR_LAUNCH = 5,      /* the HIP runtime reported an error at launch */
   GQA_ERR_ALIAS = 6        /* o overlaps q, k or v (or, for merge, partially overlaps an input) */
@@ -116,7 +116,9 @@ int gqa_attn_merge(const void* o1, const float* lse1, const void* o2, const floa
  * buffer so that the library allocates nothing). Every element of the outputs
  * is written (rows with no visible key get dq = 0; keys no row sees get
  * dk = dv = 0). Outputs must not overlap any input or each other.
- * Same shape rules as the forward, plus Lq, Lk <= 2^21. Accumulation is fp32.
+ * Same shape rules as the forward, plus Lq, Lk <= 2^21. Accumulation is fp32;
+ * for bf16 and fp16 inputs the gradients are rounded to nearest even, and so
+ * are P and dS where they enter a product in that type.
  * Deterministic: no atomics; dq comes from one kernel over query blocks, dk and
  * dv from one over key blocks. Returns a gqa_status; GQA_ERR_NULL when any
  * pointer but the segment ids is NULL.

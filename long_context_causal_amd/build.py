@@ -40,6 +40,7 @@ UNITS = {
     "fwd_f32.hip": VGPR_FORM,
     "fwd_h16.hip": [],
     "bwd_f32.hip": [],
+    "bwd_h16.hip": [],
 }
 
 # hipcc's host pass does not know the packed-fp32 target feature; that warning is expected

@@ -47,7 +47,7 @@ __device__ __forceinline__ uint32_t swz_off(int x, int c) { return (uint32_t)x *
 // Per-lane offsets of the two read shapes (m = lane % 16, g = lane / 16):
 //  dcon[j]: row m, chunk 4 c + g for c % 4 = j; chunk c adds 256 (c / 4)
 //  rowc[r]: row 4 g + r, chunk 16 a + m; a adds 256 a
-struct LanesB {
+struct LanesBwdF {
   uint32_t dcon[4];
   uint32_t rowc[4];
   __device__ __forceinline__ void init(int lane) {
@@ -145,7 +145,7 @@ __global__ __launch_bounds__(kWavesDQ * 64) void bwd_dq_f32_kernel(BwdParams bp)
 #pragma unroll
   for (int n = 0; n < 16; ++n) acc[n] = f32x4{};
 
-  LanesB ln;
+  LanesBwdF ln;
   ln.init(lane);
   int t = use_bits ? seg_next(sm.bits, 0, n_tiles) : 0;
   int st = 0;
@@ -327,7 +327,7 @@ __global__ __launch_bounds__(kWavesDKV * 64) void bwd_dkv_f32_kernel(BwdParams b
   const int h0 = kvh * n_rep;
   const char* Vs = sm.v + wave * kKeysDKV * 1024;
 
-  LanesB ln;
+  LanesBwdF ln;
   ln.init(lane);
   // tiles (rb, hh), hh fastest, row blocks from the last down to rb0: every
   // key block starts at the last rows, so the workgroups that run together on

@@ -37,6 +37,7 @@
 // query row per lane, so the rescale and the final 1/lr are lane-local.
 #pragma once
 #include "common.hpp"
+#include "elem16.hpp"
 
 namespace gqa {
 
@@ -47,50 +48,6 @@ constexpr int kTileBytesB = kBkB * kD * 2;  // 32 KB per K or V tile
 constexpr int kCopiesB = kTileBytesB / 1024 / kWavesB;  // 1 KB copies per wave for the K (or V) part of a tile
 constexpr float kLazy = 8.0f;               // lazy-rescale threshold (log2 units)
 constexpr int kVPre = 6;                    // V fragments in flight in phase B (the first read in phase A)
-
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
-typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
-
-// The two 16-bit element types: the 8-element operand vector of a 32x32x16
-// product, the product itself, a pair packed with round-to-nearest-even, and
-// the rounded pair's sum accumulated (v_dot2 with ones).
-template <typename E>
-struct Elem;
-template <>
-struct Elem<__bf16> {
-  typedef bf16x8 v8;
-  static __device__ __forceinline__ f32x16 mfma(v8 a, v8 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ unsigned pack(float a, float b) {
-    bf16x2 r;
-    r[0] = (__bf16)a;
-    r[1] = (__bf16)b;
-    return __builtin_bit_cast(unsigned, r);
-  }
-  static __device__ __forceinline__ float sum2(unsigned pair, float acc) {
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), ones, acc, false);
-  }
-};
-template <>
-struct Elem<_Float16> {
-  typedef f16x8 v8;
-  static __device__ __forceinline__ f32x16 mfma(v8 a, v8 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ unsigned pack(float a, float b) {
-    f16x2 r;
-    r[0] = (_Float16)a;
-    r[1] = (_Float16)b;
-    return __builtin_bit_cast(unsigned, r);
-  }
-  static __device__ __forceinline__ float sum2(unsigned pair, float acc) {
-    const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pair), ones, acc, false);
-  }
-};
 
 // LDS image of a bf16 tile: 512-byte key rows of 32 16-byte chunks; chunk c of
 // key k is stored at chunk c ^ swz_k(k) in K tiles and c ^ swz_v(k) in V tiles.

@@ -82,7 +82,7 @@ GQA_API int gqa_attn_bwd(const void* q, const void* k, const void* v, const void
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Lq <= 0 || Lk <= 0 || D <= 0) return GQA_ERR_SHAPE;
   if (Hq % Hkv != 0 || q_offset < 0 || q_offset > ((int64_t)1 << 62)) return GQA_ERR_SHAPE;
   if ((seg_q == nullptr) != (seg_k == nullptr)) return GQA_ERR_SHAPE;
-  if (D != gqa::kD || dtype != GQA_F32) return GQA_ERR_UNSUPPORTED;
+  if (D != gqa::kD || (dtype != GQA_F32 && dtype != GQA_BF16 && dtype != GQA_F16)) return GQA_ERR_UNSUPPORTED;
   const int64_t n_rep = Hq / Hkv;
   if (!is_pow2_rep(n_rep) || Lq > ((int64_t)1 << 21) || Lk > ((int64_t)1 << 21) || B * Hkv >= ((int64_t)1 << 24))
     return GQA_ERR_UNSUPPORTED;
@@ -90,7 +90,7 @@ GQA_API int gqa_attn_bwd(const void* q, const void* k, const void* v, const void
       misaligned(dq, 16) || misaligned(dk, 16) || misaligned(dv, 16) || misaligned(lse, 4) ||
       misaligned(delta, 4) || misaligned(seg_q, 4) || misaligned(seg_k, 4))
     return GQA_ERR_ALIGN;
-  const int64_t es = 4;
+  const int64_t es = dtype == GQA_F32 ? 4 : 2;
   const int64_t qo = B * Hq * Lq * D * es, kv = B * Hkv * Lk * D * es, rl = B * Hq * Lq * 4;
   const void* ins[6] = {q, k, v, o, lse, dout};
   const int64_t in_n[6] = {qo, kv, kv, qo, rl, qo};
@@ -109,11 +109,16 @@ GQA_API int gqa_attn_bwd(const void* q, const void* k, const void* v, const void
   p.seg_q = seg_q; p.seg_k = seg_k;
   p.Lq = Lq; p.Lk = Lk; p.q_offset = q_offset;
   p.Hq = (int)Hq; p.Hkv = (int)Hkv; p.n_rep = (int)n_rep;
+  // work shapes: dQ kernel waves x rows per wave, keys per dK/dV workgroup
+  const bool h16 = dtype != GQA_F32;
+  const int wq = h16 ? gqa::kBwdWavesDQH : gqa::kBwdWavesDQ;
+  const int rq = h16 ? gqa::kBwdRowsDQH : gqa::kBwdRowsDQ;
+  const int kb = h16 ? gqa::kBwdKeysDKVH : gqa::kBwdKeysDKV;
   p.hpc = (int)(n_rep < 4 ? n_rep : 4);
-  p.ppc = (gqa::kBwdWavesDQ / p.hpc) * gqa::kBwdRowsDQ;
+  p.ppc = (wq / p.hpc) * rq;
   const int64_t n_qb = (Lq + p.ppc - 1) / p.ppc;
   const int64_t G = B * Hkv * (n_rep / p.hpc);
-  const int64_t n_kb = (Lk + gqa::kBwdKeysDKV - 1) / gqa::kBwdKeysDKV;
+  const int64_t n_kb = (Lk + kb - 1) / kb;
   if (n_qb * G >= ((int64_t)1 << 31) || n_kb * B * Hkv >= ((int64_t)1 << 31)) return GQA_ERR_UNSUPPORTED;
   p.n_qb = (int)n_qb;
   p.G = (int)G;
@@ -125,7 +130,10 @@ GQA_API int gqa_attn_bwd(const void* q, const void* k, const void* v, const void
 
   hipStream_t s = (hipStream_t)stream;
   (void)hipGetLastError();
-  return gqa::launch_bwd_f32(bp, s) == hipSuccess ? GQA_OK : GQA_ERR_LAUNCH;
+  const hipError_t e = dtype == GQA_F32    ? gqa::launch_bwd_f32(bp, s)
+                       : dtype == GQA_BF16 ? gqa::launch_bwd_bf16(bp, s)
+                                           : gqa::launch_bwd_f16(bp, s);
+  return e == hipSuccess ? GQA_OK : GQA_ERR_LAUNCH;
 }
 
 GQA_API int gqa_attn_merge(const void* o1, const float* lse1, const void* o2, const float* lse2,
@@ -163,7 +171,7 @@ GQA_API const char* gqa_attn_strerror(int code) {
     case GQA_OK: return "success";
     case GQA_ERR_NULL: return "a required pointer is NULL";
     case GQA_ERR_SHAPE: return "invalid shape: non-positive extent, Hq not a multiple of Hkv, negative q_offset, or only one segment-id array";
-    case GQA_ERR_UNSUPPORTED: return "unsupported: D must be 256, dtype F32, BF16 or F16 (backward: F32), Hq/Hkv in {1,2,4,8,16}, "
+    case GQA_ERR_UNSUPPORTED: return "unsupported: D must be 256, dtype F32, BF16 or F16, Hq/Hkv in {1,2,4,8,16}, "
                                      "lengths below 2^31 (backward: at most 2^21)";
     case GQA_ERR_ALIGN: return "misaligned pointer: tensors need 16-byte alignment, lse and segment ids 4-byte";
     case GQA_ERR_LAUNCH: return "kernel launch failed";

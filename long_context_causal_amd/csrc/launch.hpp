@@ -1,5 +1,6 @@
 // launch.hpp -- launchers of the forward and backward kernels, each defined in
-// the translation unit of its kernel (fwd_f32.hip, fwd_h16.hip, bwd_f32.hip)
+// the translation unit of its kernel (fwd_f32.hip, fwd_h16.hip, bwd_f32.hip,
+// bwd_h16.hip)
 // so that each kernel is compiled with its own code-generation flags.
 #pragma once
 #include <hip/hip_runtime.h>
@@ -25,5 +26,10 @@ constexpr int kBwdWavesDQ = 8, kBwdRowsDQ = 16, kBwdKeysDKV = 64;
 // Enqueue the dQ kernel (grid p.f.n_qb * p.f.G) then the dK/dV kernel (grid
 // p.n_kb * p.BH) on `stream`; returns the first launch error.
 hipError_t launch_bwd_f32(const BwdParams& p, hipStream_t stream);
+
+// 16-bit backward: 4 waves x 32 query rows (dQ kernel), 128 keys per dK/dV workgroup.
+constexpr int kBwdWavesDQH = 4, kBwdRowsDQH = 32, kBwdKeysDKVH = 128;
+hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream);
+hipError_t launch_bwd_f16(const BwdParams& p, hipStream_t stream);
 
 }  // namespace gqa

@@ -24,7 +24,7 @@ from gpu_util import DEV, seg_dev, to_dev
 pytestmark = pytest.mark.gpu
 
 TOL_BWD = {"f32": 2e-5, "bf16": 2e-2, "f16": 2.5e-3}
-BWD_DTYPES = ["f32"]
+BWD_DTYPES = ["f32", "bf16", "f16"]
 
 
 def dout_dev(g):
