@@ -83,6 +83,38 @@ def run_fwd_workload(name, x, steps, warmup, torch, gqa, work, seg=None):
                 bytes=work.hbm_bytes(B, Hq, Hkv_, Lq, Lk, Dh, 4 if x.dtype == "f32" else 2, seg is not None))
 
 
+def run_bwd_workload(name, x, steps, warmup, torch, gqa, work, synth):
+    """The backward (dQ kernel + dK/dV kernel) on the forward's own o and lse;
+    dout drawn N(0,1) (seed 1). Times the backward call only."""
+    torch.cuda.synchronize()
+    q, k, v = dev_inputs(x, torch)
+    g = synth.Grad(x.q.shape, seed=1, dtype=x.dtype)
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[x.dtype]
+    if x.dtype == "f32":
+        do = torch.from_numpy(g.values).to("cuda:0")
+    else:
+        do = torch.from_numpy(g.bits.view(np.int16)).to("cuda:0").view(tdt)
+    del g
+    o, lse = gqa.fwd(q, k, v, causal=x.causal, q_offset=x.q_offset)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty_like(lse)
+    fn = lambda: gqa.bwd(q, k, v, o, lse, do, causal=x.causal, q_offset=x.q_offset, dq=dq, dk=dk, dv=dv,
+                         delta=delta)
+    fn()
+    torch.cuda.synchronize()
+    wall_ms, ev_ms, ev_min, ev_max = time_calls(fn, steps, warmup, torch)
+    B, Hq, Lq, Dh = q.shape
+    Hkv_, Lk = k.shape[1], k.shape[2]
+    fl = work.bwd_flops(B, Hq, Lq, Lk, Dh, causal=x.causal, q_offset=x.q_offset)
+    ex = work.bwd_exec_flops(B, Hq, Lq, Lk, Dh, causal=x.causal, q_offset=x.q_offset)
+    del q, k, v, do, o, lse, dq, dk, dv, delta
+    torch.cuda.empty_cache()
+    return dict(workload=name, flops=fl, exec_flops=ex, wall_ms=wall_ms, kernel_ms=ev_ms, kernel_ms_min=ev_min,
+                kernel_ms_max=ev_max, tflops=fl / (wall_ms * 1e-3) / 1e12, kernel_tflops=fl / (ev_ms * 1e-3) / 1e12,
+                exec_tflops=ex / (ev_ms * 1e-3) / 1e12,
+                bytes=work.bwd_hbm_bytes(B, Hq, Hkv_, Lq, Lk, Dh, 4 if x.dtype == "f32" else 2))
+
+
 def run_branch(steps, warmup, torch, gqa, work, synth):
     """Shared-prefix branch form, fp32: S = 30,468 prefix tokens, 40 branches of
     m = 256 query rows at positions S.. . Prefix part: one non-causal call of all
@@ -150,8 +182,8 @@ def cpu_baseline(x, target_s=15.0):
 
 # Sources and translation unit of each forward kernel.
 KERNEL_SOURCES = {"f32": (["common.hpp", "launch.hpp", "fwd_f32.hpp", "fwd_f32.hip"], "fwd_f32.hip"),
-                  "bf16": (["common.hpp", "launch.hpp", "fwd_h16.hpp", "fwd_h16.hip"], "fwd_h16.hip"),
-                  "f16": (["common.hpp", "launch.hpp", "fwd_h16.hpp", "fwd_h16.hip"], "fwd_h16.hip")}
+                  "bf16": (["common.hpp", "launch.hpp", "elem16.hpp", "fwd_h16.hpp", "fwd_h16.hip"], "fwd_h16.hip"),
+                  "f16": (["common.hpp", "launch.hpp", "elem16.hpp", "fwd_h16.hpp", "fwd_h16.hip"], "fwd_h16.hip")}
 
 
 def kernel_dtype(name: str) -> str:
@@ -237,7 +269,8 @@ def main():
     ap.add_argument("--quick", action="store_true", help="primary workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only", default=None,
-                    help="run one workload: f32-15231, f32-30468, f32-60926, bf16-60926, f16-60926")
+                    help="run one workload: f32-15231, f32-30468, f32-60926, bf16-60926, f16-60926, "
+                         "bwd-f32-30468, bwd-bf16-60926")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (3 times) to calibrate HBM byte counters")
     ap.add_argument("--pmc-report", nargs=4, metavar=("FETCH_DB", "WRITE_DB", "KERNEL_SUBSTR", "WORKLOAD"),
@@ -276,6 +309,19 @@ def main():
         "bf16-60926": ("causal GQA fwd bf16 B=1 Hq=16 Hkv=4 D=256 L=60926", 60926, "bf16"),
         "f16-60926": ("causal GQA fwd fp16 B=1 Hq=16 Hkv=4 D=256 L=60926", 60926, "f16"),
     }
+    bwd_workloads = {
+        "bwd-f32-30468": ("causal GQA bwd fp32 B=1 Hq=16 Hkv=4 D=256 L=30468", 30468, "f32"),
+        "bwd-bf16-60926": ("causal GQA bwd bf16 B=1 Hq=16 Hkv=4 D=256 L=60926", 60926, "bf16"),
+    }
+    if args.only in bwd_workloads:
+        # a profiling aid: the backward alone, its record on one line
+        nm, Ls, dts = bwd_workloads[args.only]
+        r = run_bwd_workload(nm, synth.gqa(1, HQ, HKV, Ls, seed=0, dtype=dts), args.steps, args.warmup, torch, gqa,
+                             work, synth)
+        r["pct_mfma_peak"] = 100.0 * r["kernel_tflops"] / work.PEAK_TFLOPS[dts]
+        r["pct_mfma_peak_exec"] = 100.0 * r["exec_tflops"] / work.PEAK_TFLOPS[dts]
+        print(json.dumps(r), flush=True)
+        return
     primary_key = args.only or "f32-30468"
     name, L, dt = workloads[primary_key]
     x = synth.gqa(1, HQ, HKV, L, seed=0, dtype=dt)
@@ -291,6 +337,11 @@ def main():
             del xs
             secondary.append(r)
         secondary.append(run_branch(max(3, args.steps // 2), 2, torch, gqa, work, synth))
+        # the backward (training): fp32 at L = 30,468 and bf16 at L = 60,926
+        for nm, Ls, dts in bwd_workloads.values():
+            xs = synth.gqa(1, HQ, HKV, Ls, seed=0, dtype=dts)
+            secondary.append(run_bwd_workload(nm, xs, max(3, args.steps // 2), 2, torch, gqa, work, synth))
+            del xs
         # packed segments, bf16, L = 131,072, lengths uniform in [2k, 32k] (seed 1), and the
         # single-segment comparator at the same L
         Lseg = 131072
@@ -306,6 +357,8 @@ def main():
     for r in [prim] + secondary:
         dts = "bf16" if "bf16" in r["workload"] else "f16" if "fp16" in r["workload"] else "f32"
         r["pct_mfma_peak"] = 100.0 * r["kernel_tflops"] / work.PEAK_TFLOPS[dts]
+        if "exec_tflops" in r:
+            r["pct_mfma_peak_exec"] = 100.0 * r["exec_tflops"] / work.PEAK_TFLOPS[dts]
 
     math_gib = work.score_matrix_bytes(HQ, L, L, 4) / 2 ** 30
     out = {

@@ -46,6 +46,30 @@ def hbm_bytes(B, Hq, Hkv, Lq, Lk, D, elem_bytes, segments=False) -> int:
     return B * b
 
 
+def bwd_flops(B, Hq, Lq, Lk, D, **kw) -> int:
+    """Algorithmic FLOPs of the backward: 10 D per visible (query, key) pair per
+    query head, the five products of the gradient (the scores recomputed, dP,
+    dV, dQ, dK; 2 D each), i.e. 2.5 times the forward. The products that the
+    two-kernel split computes twice (the scores and dP, once per kernel) are
+    not counted."""
+    return flops(B, Hq, Lq, Lk, D, **kw) // 4 * 10
+
+
+def bwd_exec_flops(B, Hq, Lq, Lk, D, **kw) -> int:
+    """Product FLOPs the backward kernels execute on visible pairs: 6 D in the
+    dQ kernel (scores, dP, dQ) and 8 D in the dK/dV kernel (scores, dP, dV, dK)."""
+    return flops(B, Hq, Lq, Lk, D, **kw) // 4 * 14
+
+
+def bwd_hbm_bytes(B, Hq, Hkv, Lq, Lk, D, elem_bytes, segments=False) -> int:
+    """Compulsory HBM bytes of the backward: read Q, K, V, O, dO and the lse,
+    write dQ, dK, dV, write and read back delta (fp32)."""
+    b = (4 * Hq * Lq + 4 * Hkv * Lk) * D * elem_bytes + 12 * Hq * Lq
+    if segments:
+        b += 4 * (Lq + Lk)
+    return B * b
+
+
 def score_matrix_bytes(Hq: int, Lq: int, Lk: int, elem_bytes: int = 4) -> int:
     """Bytes of the Hq x Lq x Lk score matrix an L x L (math-path) attention materialises."""
     return int(Hq) * int(Lq) * int(Lk) * int(elem_bytes)

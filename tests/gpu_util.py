@@ -11,6 +11,23 @@ import long_context_causal_amd as gqa
 TOL_O = {"f32": 2e-5, "bf16": 2e-2, "f16": 2e-2 / 8}
 TOL_LSE = 1e-4
 DEV = "cuda:0"
+# backward (no stated bar): per gradient tensor, max|d - d_ref| <= TOL_BWD *
+# max(1, max|d_ref|), the forward's bars read relative to the tensor's scale
+TOL_BWD = {"f32": 2e-5, "bf16": 2e-2, "f16": 2.5e-3}
+
+
+def dout_dev(g):
+    """synth.Grad -> device tensor with the same bytes."""
+    if g.dtype == "f32":
+        return torch.from_numpy(np.ascontiguousarray(g.values)).to(DEV)
+    t = torch.from_numpy(np.ascontiguousarray(g.bits).view(np.int16)).to(DEV)
+    return t.view(torch.bfloat16 if g.dtype == "bf16" else torch.float16)
+
+
+def rel_err(a, ref):
+    """max|a - ref| / max(1, max|ref|); a a device tensor or a host array."""
+    a = a.float().cpu().numpy().astype(np.float64) if torch.is_tensor(a) else a
+    return np.max(np.abs(a - ref)) / max(np.max(np.abs(ref)), 1.0)
 
 
 def dev_tensor(values_f32, bits=None, dtype="f32"):

@@ -19,19 +19,11 @@ import torch
 import long_context_causal_amd as gqa
 import oracle
 import synth
-from gpu_util import DEV, seg_dev, to_dev
+from gpu_util import TOL_BWD, dout_dev, rel_err, seg_dev, to_dev
 
 pytestmark = pytest.mark.gpu
 
-TOL_BWD = {"f32": 2e-5, "bf16": 2e-2, "f16": 2.5e-3}
 BWD_DTYPES = ["f32", "bf16", "f16"]
-
-
-def dout_dev(g):
-    if g.dtype == "f32":
-        return torch.from_numpy(np.ascontiguousarray(g.values)).to(DEV)
-    t = torch.from_numpy(np.ascontiguousarray(g.bits).view(np.int16)).to(DEV)
-    return t.view(torch.bfloat16 if g.dtype == "bf16" else torch.float16)
 
 
 def run_bwd(x, g):
@@ -42,11 +34,6 @@ def run_bwd(x, g):
     dq, dk, dv, delta = gqa.bwd(q, k, v, o, lse, do, **kw)
     torch.cuda.synchronize()
     return dq, dk, dv, delta
-
-
-def rel_err(a, ref):
-    a = a.float().cpu().numpy().astype(np.float64) if torch.is_tensor(a) else a
-    return np.max(np.abs(a - ref)) / max(np.max(np.abs(ref)), 1.0)
 
 
 def check_bwd(x, label, seed=1):
