@@ -64,7 +64,8 @@ enum gqa_status {
                               (backward: Lq/Lk > 2^21) */
   GQA_ERR_ALIGN = 4,       /* q, k, v, o not 16-byte aligned, or lse/seg not 4-byte aligned */
   GQA_ERR_LAUNCH = 5,      /* the HIP runtime reported an error at launch */
-  GQA_ERR_ALIAS = 6        /* o overlaps q, k or v (or, for merge, partially overlaps an input) */
+  GQA_ERR_ALIAS = 6,       /* o overlaps q, k or v (or, for merge, partially overlaps an input) */
+  GQA_ERR_WORKSPACE = 7    /* split-KV workspace smaller than gqa_attn_split_workspace() requires */
 };
 
 /*
@@ -128,6 +129,40 @@ int gqa_attn_bwd(const void* q, const void* k, const void* v, const void* o, con
                  int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
                  int64_t q_offset, const int32_t* seg_q, const int32_t* seg_k,
                  int causal, int dtype, void* stream);
+
+/*
+ * Split-KV forward: the same operation and outputs as gqa_attn_fwd (equal up
+ * to the order of the fp32 sums), for short query blocks over long key
+ * sequences (decoding after a long state; one question's branch over the
+ * shared prefix, system1-omni issue 27, "Three differences from Cua-S1 that
+ * matter", item 3), where gqa_attn_fwd would launch too few workgroups to fill
+ * the GPU. The key range is cut into n_split consecutive ranges (whole key
+ * tiles); one launch computes every (query block, head group, range) and
+ * writes a normalised partial o (fp32) and its lse into `workspace`, and a
+ * second kernel combines the parts with the log-sum-exp merge of
+ * gqa_attn_merge, over n_split parts, then rounds o once to `dtype`.
+ * n_split in [1, 1024]; fewer ranges than n_split are used when Lk has fewer
+ * key tiles; n_split = 1 is gqa_attn_fwd (workspace unused, may be NULL).
+ * workspace: device memory of at least gqa_attn_split_workspace(B, Hq, Lq, D,
+ * n_split) bytes, 16-byte aligned, not overlapping any argument; its contents
+ * on entry do not matter and on return are unspecified. Errors as for
+ * gqa_attn_fwd, plus GQA_ERR_NULL (no workspace) and GQA_ERR_WORKSPACE (too
+ * small); nothing is enqueued on an error.
+ */
+int gqa_attn_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
+                       int64_t q_offset, const int32_t* seg_q, const int32_t* seg_k,
+                       int causal, int dtype, int n_split, void* workspace, int64_t workspace_bytes,
+                       void* stream);
+
+/* Bytes of workspace gqa_attn_fwd_split needs for n_split ranges:
+ * n_split * B * Hq * Lq * (D + 1) * 4. Returns 0 for invalid arguments. */
+int64_t gqa_attn_split_workspace(int64_t B, int64_t Hq, int64_t Lq, int64_t D, int n_split);
+
+/* A split count for gqa_attn_fwd_split that fills the GPU (about two
+ * workgroups per compute unit, each range at least 4 key tiles), from the
+ * shape alone; 1 when gqa_attn_fwd already launches enough workgroups. */
+int gqa_attn_split_count(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int dtype);
 
 /* Static description of a status code (never NULL). */
 const char* gqa_attn_strerror(int code);

@@ -17,8 +17,9 @@ LIB_PATH = os.path.join(_HERE, "libgqa_attn.so")
 
 GQA_F32, GQA_BF16, GQA_F16 = 0, 1, 2
 STATUS = {0: "GQA_OK", 1: "GQA_ERR_NULL", 2: "GQA_ERR_SHAPE", 3: "GQA_ERR_UNSUPPORTED",
-          4: "GQA_ERR_ALIGN", 5: "GQA_ERR_LAUNCH", 6: "GQA_ERR_ALIAS"}
-EXPORTS = ("gqa_attn_fwd", "gqa_attn_merge", "gqa_attn_bwd", "gqa_attn_strerror", "gqa_attn_version")
+          4: "GQA_ERR_ALIGN", 5: "GQA_ERR_LAUNCH", 6: "GQA_ERR_ALIAS", 7: "GQA_ERR_WORKSPACE"}
+EXPORTS = ("gqa_attn_fwd", "gqa_attn_merge", "gqa_attn_bwd", "gqa_attn_fwd_split", "gqa_attn_split_workspace",
+           "gqa_attn_split_count", "gqa_attn_strerror", "gqa_attn_version")
 
 _lib = None
 
@@ -44,6 +45,13 @@ def load_library():
         lib.gqa_attn_merge.restype = c_int
         lib.gqa_attn_bwd.argtypes = [p] * 10 + [i64] * 7 + [p, p, c_int, c_int, p]
         lib.gqa_attn_bwd.restype = c_int
+        lib.gqa_attn_fwd_split.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i64, i64, i64, p, p, c_int, c_int,
+                                           c_int, p, i64, p]
+        lib.gqa_attn_fwd_split.restype = c_int
+        lib.gqa_attn_split_workspace.argtypes = [i64, i64, i64, i64, c_int]
+        lib.gqa_attn_split_workspace.restype = i64
+        lib.gqa_attn_split_count.argtypes = [i64, i64, i64, i64, i64, c_int]
+        lib.gqa_attn_split_count.restype = c_int
         lib.gqa_attn_strerror.argtypes = [c_int]
         lib.gqa_attn_strerror.restype = ctypes.c_char_p
         lib.gqa_attn_version.argtypes = []
@@ -72,6 +80,24 @@ def bwd_raw(q, k, v, o, lse, dout, dq, dk, dv, delta, B, Hq, Hkv, Lq, Lk, D, q_o
     """Direct call of gqa_attn_bwd with integer pointers; returns the status code."""
     return load_library().gqa_attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, Hq, Hkv, Lq, Lk, D,
                                        q_offset, seg_q, seg_k, int(causal), int(dtype), stream)
+
+
+def fwd_split_raw(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, D, q_offset, seg_q, seg_k, causal, dtype, n_split,
+                  workspace, workspace_bytes, stream) -> int:
+    """Direct call of gqa_attn_fwd_split with integer pointers; returns the status code."""
+    return load_library().gqa_attn_fwd_split(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, D, q_offset, seg_q, seg_k,
+                                             int(causal), int(dtype), int(n_split), workspace, workspace_bytes,
+                                             stream)
+
+
+def split_workspace(B, Hq, Lq, D, n_split) -> int:
+    """Workspace bytes of a split-KV forward with n_split ranges."""
+    return int(load_library().gqa_attn_split_workspace(B, Hq, Lq, D, int(n_split)))
+
+
+def split_count(B, Hq, Hkv, Lq, Lk, dtype) -> int:
+    """The library's recommended split count for a shape (dtype: GQA_* code)."""
+    return int(load_library().gqa_attn_split_count(B, Hq, Hkv, Lq, Lk, int(dtype)))
 
 
 def merge_raw(o1, lse1, o2, lse2, o, lse, rows, D, dtype, stream) -> int:
@@ -205,3 +231,40 @@ def bwd(q, k, v, o, lse, dout, *, causal=True, q_offset=0, seg_q=None, seg_k=Non
     if rc != 0:
         raise GqaError(rc, strerror(rc))
     return dq, dk, dv, delta
+
+
+def fwd_split(q, k, v, *, causal=True, q_offset=0, seg_q=None, seg_k=None, n_split=None, out=None, lse=None,
+              workspace=None, stream=None):
+    """Split-KV forward: the same result as fwd() (up to the order of fp32
+    sums), for short query blocks over long key sequences. n_split defaults to
+    the library's recommendation for the shape; workspace (a uint8 device
+    tensor) is allocated when not given. Returns (o, lse)."""
+    import torch
+    _check_dev(q, k, v, seg_q, seg_k, out, lse, workspace)
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("q must be [B,Hq,Lq,D] and k, v [B,Hkv,Lk,D]")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k and v must share a dtype")
+    B, Hq, Lq, D = q.shape
+    Hkv, Lk = k.shape[1], k.shape[2]
+    if (seg_q is None) != (seg_k is None):
+        raise ValueError("give both segment-id tensors or neither")
+    if seg_q is not None and (seg_q.dtype != torch.int32 or seg_k.dtype != torch.int32):
+        raise TypeError("segment ids must be int32")
+    dt = _dtype_code(q)
+    if n_split is None:
+        n_split = split_count(B, Hq, Hkv, Lq, Lk, dt)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device) if lse is None else lse
+    if out.shape != q.shape or out.dtype != q.dtype or lse.shape != (B, Hq, Lq) or lse.dtype != torch.float32:
+        raise ValueError("out must match q and lse must be [B,Hq,Lq] float32")
+    nbytes = split_workspace(B, Hq, Lq, D, n_split)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    rc = fwd_split_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Hq, Hkv, Lq,
+                       Lk, D, int(q_offset), None if seg_q is None else seg_q.data_ptr(),
+                       None if seg_k is None else seg_k.data_ptr(), causal, dt, n_split, workspace.data_ptr(),
+                       workspace.numel() * workspace.element_size(), _stream_ptr(stream))
+    if rc != 0:
+        raise GqaError(rc, strerror(rc))
+    return out, lse

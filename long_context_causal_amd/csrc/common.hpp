@@ -39,6 +39,15 @@ struct FwdParams {
   int G;          // B * Hkv * (n_rep / hpc): independent head groups per position block
   int causal;
   float scale_log2;  // log2(e) / sqrt(D): scores go straight to the base-2 domain
+  // Split-KV (n_split > 1): the grid is n_split x (n_qb * G); split s takes the
+  // key tiles [s split_tiles, (s + 1) split_tiles) (in the kernel's own tile
+  // size) and writes its normalised partial O (fp32) and lse to
+  // o_part[s][row][D] and lse_part[s][row] (row over B * Hq * Lq) instead of o, lse.
+  int n_split;
+  int split_tiles;
+  int64_t part_rows;  // B * Hq * Lq: the rows of one split's part
+  float* o_part;
+  float* lse_part;
 };
 
 // Arguments of one backward launch pair (passed by value to both kernels).
@@ -61,11 +70,14 @@ struct BwdParams {
 struct Work {
   int b, kvh, h0, qb;
   int64_t p0;
+  int split;  // key split of a split-KV launch (0 otherwise)
 };
 
 __device__ __forceinline__ Work decode_work(const FwdParams& p) {
-  const int i = blockIdx.x;
+  const int base = p.n_qb * p.G;
+  const int i = (int)blockIdx.x % base;
   Work w;
+  w.split = (int)blockIdx.x / base;
   w.qb = p.n_qb - 1 - i / p.G;
   const int gi = i % p.G;
   const int nhc = p.n_rep / p.hpc;

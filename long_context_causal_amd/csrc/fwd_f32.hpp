@@ -107,6 +107,10 @@ __global__ __launch_bounds__(W * 64) void fwd_f32_kernel(FwdParams p) {
   const bool seg = p.seg_q != nullptr;
   const bool use_bits = seg && n_tiles <= kMaxSegTiles;
   if (use_bits) seg_scan<W, kBkF>(sm.bits, p, w, n_tiles);
+  // tiles [t_lo, t_hi): all of them, or this workgroup's key split
+  const bool split = p.n_split > 1;
+  const int t_lo = split ? w.split * p.split_tiles : 0;
+  const int t_hi = split ? min(n_tiles, t_lo + p.split_tiles) : n_tiles;
 
   const int64_t kv_head = (int64_t)w.b * p.Hkv + w.kvh;
   const char* kb = (const char*)p.k + kv_head * p.Lk * kD * 4;
@@ -130,16 +134,16 @@ __global__ __launch_bounds__(W * 64) void fwd_f32_kernel(FwdParams p) {
   float m_run = -INFINITY, l_part = 0.f;
   const float sl2 = p.scale_log2;
 
-  int t = use_bits ? seg_next(sm.bits, 0, n_tiles) : 0;
+  int t = use_bits ? seg_next(sm.bits, t_lo, t_hi) : t_lo;
   int st = 0;
   LanesF ln;
   ln.init(wave, lane);
-  if (t < n_tiles) load_tile_f<W>(sm, 0, kb, vb, skb, t, p.Lk, wave, lane, ln);
-  while (t < n_tiles) {
-    const int tn = use_bits ? seg_next(sm.bits, t + 1, n_tiles) : t + 1;
+  if (t < t_hi) load_tile_f<W>(sm, 0, kb, vb, skb, t, p.Lk, wave, lane, ln);
+  while (t < t_hi) {
+    const int tn = use_bits ? seg_next(sm.bits, t + 1, t_hi) : t + 1;
     wait_vm0();
     __syncthreads();
-    if (tn < n_tiles) load_tile_f<W>(sm, st ^ 1, kb, vb, skb, tn, p.Lk, wave, lane, ln);
+    if (tn < t_hi) load_tile_f<W>(sm, st ^ 1, kb, vb, skb, tn, p.Lk, wave, lane, ln);
     const int64_t k0 = (int64_t)t * kBkF;
     if (!(p.causal && k0 > p.q_offset + pw + 31)) {
       const bool seg_full = !seg || (use_bits && ((sm.bits.full[t >> 5] >> (t & 31)) & 1u));
@@ -225,7 +229,10 @@ __global__ __launch_bounds__(W * 64) void fwd_f32_kernel(FwdParams p) {
   const float l_tot = xor32_sum(l_part);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (row < p.Lq) {
-    float* op = (float*)p.o + (hq + row) * kD;
+    // a split writes its normalised part and its lse to the split's slots
+    float* obase = split ? p.o_part + (int64_t)w.split * p.part_rows * kD : (float*)p.o;
+    float* lbase = split ? p.lse_part + (int64_t)w.split * p.part_rows : p.lse;
+    float* op = obase + (hq + row) * kD;
 #pragma unroll
     for (int n = 0; n < 8; ++n)
 #pragma unroll
@@ -236,7 +243,7 @@ __global__ __launch_bounds__(W * 64) void fwd_f32_kernel(FwdParams p) {
       }
     if (g == 0) {
       const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-      p.lse[hq + row] = l_tot > 0.f ? (m_use + log2f(l_tot)) * 0.69314718055994530942f : -INFINITY;
+      lbase[hq + row] = l_tot > 0.f ? (m_use + log2f(l_tot)) * 0.69314718055994530942f : -INFINITY;
     }
   }
 }

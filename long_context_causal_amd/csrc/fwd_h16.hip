@@ -5,10 +5,12 @@
 namespace gqa {
 
 static_assert(kWavesH16 == kWavesB && kRowsH16 == kRowsB, "host plan and kernel disagree on the workgroup shape");
+static_assert(kTileKeysH16 == kBkB, "host plan and kernel disagree on the key tile");
 
 template <typename E>
 static hipError_t launch_h16(const FwdParams& p, hipStream_t stream) {
-  const dim3 grid((unsigned)p.n_qb * (unsigned)p.G), block(kWavesB * 64);
+  const unsigned splits = p.n_split > 1 ? (unsigned)p.n_split : 1u;
+  const dim3 grid((unsigned)p.n_qb * (unsigned)p.G * splits), block(kWavesB * 64);
   if (p.seg_q != nullptr)
     hipLaunchKernelGGL((fwd_h16_kernel<E, true>), grid, block, 0, stream, p);
   else

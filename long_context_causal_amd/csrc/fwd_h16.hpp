@@ -442,6 +442,11 @@ __global__ __launch_bounds__(kWavesB * 64) void fwd_h16_kernel(FwdParams p) {
 
   wv.use_bits = SEG && wv.n_tiles <= kMaxSegTiles;
   if (SEG && wv.use_bits) seg_scan<kWavesB, kBkB>(sm.bits, p, w, wv.n_tiles);
+  // tiles [t_lo, n_tiles): all of them, or this workgroup's key split (tiles
+  // at or past the new n_tiles count as past the end)
+  const bool split = p.n_split > 1;
+  const int t_lo = split ? w.split * p.split_tiles : 0;
+  if (split) wv.n_tiles = min(wv.n_tiles, t_lo + p.split_tiles);
 
   const int64_t kv_head = (int64_t)w.b * p.Hkv + w.kvh;
   wv.kb = (const char*)p.k + kv_head * p.Lk * kD * 2;
@@ -466,7 +471,7 @@ __global__ __launch_bounds__(kWavesB * 64) void fwd_h16_kernel(FwdParams p) {
   wv.ln.init(wv.wave, wv.lane, (lds_cchar*)sm.k[0], (lds_cchar*)sm.v[0]);
   wv.rb = RingBase{lds_addr(sm.k[0]), lds_addr(sm.v[0]), lds_addr(sm.segk[0])};
 
-  wv.cur = SEG && wv.use_bits ? seg_next(sm.bits, 0, wv.n_tiles) : 0;
+  wv.cur = SEG && wv.use_bits ? seg_next(sm.bits, t_lo, wv.n_tiles) : t_lo;
   if (wv.cur < wv.n_tiles) {
     wv.nxt = wv.next_tile(wv.cur);
     wv.nn = wv.next_tile(wv.nxt);
@@ -498,17 +503,29 @@ __global__ __launch_bounds__(kWavesB * 64) void fwd_h16_kernel(FwdParams p) {
   const float lr_tot = xor32_sum(wv.rs.lr);
   if (row < p.Lq) {
     const float inv = lr_tot > 0.f ? 1.f / lr_tot : 0.f;
-    char* op = (char*)p.o + (hq + row) * kD * 2;
+    const float lse = l_tot > 0.f ? (wv.rs.m_use + log2f(l_tot)) * 0.69314718055994530942f : -INFINITY;
+    if (split) {
+      // a split writes its normalised part in fp32 (the merge rounds once) and its lse
+      float* op = p.o_part + ((int64_t)w.split * p.part_rows + hq + row) * kD;
 #pragma unroll
-    for (int n = 0; n < 8; ++n)
+      for (int n = 0; n < 8; ++n)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const u32x2 val = {Elem<E>::pack(wv.acc[n][4 * j] * inv, wv.acc[n][4 * j + 1] * inv),
-                           Elem<E>::pack(wv.acc[n][4 * j + 2] * inv, wv.acc[n][4 * j + 3] * inv)};
-        *(u32x2*)(op + (32 * n + 8 * j + 4 * wv.g) * 2) = val;
-      }
-    if (wv.g == 0)
-      p.lse[hq + row] = l_tot > 0.f ? (wv.rs.m_use + log2f(l_tot)) * 0.69314718055994530942f : -INFINITY;
+        for (int j = 0; j < 4; ++j)
+          *(f32x4*)(op + 32 * n + 8 * j + 4 * wv.g) = f32x4{wv.acc[n][4 * j] * inv, wv.acc[n][4 * j + 1] * inv,
+                                                              wv.acc[n][4 * j + 2] * inv, wv.acc[n][4 * j + 3] * inv};
+      if (wv.g == 0) p.lse_part[(int64_t)w.split * p.part_rows + hq + row] = lse;
+    } else {
+      char* op = (char*)p.o + (hq + row) * kD * 2;
+#pragma unroll
+      for (int n = 0; n < 8; ++n)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const u32x2 val = {Elem<E>::pack(wv.acc[n][4 * j] * inv, wv.acc[n][4 * j + 1] * inv),
+                             Elem<E>::pack(wv.acc[n][4 * j + 2] * inv, wv.acc[n][4 * j + 3] * inv)};
+          *(u32x2*)(op + (32 * n + 8 * j + 4 * wv.g) * 2) = val;
+        }
+      if (wv.g == 0) p.lse[hq + row] = lse;
+    }
   }
 }
 

@@ -22,15 +22,20 @@ bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
 
 bool is_pow2_rep(int64_t r) { return r == 1 || r == 2 || r == 4 || r == 8 || r == 16; }
 
+// split-KV: the most splits one launch takes, and the workgroup count the
+// recommended split count aims at (two per compute unit)
+constexpr int kMaxSplits = 1024;
+constexpr int64_t kSplitTargetWorkgroups = 512;
+
 }  // namespace
 
 // The library is built with hidden visibility; these are its only exports.
 #define GQA_API extern "C" __attribute__((visibility("default")))
 
-GQA_API int gqa_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                            int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
-                            int64_t q_offset, const int32_t* seg_q, const int32_t* seg_k,
-                            int causal, int dtype, void* stream) {
+// Argument checks and launch plan shared by the forward entry points.
+static int fwd_plan(gqa::FwdParams& p, const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                    int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D, int64_t q_offset,
+                    const int32_t* seg_q, const int32_t* seg_k, int causal, int dtype) {
   if (!q || !k || !v || !o || !lse) return GQA_ERR_NULL;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Lq <= 0 || Lk <= 0 || D <= 0) return GQA_ERR_SHAPE;
   if (Hq % Hkv != 0 || q_offset < 0 || q_offset > ((int64_t)1 << 62)) return GQA_ERR_SHAPE;
@@ -50,7 +55,6 @@ GQA_API int gqa_attn_fwd(const void* q, const void* k, const void* v, void* o, f
     return GQA_ERR_ALIAS;
 
   const int W = dtype == GQA_F32 ? gqa::kWavesF32 : gqa::kWavesH16;
-  gqa::FwdParams p;
   p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
   p.seg_q = seg_q; p.seg_k = seg_k;
   p.Lq = Lq; p.Lk = Lk; p.q_offset = q_offset;
@@ -64,13 +68,101 @@ GQA_API int gqa_attn_fwd(const void* q, const void* k, const void* v, void* o, f
   p.G = (int)G;
   p.causal = causal ? 1 : 0;
   p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
+  p.n_split = 1;
+  p.part_rows = B * Hq * Lq;
+  return GQA_OK;
+}
 
+static hipError_t launch_fwd(const gqa::FwdParams& p, int dtype, hipStream_t s) {
+  return dtype == GQA_F32    ? gqa::launch_fwd_f32(p, s)
+         : dtype == GQA_BF16 ? gqa::launch_fwd_bf16(p, s)
+                             : gqa::launch_fwd_f16(p, s);
+}
+
+// Key tiles per split and the number of (non-empty) splits for a requested count.
+static void split_shape(int64_t Lk, int dtype, int n_split, int* split_tiles, int* n_eff) {
+  const int64_t tile = dtype == GQA_F32 ? gqa::kTileKeysF32 : gqa::kTileKeysH16;
+  const int64_t n_tiles = (Lk + tile - 1) / tile;
+  const int64_t st = (n_tiles + n_split - 1) / n_split;
+  *split_tiles = (int)st;
+  *n_eff = (int)((n_tiles + st - 1) / st);
+}
+
+GQA_API int gqa_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
+                            int64_t q_offset, const int32_t* seg_q, const int32_t* seg_k,
+                            int causal, int dtype, void* stream) {
+  gqa::FwdParams p{};
+  const int rc = fwd_plan(p, q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, D, q_offset, seg_q, seg_k, causal, dtype);
+  if (rc != GQA_OK) return rc;
+  (void)hipGetLastError();
+  return launch_fwd(p, dtype, (hipStream_t)stream) == hipSuccess ? GQA_OK : GQA_ERR_LAUNCH;
+}
+
+GQA_API int gqa_attn_split_count(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int dtype) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Lq <= 0 || Lk <= 0 || Hq % Hkv != 0) return 1;
+  const int64_t n_rep = Hq / Hkv;
+  const int W = dtype == GQA_F32 ? gqa::kWavesF32 : gqa::kWavesH16;
+  const int64_t hpc = n_rep < W ? n_rep : W;
+  const int64_t ppc = (W / hpc) * (dtype == GQA_F32 ? gqa::kRowsF32 : gqa::kRowsH16);
+  const int64_t base = ((Lq + ppc - 1) / ppc) * B * Hkv * (n_rep / hpc);
+  const int64_t tile = dtype == GQA_F32 ? gqa::kTileKeysF32 : gqa::kTileKeysH16;
+  const int64_t n_tiles = (Lk + tile - 1) / tile;
+  // aim at two workgroups per compute unit, each split at least 4 tiles long
+  int64_t n = (kSplitTargetWorkgroups + base - 1) / base;
+  n = n < n_tiles / 4 ? n : n_tiles / 4;
+  n = n < kMaxSplits ? n : kMaxSplits;
+  return (int)(n < 1 ? 1 : n);
+}
+
+GQA_API int64_t gqa_attn_split_workspace(int64_t B, int64_t Hq, int64_t Lq, int64_t D, int n_split) {
+  if (B <= 0 || Hq <= 0 || Lq <= 0 || D <= 0 || n_split < 1) return 0;
+  return (int64_t)n_split * B * Hq * Lq * (D + 1) * 4;
+}
+
+GQA_API int gqa_attn_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
+                                  int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
+                                  int64_t q_offset, const int32_t* seg_q, const int32_t* seg_k,
+                                  int causal, int dtype, int n_split, void* workspace, int64_t workspace_bytes,
+                                  void* stream) {
+  gqa::FwdParams p{};
+  const int rc = fwd_plan(p, q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, D, q_offset, seg_q, seg_k, causal, dtype);
+  if (rc != GQA_OK) return rc;
+  if (n_split < 1 || n_split > kMaxSplits) return GQA_ERR_UNSUPPORTED;
+  int split_tiles, n_eff;
+  split_shape(Lk, dtype, n_split, &split_tiles, &n_eff);
   hipStream_t s = (hipStream_t)stream;
   (void)hipGetLastError();
-  const hipError_t e = dtype == GQA_F32    ? gqa::launch_fwd_f32(p, s)
-                       : dtype == GQA_BF16 ? gqa::launch_fwd_bf16(p, s)
-                                           : gqa::launch_fwd_f16(p, s);
-  return e == hipSuccess ? GQA_OK : GQA_ERR_LAUNCH;
+  if (n_eff <= 1) return launch_fwd(p, dtype, s) == hipSuccess ? GQA_OK : GQA_ERR_LAUNCH;
+  // workspace: fp32 partial O [n_eff][rows][D], then lse parts [n_eff][rows]
+  const int64_t rows = B * Hq * Lq;
+  const int64_t need = (int64_t)n_eff * rows * (D + 1) * 4;
+  if (!workspace) return GQA_ERR_NULL;
+  if (workspace_bytes < need) return GQA_ERR_WORKSPACE;
+  if (misaligned(workspace, 16)) return GQA_ERR_ALIGN;
+  const int64_t es = dtype == GQA_F32 ? 4 : 2;
+  const int64_t qo = rows * D * es, kv = B * Hkv * Lk * D * es;
+  if (overlap(workspace, need, q, qo) || overlap(workspace, need, k, kv) || overlap(workspace, need, v, kv) ||
+      overlap(workspace, need, o, qo) || overlap(workspace, need, lse, rows * 4) ||
+      (seg_q && overlap(workspace, need, seg_q, B * Lq * 4)) || (seg_k && overlap(workspace, need, seg_k, B * Lk * 4)))
+    return GQA_ERR_ALIAS;
+  if ((int64_t)n_eff * p.n_qb * p.G >= ((int64_t)1 << 31)) return GQA_ERR_UNSUPPORTED;
+  p.n_split = n_eff;
+  p.split_tiles = split_tiles;
+  p.o_part = (float*)workspace;
+  p.lse_part = (float*)workspace + n_eff * rows * D;
+  if (launch_fwd(p, dtype, s) != hipSuccess) return GQA_ERR_LAUNCH;
+  const dim3 grid((unsigned)((rows + 3) / 4));
+  if (dtype == GQA_F32)
+    hipLaunchKernelGGL(gqa::merge_splits_kernel<float>, grid, dim3(256), 0, s, p.o_part, p.lse_part, n_eff,
+                       (float*)o, lse, rows, D);
+  else if (dtype == GQA_BF16)
+    hipLaunchKernelGGL(gqa::merge_splits_kernel<__bf16>, grid, dim3(256), 0, s, p.o_part, p.lse_part, n_eff,
+                       (__bf16*)o, lse, rows, D);
+  else
+    hipLaunchKernelGGL(gqa::merge_splits_kernel<_Float16>, grid, dim3(256), 0, s, p.o_part, p.lse_part, n_eff,
+                       (_Float16*)o, lse, rows, D);
+  return hipGetLastError() == hipSuccess ? GQA_OK : GQA_ERR_LAUNCH;
 }
 
 GQA_API int gqa_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -103,7 +195,7 @@ GQA_API int gqa_attn_bwd(const void* q, const void* k, const void* v, const void
       if (overlap(outs[a], out_n[a], outs[b2], out_n[b2])) return GQA_ERR_ALIAS;
   }
 
-  gqa::BwdParams bp;
+  gqa::BwdParams bp{};
   gqa::FwdParams& p = bp.f;
   p.q = q; p.k = k; p.v = v; p.o = const_cast<void*>(o); p.lse = const_cast<float*>(lse);
   p.seg_q = seg_q; p.seg_k = seg_k;
@@ -176,8 +268,9 @@ GQA_API const char* gqa_attn_strerror(int code) {
     case GQA_ERR_ALIGN: return "misaligned pointer: tensors need 16-byte alignment, lse and segment ids 4-byte";
     case GQA_ERR_LAUNCH: return "kernel launch failed";
     case GQA_ERR_ALIAS: return "output overlaps an input";
+    case GQA_ERR_WORKSPACE: return "workspace smaller than gqa_attn_split_workspace() for the split count";
     default: return "unknown status code";
   }
 }
 
-GQA_API int gqa_attn_version(void) { return (1 << 16) | 2; }
+GQA_API int gqa_attn_version(void) { return (1 << 16) | 3; }

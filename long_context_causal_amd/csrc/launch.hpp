@@ -12,9 +12,11 @@ namespace gqa {
 // Workgroup shapes the host plan needs: waves per workgroup and query rows per wave.
 constexpr int kWavesF32 = 4, kRowsF32 = 32;
 constexpr int kWavesH16 = 4, kRowsH16 = 32;  // bf16 and fp16
+// Keys per tile of the forward kernels (the unit of a split-KV range).
+constexpr int kTileKeysF32 = 32, kTileKeysH16 = 64;
 
-// Enqueue one forward launch (grid = p.n_qb * p.G workgroups); returns
-// hipGetLastError() after the launch.
+// Enqueue one forward launch (grid = p.n_qb * p.G workgroups, times p.n_split
+// for a split-KV launch); returns hipGetLastError() after the launch.
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream);
 hipError_t launch_fwd_f16(const FwdParams& p, hipStream_t stream);

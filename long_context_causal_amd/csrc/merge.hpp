@@ -89,4 +89,37 @@ __global__ __launch_bounds__(256) void merge_kernel(const T* o1, const float* ls
   if (lane == 0) lse[r] = out_lse;
 }
 
+// Merge of the n_split partial results of a split-KV forward (fp32 O parts
+// [n_split][rows][D], lse parts [n_split][rows]) into o (in T) and lse: the
+// same log-sum-exp combination over n_split disjoint key ranges. One wave per
+// row.
+template <typename T>
+__global__ __launch_bounds__(256) void merge_splits_kernel(const float* o_part, const float* lse_part, int n_split,
+                                                           T* o, float* lse, int64_t rows, int64_t D) {
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (r >= rows) return;
+  float M = -INFINITY;
+  for (int s = 0; s < n_split; ++s) M = fmaxf(M, lse_part[(int64_t)s * rows + r]);
+  float wsum = 0.f;
+  for (int s = 0; s < n_split; ++s) {
+    const float l = lse_part[(int64_t)s * rows + r];
+    wsum += (M == -INFINITY) ? 0.f : expf(l - M);
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  for (int64_t d = (int64_t)lane * 8; d < D; d += 512) {
+    float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < n_split; ++s) {
+      const float l = lse_part[(int64_t)s * rows + r];
+      const float w = (M == -INFINITY) ? 0.f : expf(l - M) * inv;
+      float x[8];
+      load8<float>(o_part + ((int64_t)s * rows + r) * D + d, x);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) z[i] = fmaf(w, x[i], z[i]);
+    }
+    store8<T>(o + r * D + d, z);
+  }
+  if (lane == 0) lse[r] = (M == -INFINITY) ? -INFINITY : M + logf(wsum);
+}
+
 }  // namespace gqa

@@ -27,7 +27,7 @@ def call(**over):
 
 def declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^(?:int|const char\s*\*)\s*(gqa_attn_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^(?:int64_t|int|const char\s*\*)\s*(gqa_attn_\w+)\s*\(", text, re.M)))
 
 
 def test_library_exports_every_declared_function():
@@ -45,9 +45,9 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_strerror():
-    assert gqa.version() == (1, 2)
-    msgs = [gqa.strerror(c) for c in range(7)]
-    assert len(set(msgs)) == 7 and msgs[0] == "success"
+    assert gqa.version() == (1, 3)
+    msgs = [gqa.strerror(c) for c in range(8)]
+    assert len(set(msgs)) == 8 and msgs[0] == "success"
     assert "unknown" in gqa.strerror(99)
 
 
@@ -99,6 +99,41 @@ def test_bwd_rejects_before_launch(over, code):
     assert gqa.bwd_raw(*(a[n] for n in ("q", "k", "v", "o", "lse", "dout", "dq", "dk", "dv", "delta", "B", "Hq",
                                          "Hkv", "Lq", "Lk", "D", "q_offset", "seg_q", "seg_k", "causal",
                                          "dtype", "stream"))) == code
+
+
+WS = 13 << 40
+SPLIT_GOOD = dict(GOOD, n_split=8, workspace=WS, workspace_bytes=1 << 30)
+
+
+def call_split(**over):
+    a = dict(SPLIT_GOOD)
+    a.update(over)
+    return gqa.fwd_split_raw(*(a[n] for n in ("q", "k", "v", "o", "lse", "B", "Hq", "Hkv", "Lq", "Lk", "D",
+                                              "q_offset", "seg_q", "seg_k", "causal", "dtype", "n_split",
+                                              "workspace", "workspace_bytes", "stream")))
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), 1), (dict(Lq=0), 2), (dict(D=128), 3), (dict(q=Q + 2), 4), (dict(o=K), 6),
+    (dict(n_split=0), 3), (dict(n_split=1025), 3), (dict(workspace=None), 1),
+    (dict(workspace_bytes=8 * 16 * 512 * 257 * 4 - 1), 7), (dict(workspace=WS + 4), 4),
+    (dict(workspace=Q + 4096), 6), (dict(workspace=LSE - 1024), 6),
+])
+def test_fwd_split_rejects_before_launch(over, code):
+    assert call_split(**over) == code
+
+
+def test_split_workspace_and_count():
+    # workspace: n_split * B * Hq * Lq * (D + 1) fp32 values
+    assert gqa.split_workspace(2, 16, 100, 256, 8) == 8 * 2 * 16 * 100 * 257 * 4
+    assert gqa.split_workspace(1, 16, 100, 256, 0) == 0
+    # one decode row over 60,926 keys (bf16, 64-key tiles): 4 workgroups without
+    # splits, so the count aims at 512 workgroups: 128 ranges of >= 4 tiles
+    assert gqa.split_count(1, 16, 4, 1, 60926, gqa.GQA_BF16) == 128
+    # the 30k fp32 forward already launches 3,808 workgroups
+    assert gqa.split_count(1, 16, 4, 30468, 30468, gqa.GQA_F32) == 1
+    # short keys: at most a quarter of the tile count (1000 keys = 32 tiles of 32)
+    assert gqa.split_count(1, 16, 4, 1, 1000, gqa.GQA_F32) == 8
 
 
 def test_python_binding_rejects_host_tensors():
