@@ -115,6 +115,38 @@ def run_bwd_workload(name, x, steps, warmup, torch, gqa, work, synth):
                 bytes=work.bwd_hbm_bytes(B, Hq, Hkv_, Lq, Lk, Dh, 4 if x.dtype == "f32" else 2))
 
 
+def run_split_workload(name, x, steps, warmup, torch, gqa, work):
+    """Short query block over a long key sequence: gqa_attn_fwd (one launch of
+    n_qb * G workgroups) against gqa_attn_fwd_split at the library's split
+    count (partials + merge), both timed; the record carries both times, the
+    algorithmic flops and the K/V bytes every call must read."""
+    q, k, v = dev_inputs(x, torch)
+    B, Hq, Lq, Dh = q.shape
+    Hkv_, Lk = k.shape[1], k.shape[2]
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device)
+    dt = {"f32": gqa.GQA_F32, "bf16": gqa.GQA_BF16, "f16": gqa.GQA_F16}[x.dtype]
+    n_split = gqa.split_count(B, Hq, Hkv_, Lq, Lk, dt)
+    ws = torch.empty(max(gqa.split_workspace(B, Hq, Lq, Dh, n_split), 16), dtype=torch.uint8, device=q.device)
+    plain = lambda: gqa.fwd(q, k, v, causal=x.causal, q_offset=x.q_offset, out=o, lse=lse)
+    split = lambda: gqa.fwd_split(q, k, v, causal=x.causal, q_offset=x.q_offset, n_split=n_split, out=o, lse=lse,
+                                  workspace=ws)
+    plain()
+    split()
+    torch.cuda.synchronize()
+    _, ms_plain, _, _ = time_calls(plain, steps, warmup, torch)
+    wall_ms, ms_split, ev_min, ev_max = time_calls(split, steps, warmup, torch)
+    fl = work.flops(B, Hq, Lq, Lk, Dh, causal=x.causal, q_offset=x.q_offset)
+    es = 4 if x.dtype == "f32" else 2
+    kv_bytes = 2 * B * Hkv_ * Lk * Dh * es
+    del q, k, v, o, lse, ws
+    torch.cuda.empty_cache()
+    return dict(workload=name, n_split=n_split, flops=fl, wall_ms=wall_ms, kernel_ms=ms_split,
+                kernel_ms_min=ev_min, kernel_ms_max=ev_max, unsplit_ms=ms_plain, speedup=ms_plain / ms_split,
+                tflops=fl / (wall_ms * 1e-3) / 1e12, kernel_tflops=fl / (ms_split * 1e-3) / 1e12,
+                kv_bytes=kv_bytes, kv_gbs=kv_bytes / (ms_split * 1e-3) / 1e9)
+
+
 def run_branch(steps, warmup, torch, gqa, work, synth):
     """Shared-prefix branch form, fp32: S = 30,468 prefix tokens, 40 branches of
     m = 256 query rows at positions S.. . Prefix part: one non-causal call of all
@@ -341,6 +373,13 @@ def main():
         for nm, Ls, dts in bwd_workloads.values():
             xs = synth.gqa(1, HQ, HKV, Ls, seed=0, dtype=dts)
             secondary.append(run_bwd_workload(nm, xs, max(3, args.steps // 2), 2, torch, gqa, work, synth))
+            del xs
+        # split-KV: 16 decode rows over the 64k state (bf16) and one 256-row
+        # branch over the 30k prefix (fp32)
+        for nm, Lq_, Lk_, dts in (("split-KV decode bf16 Lq=16 over Lk=60926", 16, 60926, "bf16"),
+                                  ("split-KV branch fp32 m=256 over S=30468 (Lk=30724)", 256, 30724, "f32")):
+            xs = synth.gqa(1, HQ, HKV, Lq_, Lk_, seed=0, dtype=dts, q_offset=Lk_ - Lq_)
+            secondary.append(run_split_workload(nm, xs, max(5, args.steps), 3, torch, gqa, work))
             del xs
         # packed segments, bf16, L = 131,072, lengths uniform in [2k, 32k] (seed 1), and the
         # single-segment comparator at the same L

@@ -159,8 +159,8 @@ int gqa_attn_fwd_split(const void* q, const void* k, const void* v, void* o, flo
  * n_split * B * Hq * Lq * (D + 1) * 4. Returns 0 for invalid arguments. */
 int64_t gqa_attn_split_workspace(int64_t B, int64_t Hq, int64_t Lq, int64_t D, int n_split);
 
-/* A split count for gqa_attn_fwd_split that fills the GPU (about two
- * workgroups per compute unit, each range at least 4 key tiles), from the
+/* A split count for gqa_attn_fwd_split that fills the GPU (about one
+ * workgroup per compute unit, each range at least 4 key tiles), from the
  * shape alone; 1 when gqa_attn_fwd already launches enough workgroups. */
 int gqa_attn_split_count(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int dtype);
 

@@ -23,9 +23,11 @@ bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
 bool is_pow2_rep(int64_t r) { return r == 1 || r == 2 || r == 4 || r == 8 || r == 16; }
 
 // split-KV: the most splits one launch takes, and the workgroup count the
-// recommended split count aims at (two per compute unit)
+// recommended split count aims at: one per compute unit (the forward kernels'
+// LDS use admits one workgroup per CU; measured on 16 decode rows over 60,926
+// keys, 64 splits = 256 workgroups ran in 51 us against 63 us for 128)
 constexpr int kMaxSplits = 1024;
-constexpr int64_t kSplitTargetWorkgroups = 512;
+constexpr int64_t kSplitTargetWorkgroups = 256;
 
 }  // namespace
 
@@ -108,7 +110,7 @@ GQA_API int gqa_attn_split_count(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq,
   const int64_t base = ((Lq + ppc - 1) / ppc) * B * Hkv * (n_rep / hpc);
   const int64_t tile = dtype == GQA_F32 ? gqa::kTileKeysF32 : gqa::kTileKeysH16;
   const int64_t n_tiles = (Lk + tile - 1) / tile;
-  // aim at two workgroups per compute unit, each split at least 4 tiles long
+  // aim at one workgroup per compute unit, each split at least 4 tiles long
   int64_t n = (kSplitTargetWorkgroups + base - 1) / base;
   n = n < n_tiles / 4 ? n : n_tiles / 4;
   n = n < kMaxSplits ? n : kMaxSplits;
@@ -146,22 +148,22 @@ GQA_API int gqa_attn_fwd_split(const void* q, const void* k, const void* v, void
       overlap(workspace, need, o, qo) || overlap(workspace, need, lse, rows * 4) ||
       (seg_q && overlap(workspace, need, seg_q, B * Lq * 4)) || (seg_k && overlap(workspace, need, seg_k, B * Lk * 4)))
     return GQA_ERR_ALIAS;
-  if ((int64_t)n_eff * p.n_qb * p.G >= ((int64_t)1 << 31)) return GQA_ERR_UNSUPPORTED;
+  if ((int64_t)n_eff * p.n_qb * p.G >= ((int64_t)1 << 31) || rows >= ((int64_t)1 << 31)) return GQA_ERR_UNSUPPORTED;
   p.n_split = n_eff;
   p.split_tiles = split_tiles;
   p.o_part = (float*)workspace;
   p.lse_part = (float*)workspace + n_eff * rows * D;
   if (launch_fwd(p, dtype, s) != hipSuccess) return GQA_ERR_LAUNCH;
-  const dim3 grid((unsigned)((rows + 3) / 4));
+  const dim3 grid((unsigned)rows);  // one workgroup per row (rows < 2^31, checked above)
   if (dtype == GQA_F32)
     hipLaunchKernelGGL(gqa::merge_splits_kernel<float>, grid, dim3(256), 0, s, p.o_part, p.lse_part, n_eff,
-                       (float*)o, lse, rows, D);
+                       (float*)o, lse, rows);
   else if (dtype == GQA_BF16)
     hipLaunchKernelGGL(gqa::merge_splits_kernel<__bf16>, grid, dim3(256), 0, s, p.o_part, p.lse_part, n_eff,
-                       (__bf16*)o, lse, rows, D);
+                       (__bf16*)o, lse, rows);
   else
     hipLaunchKernelGGL(gqa::merge_splits_kernel<_Float16>, grid, dim3(256), 0, s, p.o_part, p.lse_part, n_eff,
-                       (_Float16*)o, lse, rows, D);
+                       (_Float16*)o, lse, rows);
   return hipGetLastError() == hipSuccess ? GQA_OK : GQA_ERR_LAUNCH;
 }
 

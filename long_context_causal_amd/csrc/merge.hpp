@@ -91,35 +91,64 @@ __global__ __launch_bounds__(256) void merge_kernel(const T* o1, const float* ls
 
 // Merge of the n_split partial results of a split-KV forward (fp32 O parts
 // [n_split][rows][D], lse parts [n_split][rows]) into o (in T) and lse: the
-// same log-sum-exp combination over n_split disjoint key ranges. One wave per
-// row.
+// same log-sum-exp combination over n_split disjoint key ranges. One
+// workgroup per row (D = 256): wave 0 forms the max and the sum of the
+// weights; then 8 groups of 32 lanes each take every 8th split (lane c of a
+// group holds d 8c .. 8c + 7), with the loads of several splits in flight,
+// and the 8 group sums meet in LDS. With many splits and few rows (decoding)
+// a wave per row walking the splits one after another would wait on every
+// load in turn.
+constexpr int kMergeGroups = 8;
 template <typename T>
 __global__ __launch_bounds__(256) void merge_splits_kernel(const float* o_part, const float* lse_part, int n_split,
-                                                           T* o, float* lse, int64_t rows, int64_t D) {
-  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (r >= rows) return;
-  float M = -INFINITY;
-  for (int s = 0; s < n_split; ++s) M = fmaxf(M, lse_part[(int64_t)s * rows + r]);
-  float wsum = 0.f;
-  for (int s = 0; s < n_split; ++s) {
-    const float l = lse_part[(int64_t)s * rows + r];
-    wsum += (M == -INFINITY) ? 0.f : expf(l - M);
+                                                           T* o, float* lse, int64_t rows) {
+  __shared__ float part[kMergeGroups][kD];
+  __shared__ float s_max, s_inv, s_lse;
+  const int64_t r = blockIdx.x;
+  const int t = threadIdx.x, lane = t & 63;
+  if (t < 64) {
+    float m = -INFINITY;
+    for (int s = lane; s < n_split; s += 64) m = fmaxf(m, lse_part[(int64_t)s * rows + r]);
+    for (int x = 32; x >= 1; x >>= 1) m = fmaxf(m, __shfl_xor(m, x));
+    float sum = 0.f;
+    if (m != -INFINITY)
+      for (int s = lane; s < n_split; s += 64) sum += expf(lse_part[(int64_t)s * rows + r] - m);
+    for (int x = 32; x >= 1; x >>= 1) sum += __shfl_xor(sum, x);
+    if (lane == 0) {
+      s_max = m;
+      s_inv = sum > 0.f ? 1.f / sum : 0.f;
+      s_lse = (m == -INFINITY) ? -INFINITY : m + logf(sum);
+    }
   }
-  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  for (int64_t d = (int64_t)lane * 8; d < D; d += 512) {
-    float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < n_split; ++s) {
-      const float l = lse_part[(int64_t)s * rows + r];
-      const float w = (M == -INFINITY) ? 0.f : expf(l - M) * inv;
+  __syncthreads();
+  const float M = s_max, inv = s_inv;
+  const int sg = t >> 5, c = t & 31;
+  float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (M != -INFINITY) {
+#pragma unroll 4
+    for (int s = sg; s < n_split; s += kMergeGroups) {
+      const float w = expf(lse_part[(int64_t)s * rows + r] - M) * inv;
       float x[8];
-      load8<float>(o_part + ((int64_t)s * rows + r) * D + d, x);
+      load8<float>(o_part + ((int64_t)s * rows + r) * kD + 8 * c, x);
 #pragma unroll
       for (int i = 0; i < 8; ++i) z[i] = fmaf(w, x[i], z[i]);
     }
-    store8<T>(o + r * D + d, z);
   }
-  if (lane == 0) lse[r] = (M == -INFINITY) ? -INFINITY : M + logf(wsum);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) part[sg][8 * c + i] = z[i];
+  __syncthreads();
+  if (t < 32) {
+    float y[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float acc = 0.f;
+#pragma unroll
+      for (int g2 = 0; g2 < kMergeGroups; ++g2) acc += part[g2][8 * t + i];
+      y[i] = acc;
+    }
+    store8<T>(o + r * kD + 8 * t, y);
+  }
+  if (t == 0) lse[r] = s_lse;
 }
 
 }  // namespace gqa

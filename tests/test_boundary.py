@@ -128,8 +128,8 @@ def test_split_workspace_and_count():
     assert gqa.split_workspace(2, 16, 100, 256, 8) == 8 * 2 * 16 * 100 * 257 * 4
     assert gqa.split_workspace(1, 16, 100, 256, 0) == 0
     # one decode row over 60,926 keys (bf16, 64-key tiles): 4 workgroups without
-    # splits, so the count aims at 512 workgroups: 128 ranges of >= 4 tiles
-    assert gqa.split_count(1, 16, 4, 1, 60926, gqa.GQA_BF16) == 128
+    # splits, so the count aims at 256 workgroups: 64 ranges of >= 4 tiles
+    assert gqa.split_count(1, 16, 4, 1, 60926, gqa.GQA_BF16) == 64
     # the 30k fp32 forward already launches 3,808 workgroups
     assert gqa.split_count(1, 16, 4, 30468, 30468, gqa.GQA_F32) == 1
     # short keys: at most a quarter of the tile count (1000 keys = 32 tiles of 32)
