@@ -302,7 +302,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only", default=None,
                     help="run one workload: f32-15231, f32-30468, f32-60926, bf16-60926, f16-60926, "
-                         "bwd-f32-30468, bwd-bf16-60926")
+                         "bwd-f32-30468, bwd-bf16-60926, split-decode-bf16, split-branch-f32")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (3 times) to calibrate HBM byte counters")
     ap.add_argument("--pmc-report", nargs=4, metavar=("FETCH_DB", "WRITE_DB", "KERNEL_SUBSTR", "WORKLOAD"),
@@ -345,6 +345,16 @@ def main():
         "bwd-f32-30468": ("causal GQA bwd fp32 B=1 Hq=16 Hkv=4 D=256 L=30468", 30468, "f32"),
         "bwd-bf16-60926": ("causal GQA bwd bf16 B=1 Hq=16 Hkv=4 D=256 L=60926", 60926, "bf16"),
     }
+    split_workloads = {
+        "split-decode-bf16": ("split-KV decode bf16 Lq=16 over Lk=60926", 16, 60926, "bf16"),
+        "split-branch-f32": ("split-KV branch fp32 m=256 over S=30468 (Lk=30724)", 256, 30724, "f32"),
+    }
+    if args.only in split_workloads:
+        # a profiling aid: the split-KV workload alone, its record on one line
+        nm, Lq_, Lk_, dts = split_workloads[args.only]
+        xs = synth.gqa(1, HQ, HKV, Lq_, Lk_, seed=0, dtype=dts, q_offset=Lk_ - Lq_)
+        print(json.dumps(run_split_workload(nm, xs, args.steps, args.warmup, torch, gqa, work)), flush=True)
+        return
     if args.only in bwd_workloads:
         # a profiling aid: the backward alone, its record on one line
         nm, Ls, dts = bwd_workloads[args.only]
@@ -376,8 +386,7 @@ def main():
             del xs
         # split-KV: 16 decode rows over the 64k state (bf16) and one 256-row
         # branch over the 30k prefix (fp32)
-        for nm, Lq_, Lk_, dts in (("split-KV decode bf16 Lq=16 over Lk=60926", 16, 60926, "bf16"),
-                                  ("split-KV branch fp32 m=256 over S=30468 (Lk=30724)", 256, 30724, "f32")):
+        for nm, Lq_, Lk_, dts in split_workloads.values():
             xs = synth.gqa(1, HQ, HKV, Lq_, Lk_, seed=0, dtype=dts, q_offset=Lk_ - Lq_)
             secondary.append(run_split_workload(nm, xs, max(5, args.steps), 3, torch, gqa, work))
             del xs

@@ -214,65 +214,77 @@ __global__ __launch_bounds__(kWavesH * 64) void bwd_dq_h16_kernel(BwdParams bp) 
     const int64_t k0 = (int64_t)t * kBkH;
     const uint32_t so = (uint32_t)st * kStage;
 
-    // S^T = K Q^T and dP^T = V dO^T, two key halves each (4 chains); lane holds
-    // key 32 j + 8 (r / 4) + 4 g + r % 4 of its row. Fragments read two steps
-    // ahead; the next tile's copies are spread over the steps.
+    // mask of the tile in 32 bits: key 32 j + 8 (r / 4) + 4 g + r % 4 of the
+    // tile is visible to the lane's row iff it is below kl (causal and Lk) and
+    // (with ids) its id equals the row's
+    const bool seg_elem = SEG && !(use_bits && ((sm.bits.full[t >> 5] >> (t & 31)) & 1u));
+    const int64_t kend = p.causal ? min(p.Lk, p.q_offset + row + 1) : p.Lk;
+    const int kl = (int)max((int64_t)0, min((int64_t)kBkH, kend - k0));
+
+    // S^T = K Q^T, two key halves (2 chains of 16 products); lane holds key
+    // 32 j + 8 (r / 4) + 4 g + r % 4 of its row. K fragments two steps ahead;
+    // the K copies of the next tile spread over the steps.
     f32x16 s[2], dp[2];
-    V8 kr[3][2], vr[3][2];
+    {
+      V8 kr[3][2];
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+      for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        kr[u][j] = row_frag<V8>(pk0, u, j, so);
-        vr[u][j] = row_frag<V8>(pv0, u, j, so);
+        for (int j = 0; j < 2; ++j) kr[u][j] = row_frag<V8>(pk0, u, j, so);
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+        if (c + 2 < 16) {
+#pragma unroll
+          for (int j = 0; j < 2; ++j) kr[(c + 2) % 3][j] = row_frag<V8>(pk0, c + 2, j, so);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) s[j] = Elem<E>::mfma(kr[c % 3][j], qf[c], c == 0 ? f32x16{} : s[j]);
+        if ((c & 1) == 0) ck.block(8 * wave + (c >> 1), lane);
+        __builtin_amdgcn_sched_barrier(0);
       }
+    }
+    // dP^T = V dO^T (2 chains of 16) with P^T = exp2(S^T log2(e)/sqrt(D) -
+    // lse log2(e)) formed beside them, one score per product (score e is
+    // s[e / 16][e % 16]); the V copies of the next tile spread over the steps;
+    // key ids of the 4-key group of a score read one group ahead.
+    float pv[32];
+    {
+      V8 vr[3][2];
 #pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      if (c + 2 < 16) {
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) vr[u][j] = row_frag<V8>(pv0, u, j, so);
+      i32x4b id4[2];
+      id4[0] = i32x4b{sq, sq, sq, sq};
+      if (seg_elem) id4[0] = *(const i32x4b*)(&sm.segk[st][4 * g]);
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+        if (c + 2 < 16) {
+#pragma unroll
+          for (int j = 0; j < 2; ++j) vr[(c + 2) % 3][j] = row_frag<V8>(pv0, c + 2, j, so);
+        }
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          kr[(c + 2) % 3][j] = row_frag<V8>(pk0, c + 2, j, so);
-          vr[(c + 2) % 3][j] = row_frag<V8>(pv0, c + 2, j, so);
+          dp[j] = Elem<E>::mfma(vr[c % 3][j], df[c], c == 0 ? f32x16{} : dp[j]);
+          const int e = 2 * c + j, je = e >> 4, re = e & 15, grp = e >> 2;
+          if ((e & 3) == 1 && grp + 1 < 8) {
+            const int gn = grp + 1;  // group gn: half gn / 4, registers 4 (gn % 4) ..
+            id4[gn & 1] = i32x4b{sq, sq, sq, sq};
+            if (seg_elem) id4[gn & 1] = *(const i32x4b*)(&sm.segk[st][32 * (gn >> 2) + 8 * (gn & 3) + 4 * g]);
+          }
+          const int rk = 32 * je + 8 * (re >> 2) + 4 * g + (re & 3);
+          const float x = fast_exp2(fmaf(s[je][re], sl2, -lse2));
+          pv[e] = (rk < kl && id4[grp & 1][re & 3] == sq) ? x : 0.f;
         }
+        if ((c & 1) == 1) cv.block(8 * wave + (c >> 1), lane);
+        __builtin_amdgcn_sched_barrier(0);
       }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        s[j] = Elem<E>::mfma(kr[c % 3][j], qf[c], c == 0 ? f32x16{} : s[j]);
-        dp[j] = Elem<E>::mfma(vr[c % 3][j], df[c], c == 0 ? f32x16{} : dp[j]);
-      }
-      // even steps: K block c / 2 of this wave; odd steps: V block c / 2
-      if ((c & 1) == 0) ck.block(8 * wave + (c >> 1), lane);
-      else cv.block(8 * wave + (c >> 1), lane);
-      __builtin_amdgcn_sched_barrier(0);
     }
-
-    // dS^T = P^T (dP^T - delta), P^T = exp2(S^T log2(e)/sqrt(D) - lse log2(e)),
-    // masked where the tile needs it; packed pairs, key quarter h in dsk[4 h ..]
-    const bool seg_elem = SEG && !(use_bits && ((sm.bits.full[t >> 5] >> (t & 31)) & 1u));
-    const bool need_mask = seg_elem || k0 + kBkH > p.Lk || (p.causal && k0 + kBkH - 1 > p.q_offset + pw);
-    const int64_t lim = p.causal ? p.q_offset + row : INT64_MAX;
+    // dS^T = P^T (dP^T - delta), packed in pairs; key quarter h in dsk[4 h ..]
     unsigned dsk[16];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        i32x4b ids = {sq, sq, sq, sq};
-        if (seg_elem) ids = *(const i32x4b*)(&sm.segk[st][32 * j + 8 * r4 + 4 * g]);
-        float dsv[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 4 * r4 + i;
-          float pv = fast_exp2(fmaf(s[j][r], sl2, -lse2));
-          if (need_mask) {
-            const int64_t key = k0 + 32 * j + 8 * r4 + 4 * g + i;
-            pv = (key < p.Lk && key <= lim && ids[i] == sq) ? pv : 0.f;
-          }
-          dsv[i] = pv * (dp[j][r] - delta);
-        }
-        dsk[8 * j + 2 * r4] = Elem<E>::pack(dsv[0], dsv[1]);
-        dsk[8 * j + 2 * r4 + 1] = Elem<E>::pack(dsv[2], dsv[3]);
-      }
-    }
+    for (int e = 0; e < 32; e += 2)
+      dsk[e >> 1] = Elem<E>::pack(pv[e] * (dp[e >> 4][e & 15] - delta), pv[e + 1] * (dp[e >> 4][(e + 1) & 15] - delta));
     __builtin_amdgcn_sched_barrier(0);
 
     // dQ^T += K^T dS^T: 4 key quarters x 8 d blocks; K^T fragments through the
@@ -430,60 +442,82 @@ __global__ __launch_bounds__(kWavesH * 64) void bwd_dkv_h16_kernel(BwdParams bp)
     const int64_t i0 = (int64_t)rb * kRowsDKVH;
     const uint32_t so = (uint32_t)st * kStage;
 
-    // S = Q K^T and dP = dO V^T: lane holds row 8 (r / 4) + 4 g + r % 4 of its
-    // key; row fragments two steps ahead; the next tile's copies spread over
-    // the steps
-    f32x16 s, dp;
-    V8 qr[3], dr[3], vr[3];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      qr[u] = row_frag<V8>(pq0, u, 0, so);
-      dr[u] = row_frag<V8>(pd0, u, 0, so);
-      vr[u] = row_frag<V8>(pvw, u, 0, 0);
-    }
-#pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      if (c + 2 < 16) {
-        qr[(c + 2) % 3] = row_frag<V8>(pq0, c + 2, 0, so);
-        dr[(c + 2) % 3] = row_frag<V8>(pd0, c + 2, 0, so);
-        vr[(c + 2) % 3] = row_frag<V8>(pvw, c + 2, 0, 0);
-      }
-      s = Elem<E>::mfma(qr[c % 3], kf[c], c == 0 ? f32x16{} : s);
-      dp = Elem<E>::mfma(dr[c % 3], vr[c % 3], c == 0 ? f32x16{} : dp);
-      // steps 4 k: Q block k of this wave; steps 4 k + 2: dO block k
-      if ((c & 3) == 0) cq.block(4 * wave + (c >> 2), lane);
-      if ((c & 3) == 2) cd.block(4 * wave + (c >> 2), lane);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-
-    // P = exp2(S log2(e)/sqrt(D) - lse log2(e)), dS = P (dP - delta), masked
-    // where needed; packed pairs, row quarter h in pk/dk[4 h ..]
+    // mask limits of the tile (32-bit): row ri of the tile sees the lane's key
+    // iff lim <= ri < nrow and (with ids) the row's id equals the key's
     const bool seg_elem = SEG && !(use_bits && ((sm.bits.full[rb >> 5] >> (rb & 31)) & 1u));
     const bool need_mask = seg_elem || i0 + kRowsDKVH > p.Lq || (p.causal && kw0 + kKeysDKVH - 1 > p.q_offset + i0);
     const int lim = (p.causal && need_mask)
                         ? (int)max((int64_t)-1, min((int64_t)kRowsDKVH, key - p.q_offset - i0))
-                        : -1;  // row index within the tile from which the lane's key is visible
+                        : -1;
     const int nrow = (int)min((int64_t)kRowsDKVH, p.Lq - i0);
+
+    // S = Q K^T (16 products, one chain): lane holds row 8 (r / 4) + 4 g + r % 4
+    // of its key. Q fragments two steps ahead; the next tile's copies spread
+    // over the steps.
+    f32x16 s, dp;
+    {
+      V8 qr[3];
+      qr[0] = row_frag<V8>(pq0, 0, 0, so);
+      qr[1] = row_frag<V8>(pq0, 1, 0, so);
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+        if (c + 2 < 16) qr[(c + 2) % 3] = row_frag<V8>(pq0, c + 2, 0, so);
+        s = Elem<E>::mfma(qr[c % 3], kf[c], c == 0 ? f32x16{} : s);
+        // steps 4 k: Q block k of this wave; steps 4 k + 2: dO block k
+        if ((c & 3) == 0) cq.block(4 * wave + (c >> 2), lane);
+        if ((c & 3) == 2) cd.block(4 * wave + (c >> 2), lane);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // dP = dO V^T (16 products) with P = exp2(S log2(e)/sqrt(D) - lse log2(e))
+    // formed beside them (P needs only S): register r at step r. The lse (and
+    // ids) of the 4 rows of register group r / 4 are read one group ahead.
+    float pv[16];
+    {
+      V8 dr[3], vr[3];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        dr[u] = row_frag<V8>(pd0, u, 0, so);
+        vr[u] = row_frag<V8>(pvw, u, 0, 0);
+      }
+      f32x4 l4[2];
+      i32x4b id4[2];
+      l4[0] = *(const f32x4*)(&sm.lse[st][4 * g]);
+      id4[0] = i32x4b{sk, sk, sk, sk};
+      if (seg_elem) id4[0] = *(const i32x4b*)(&sm.segq[st][4 * g]);
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+        if (c + 2 < 16) {
+          dr[(c + 2) % 3] = row_frag<V8>(pd0, c + 2, 0, so);
+          vr[(c + 2) % 3] = row_frag<V8>(pvw, c + 2, 0, 0);
+        }
+        if ((c & 3) == 1 && c < 12) {
+          const int j = (c >> 2) + 1;
+          l4[j & 1] = *(const f32x4*)(&sm.lse[st][8 * j + 4 * g]);
+          id4[j & 1] = i32x4b{sk, sk, sk, sk};
+          if (seg_elem) id4[j & 1] = *(const i32x4b*)(&sm.segq[st][8 * j + 4 * g]);
+        }
+        dp = Elem<E>::mfma(dr[c % 3], vr[c % 3], c == 0 ? f32x16{} : dp);
+        {
+          const int j = c >> 2, i = c & 3, ri = 8 * j + 4 * g + i;
+          const float lv = l4[j & 1][i];
+          const float l2 = lv == -INFINITY ? 0.f : lv * 1.4426950408889634f;
+          const float x = fast_exp2(fmaf(s[c], sl2, -l2));
+          pv[c] = (ri < nrow && ri >= lim && id4[j & 1][i] == sk) ? x : 0.f;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // dS = P (dP - delta); P and dS packed in pairs, row quarter h in pk/dk[4 h ..]
     unsigned pk[8], dk[8];
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
-      const int ri0 = 8 * r4 + 4 * g;
-      const f32x4 l4 = *(const f32x4*)(&sm.lse[st][ri0]);
-      const f32x4 d4 = *(const f32x4*)(&sm.delta[st][ri0]);
-      i32x4b ids = {sk, sk, sk, sk};
-      if (seg_elem) ids = *(const i32x4b*)(&sm.segq[st][ri0]);
-      float pv[4], dsv[4];
+      const f32x4 d4 = *(const f32x4*)(&sm.delta[st][8 * r4 + 4 * g]);
+      float dsv[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 4 * r4 + i, ri = ri0 + i;
-        const float l2 = l4[i] == -INFINITY ? 0.f : l4[i] * 1.4426950408889634f;
-        float x = fast_exp2(fmaf(s[r], sl2, -l2));
-        x = (ri < nrow && ri >= lim && ids[i] == sk) ? x : 0.f;
-        pv[i] = x;
-        dsv[i] = x * (dp[r] - d4[i]);
-      }
-      pk[2 * r4] = Elem<E>::pack(pv[0], pv[1]);
-      pk[2 * r4 + 1] = Elem<E>::pack(pv[2], pv[3]);
+      for (int i = 0; i < 4; ++i) dsv[i] = pv[4 * r4 + i] * (dp[4 * r4 + i] - d4[i]);
+      pk[2 * r4] = Elem<E>::pack(pv[4 * r4], pv[4 * r4 + 1]);
+      pk[2 * r4 + 1] = Elem<E>::pack(pv[4 * r4 + 2], pv[4 * r4 + 3]);
       dk[2 * r4] = Elem<E>::pack(dsv[0], dsv[1]);
       dk[2 * r4 + 1] = Elem<E>::pack(dsv[2], dsv[3]);
     }
