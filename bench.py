@@ -83,11 +83,13 @@ def run_fwd_workload(name, x, steps, warmup, torch, gqa, work, seg=None):
                 bytes=work.hbm_bytes(B, Hq, Hkv_, Lq, Lk, Dh, 4 if x.dtype == "f32" else 2, seg is not None))
 
 
-def run_bwd_workload(name, x, steps, warmup, torch, gqa, work, synth):
+def run_bwd_workload(name, x, steps, warmup, torch, gqa, work, synth, seg=None):
     """The backward (dQ kernel + dK/dV kernel) on the forward's own o and lse;
-    dout drawn N(0,1) (seed 1). Times the backward call only."""
+    dout drawn N(0,1) (seed 1); optional packed segment ids. Times the backward
+    call only."""
     torch.cuda.synchronize()
     q, k, v = dev_inputs(x, torch)
+    sid = None if seg is None else torch.from_numpy(seg[None]).to("cuda:0")
     g = synth.Grad(x.q.shape, seed=1, dtype=x.dtype)
     tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[x.dtype]
     if x.dtype == "f32":
@@ -95,24 +97,25 @@ def run_bwd_workload(name, x, steps, warmup, torch, gqa, work, synth):
     else:
         do = torch.from_numpy(g.bits.view(np.int16)).to("cuda:0").view(tdt)
     del g
-    o, lse = gqa.fwd(q, k, v, causal=x.causal, q_offset=x.q_offset)
+    o, lse = gqa.fwd(q, k, v, causal=x.causal, q_offset=x.q_offset, seg_q=sid, seg_k=sid)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     delta = torch.empty_like(lse)
-    fn = lambda: gqa.bwd(q, k, v, o, lse, do, causal=x.causal, q_offset=x.q_offset, dq=dq, dk=dk, dv=dv,
-                         delta=delta)
+    fn = lambda: gqa.bwd(q, k, v, o, lse, do, causal=x.causal, q_offset=x.q_offset, seg_q=sid, seg_k=sid, dq=dq,
+                         dk=dk, dv=dv, delta=delta)
     fn()
     torch.cuda.synchronize()
     wall_ms, ev_ms, ev_min, ev_max = time_calls(fn, steps, warmup, torch)
     B, Hq, Lq, Dh = q.shape
     Hkv_, Lk = k.shape[1], k.shape[2]
-    fl = work.bwd_flops(B, Hq, Lq, Lk, Dh, causal=x.causal, q_offset=x.q_offset)
-    ex = work.bwd_exec_flops(B, Hq, Lq, Lk, Dh, causal=x.causal, q_offset=x.q_offset)
-    del q, k, v, do, o, lse, dq, dk, dv, delta
+    sk = None if seg is None else seg[None]
+    fl = work.bwd_flops(B, Hq, Lq, Lk, Dh, causal=x.causal, q_offset=x.q_offset, seg_q=sk, seg_k=sk)
+    ex = work.bwd_exec_flops(B, Hq, Lq, Lk, Dh, causal=x.causal, q_offset=x.q_offset, seg_q=sk, seg_k=sk)
+    del q, k, v, do, o, lse, dq, dk, dv, delta, sid
     torch.cuda.empty_cache()
     return dict(workload=name, flops=fl, exec_flops=ex, wall_ms=wall_ms, kernel_ms=ev_ms, kernel_ms_min=ev_min,
                 kernel_ms_max=ev_max, tflops=fl / (wall_ms * 1e-3) / 1e12, kernel_tflops=fl / (ev_ms * 1e-3) / 1e12,
                 exec_tflops=ex / (ev_ms * 1e-3) / 1e12,
-                bytes=work.bwd_hbm_bytes(B, Hq, Hkv_, Lq, Lk, Dh, 4 if x.dtype == "f32" else 2))
+                bytes=work.bwd_hbm_bytes(B, Hq, Hkv_, Lq, Lk, Dh, 4 if x.dtype == "f32" else 2, seg is not None))
 
 
 def run_split_workload(name, x, steps, warmup, torch, gqa, work):
@@ -400,6 +403,9 @@ def main():
                              max(3, args.steps // 2), 2, torch, gqa, work, seg=ids)
         secondary.append(r)
         r = run_fwd_workload("single-segment comparator bf16 L=131072 (no ids)", xs, 3, 1, torch, gqa, work)
+        secondary.append(r)
+        r = run_bwd_workload("segmented bwd bf16 L=131072, %d segments (2k-32k)" % len(lens), xs, 3, 1, torch, gqa,
+                             work, synth, seg=ids)
         secondary.append(r)
         del xs
     for r in [prim] + secondary:
