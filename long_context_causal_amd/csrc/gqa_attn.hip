@@ -186,13 +186,13 @@ GQA_API int gqa_attn_bwd(const void* q, const void* k, const void* v, const void
     return GQA_ERR_ALIGN;
   const int64_t es = dtype == GQA_F32 ? 4 : 2;
   const int64_t qo = B * Hq * Lq * D * es, kv = B * Hkv * Lk * D * es, rl = B * Hq * Lq * 4;
-  const void* ins[6] = {q, k, v, o, lse, dout};
-  const int64_t in_n[6] = {qo, kv, kv, qo, rl, qo};
+  const void* ins[8] = {q, k, v, o, lse, dout, seg_q, seg_k};
+  const int64_t in_n[8] = {qo, kv, kv, qo, rl, qo, seg_q ? B * Lq * 4 : 0, seg_k ? B * Lk * 4 : 0};
   const void* outs[4] = {dq, dk, dv, delta};
   const int64_t out_n[4] = {qo, kv, kv, rl};
   for (int a = 0; a < 4; ++a) {
-    for (int i = 0; i < 6; ++i)
-      if (overlap(outs[a], out_n[a], ins[i], in_n[i])) return GQA_ERR_ALIAS;
+    for (int i = 0; i < 8; ++i)
+      if (in_n[i] > 0 && overlap(outs[a], out_n[a], ins[i], in_n[i])) return GQA_ERR_ALIAS;
     for (int b2 = a + 1; b2 < 4; ++b2)
       if (overlap(outs[a], out_n[a], outs[b2], out_n[b2])) return GQA_ERR_ALIAS;
   }

@@ -91,7 +91,8 @@ BWD_GOOD = dict(q=Q, k=K, v=V, o=O, lse=LSE, dout=DO, dq=DQ, dk=DK, dv=DV, delta
     (dict(Lk=(1 << 21) + 1), 3),
     (dict(dout=DO + 4), 4), (dict(dq=DQ + 8), 4), (dict(dk=DK + 2), 4), (dict(delta=DEL + 2), 4),
     (dict(dq=Q), 6), (dict(dq=DO + 256), 6), (dict(dk=V), 6), (dict(dv=DK), 6), (dict(delta=LSE), 6),
-    (dict(delta=DQ + 1024), 6), (dict(dv=O + 1024), 6),
+    (dict(delta=DQ + 1024), 6), (dict(dv=O + 1024), 6), (dict(seg_q=DQ + 64, seg_k=SK), 6),
+    (dict(seg_q=SQ, seg_k=DEL), 6),
 ])
 def test_bwd_rejects_before_launch(over, code):
     a = dict(BWD_GOOD)
