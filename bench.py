@@ -192,7 +192,7 @@ def cpu_baseline(x, target_s=15.0):
     """The oracle (fp64, OpenMP over rows) on a bounded sample of query rows of
     the same workload, all heads; rows spread evenly over the sequence."""
     import oracle
-    from long_context_causal_amd import work
+    import synth
     L = x.q.shape[2]
     threads = len(os.sched_getaffinity(0))
     threads = min(threads, 16)
@@ -210,9 +210,30 @@ def cpu_baseline(x, target_s=15.0):
     oracle.attn(x.q, x.k, x.v, causal=True, rows=rows, nthreads=threads)
     dt = time.perf_counter() - t0
     fl = 4 * D * HQ * pairs(rows)
+    # the whole small case (L = 512, inputs x 1/16) on one thread
+    xs = synth.gqa(1, HQ, HKV, 512, seed=0, scale=1.0 / 16)
+    t0 = time.perf_counter()
+    oracle.attn(xs.q, xs.k, xs.v, causal=True, nthreads=1)
+    dt1 = time.perf_counter() - t0
+    fl1 = 4 * D * HQ * 512 * 513 // 2
     return dict(value=fl / dt / 1e12, unit="TFLOP/s", cores=threads, kind="oracle",
                 sample="%d of %d query rows (evenly spaced) x 16 heads of the fp32 causal forward at L=%d, "
-                       "all their visible keys; %.1f s" % (n, L, L, dt))
+                       "all their visible keys; %.1f s" % (n, L, L, dt),
+                cpu_model=cpu_model(),
+                one_thread_L512=dict(value=fl1 / dt1 / 1e12, unit="TFLOP/s", seconds=dt1,
+                                     sample="the whole fp32 causal forward at L=512, one thread"))
+
+
+def cpu_model():
+    """The host CPU's model name (/proc/cpuinfo), or None where it is not listed."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 # Sources and translation unit of each forward kernel.
