@@ -2,18 +2,31 @@
 // output, full-fp32 products on gfx950 MFMA (v_mfma_f32_32x32x2_f32; no
 // reduced-precision variant, matching the pages' fp32 runs with TF32 off).
 //
-// One workgroup = 4 waves, one per SIMD: Q (128 VGPRs per lane) and the O^T
-// accumulator (128) stay in registers. For Hq/Hkv = 4 the workgroup owns the 4
-// query heads of one KV head x 32 positions. Key tiles of 32 keys (32 KB each
-// for K and V) are copied HBM -> LDS once per workgroup with async
-// global_load_lds, double-buffered, and shared by the 4 heads.
+// One workgroup = 4 waves, one per SIMD. For Hq/Hkv = 4 the workgroup owns the
+// 4 query heads of one KV head x 32 positions; each wave owns one head and 32
+// query rows. Key tiles of 32 keys (32 KB each for K and V) are copied HBM ->
+// LDS once per workgroup with async buffer loads and shared by the 4 heads.
+// Q (128 registers per lane) lives in AGPRs, read by the score products in
+// place; the O^T accumulator (128), the scores and P live in VGPRs.
 //
-// The data flow matches the bf16 kernel: S^T = K Q^T leaves one query row per
-// lane (16 of the 32 keys in registers), the base-2 online softmax with a lazy
-// rescale runs lane-locally plus one lane-pair exchange for the row max, and
-// O^T += V^T P^T takes P straight from the S^T registers. The fp32 MFMA takes
-// one element per lane per operand, so V needs no transposing read: lanes
-// 0-31 read 32 consecutive d of one key row.
+// S^T = K Q^T leaves one query row per lane (16 of the 32 keys in registers),
+// the base-2 online softmax with a lazy rescale runs lane-locally plus one
+// lane-pair exchange for the row max, and O^T += V^T P^T takes P straight from
+// the S^T registers. The fp32 MFMA takes one element per lane per operand, so
+// V needs no transposing read: lanes 0-31 read 32 consecutive d of one key row.
+//
+// The loop is software-pipelined over tiles, so the matrix cores never wait
+// for the softmax. Step i:
+//   phase A: the 128 score products of the next tile, with the 16 exps of
+//            the current tile spread between them, and the tile copies;
+//   phase B: the 128 PV products of the current tile, with the mask and row
+//            max of the next tile's scores spread between them;
+//   after:   the lazy update of the running max. The max moves only when a
+//            row's maximum grows by more than 8 in log2 units. Then O and l
+//            are rescaled, rarely.
+// K and V have two-stage rings of their own. In step i the copies of K(#i+2)
+// and V(#i+1) refill the stages that K(#i) and V(#i-1) left, and one barrier
+// per step covers both.
 #pragma once
 #include "common.hpp"
 
@@ -36,7 +49,7 @@ __device__ __forceinline__ int swzv_f(int key) { return (((key >> 2) & 1) << 3) 
 struct SmemF {
   __attribute__((aligned(16))) char k[2][kTileBytesF];
   __attribute__((aligned(16))) char v[2][kTileBytesF];
-  __attribute__((aligned(16))) int segk[2][kBkF];
+  __attribute__((aligned(16))) int segk[2][2 * kBkF];  // key ids of a K stage (the upper half takes the copy's spill)
   SegBits bits;
 };
 
@@ -67,30 +80,43 @@ struct LanesF {
   }
 };
 
-// Async copy of key tile t into LDS stage `st`: wave w copies key rows
-// w, w + W, ... (1 KB each, lane l fetching the global chunk that the swizzle
-// places at its position). Missing keys past Lk re-read row Lk-1.
-template <int W>
-__device__ __forceinline__ void load_tile_f(SmemF& sm, int st, const char* kb, const char* vb, const int32_t* skb,
-                                            int64_t t, int64_t Lk, int wave, int lane, const LanesF& ln) {
-  static_assert(W == 4, "the lane patterns assume 4 waves");
-  const char* kt = kb + t * kTileBytesF;
-  const char* vt = vb + t * kTileBytesF;
-  const int64_t last = Lk - 1 - t * kBkF;  // last valid key within the tile (>= 0)
-#pragma unroll
-  for (int it = 0; it < kBkF / W; ++it) {
-    const int kk = wave + W * it;
-    const uint32_t src = (uint32_t)(kk <= last ? kk : (int)last) * 1024u;
-    g2lds16(kt, src + ln.ldk[it & 3], sm.k[st] + kk * 1024);
-    g2lds16(vt, src + ln.ldv[it & 1], sm.v[st] + kk * 1024);
+// Async copy of one part (K with its key segment ids, or V) of key tile t
+// (keys 32t .. 32t+31) into an LDS stage. Wave w copies the key rows w + 4 it,
+// it = 0..7 (1 KB each; lane l fetches the 16-byte chunk that the swizzle
+// places at its position). The buffer resource ends at Lk, so keys past it
+// read as zeros (finite data that the mask removes); a resource of size 0 (no
+// tile) writes only zeros.
+struct PartCopyF {
+  rsrc_t r, rs;    // rows (K or V) and key ids from the tile start
+  uint32_t lds;    // LDS stage
+  uint32_t s_lds;  // LDS stage of the ids
+  __device__ __forceinline__ void row(int it, int wave, uint32_t lane_off) const {
+    const uint32_t kk = (uint32_t)(wave + 4 * it);
+    buf2lds16(r, kk * 1024u + lane_off, lds + kk * 1024u);
   }
-  if (skb != nullptr && wave == W - 1 && lane < kBkF) {
-    g2lds4((const char*)(skb + t * kBkF), (uint32_t)min((int64_t)lane, last) * 4u, sm.segk[st]);
+  // the tile's 32 ids (lanes 32-63 read zeros into the stage's upper half)
+  __device__ __forceinline__ void ids(int wave, int lane) const {
+    if (wave == 3) buf2lds4(rs, (uint32_t)lane * 4u, s_lds);  // uniform branch
   }
+};
+
+__device__ __forceinline__ PartCopyF part_copy_f(uint32_t lds, uint32_t s_lds, const char* base, const int32_t* skb,
+                                                 int64_t t, bool valid, int64_t Lk) {
+  const int64_t keys = valid ? min((int64_t)kBkF, Lk - t * kBkF) : 0;
+  PartCopyF c;
+  c.r = make_rsrc(base + (valid ? t * kTileBytesF : 0), (uint32_t)keys * 1024u);
+  c.rs = make_rsrc(skb != nullptr ? skb + (valid ? t * kBkF : 0) : nullptr, skb != nullptr ? (uint32_t)keys * 4u : 0u);
+  c.lds = lds;
+  c.s_lds = s_lds;
+  return c;
 }
+
+// Each product and the work placed beside it form one scheduling segment.
+#define GQA_SEGMENT_END_F() __builtin_amdgcn_sched_barrier(0)
 
 template <int W>
 __global__ __launch_bounds__(W * 64) void fwd_f32_kernel(FwdParams p) {
+  static_assert(W == 4, "the lane patterns assume 4 waves");
   __shared__ SmemF sm;
   const Work w = decode_work(p);
   const int wave = wave_id(), lane = lane_id();
@@ -117,8 +143,10 @@ __global__ __launch_bounds__(W * 64) void fwd_f32_kernel(FwdParams p) {
   const char* vb = (const char*)p.v + kv_head * p.Lk * kD * 4;
   const int32_t* skb = seg ? p.seg_k + (int64_t)w.b * p.Lk : nullptr;
   const int sq = seg ? p.seg_q[(int64_t)w.b * p.Lq + row_c] : 0;
+  const int64_t lim = p.q_offset + row;  // last key this row may see (causal)
 
-  // Q in registers: lane holds Q[row][8c + 4g + e], e = 0..3.
+  // Q: lane holds Q[row][8c + 4g + e], e = 0..3, in AGPRs (the empty asm
+  // statements keep it there; the products read it in place).
   f32x4 qf[32];
   const int64_t hq = ((int64_t)w.b * p.Hq + h) * p.Lq;
   {
@@ -127,6 +155,8 @@ __global__ __launch_bounds__(W * 64) void fwd_f32_kernel(FwdParams p) {
     for (int c = 0; c < 32; ++c) qf[c] = qr[2 * c + g];
   }
   wait_vm0_known();
+#pragma unroll
+  for (int c = 0; c < 32; ++c) asm volatile("" : "+a"(qf[c]));
 
   f32x16 acc[8];
 #pragma unroll
@@ -134,96 +164,169 @@ __global__ __launch_bounds__(W * 64) void fwd_f32_kernel(FwdParams p) {
   float m_run = -INFINITY, l_part = 0.f;
   const float sl2 = p.scale_log2;
 
-  int t = use_bits ? seg_next(sm.bits, t_lo, t_hi) : t_lo;
-  int st = 0;
   LanesF ln;
   ln.init(wave, lane);
-  if (t < t_hi) load_tile_f<W>(sm, 0, kb, vb, skb, t, p.Lk, wave, lane, ln);
-  while (t < t_hi) {
-    const int tn = use_bits ? seg_next(sm.bits, t + 1, t_hi) : t + 1;
-    wait_vm0();
-    __syncthreads();
-    if (tn < t_hi) load_tile_f<W>(sm, st ^ 1, kb, vb, skb, tn, p.Lk, wave, lane, ln);
-    const int64_t k0 = (int64_t)t * kBkF;
-    if (!(p.causal && k0 > p.q_offset + pw + 31)) {
-      const bool seg_full = !seg || (use_bits && ((sm.bits.full[t >> 5] >> (t & 31)) & 1u));
-      const bool need_mask = !seg_full || k0 + kBkF > p.Lk || (p.causal && k0 + kBkF - 1 > p.q_offset + pw);
-      const char* Ks = sm.k[st];
-      const char* Vs = sm.v[st];
+  const uint32_t kbase = lds_addr(sm.k[0]), vbase = lds_addr(sm.v[0]), sbase = lds_addr(sm.segk[0]);
 
-      // S^T = K Q^T: MFMA (c, e) contracts d = 8c + e (lanes 0-31) and 8c + 4 + e (lanes 32-63).
-      // K fragments are read two steps ahead of their MFMAs.
-      f32x16 s = {};
-      f32x4 kf0 = *(const f32x4*)(Ks + ln.kq[0]);
-      f32x4 kf1 = *(const f32x4*)(Ks + ln.kq[1]);
+  auto next_tile = [&](int t) -> int {
+    if (t >= t_hi) return t_hi;
+    return use_bits ? seg_next(sm.bits, t + 1, t_hi) : t + 1;
+  };
+  auto k_copy = [&](int st, int t) {
+    return part_copy_f(kbase + (uint32_t)st * kTileBytesF, sbase + (uint32_t)st * (2 * kBkF * 4), kb, skb, t,
+                       t < t_hi, p.Lk);
+  };
+  auto v_copy = [&](int st, int t) {
+    return part_copy_f(vbase + (uint32_t)st * kTileBytesF, 0u, vb, nullptr, t, t < t_hi, p.Lk);
+  };
+  // S^T of tile t from K stage st (32 chunks x 4 products, K read two chunks ahead)
+  auto mask_if_needed = [&](f32x16& s, int t, int st) {
+    if (t >= t_hi) {
+      // past the range: nothing visible (the zeros its copy wrote are no scores)
 #pragma unroll
-      for (int c = 0; c < 32; ++c) {
-        const f32x4 a = kf0;
-        kf0 = kf1;
-        if (c + 2 < 32) kf1 = *(const f32x4*)(Ks + ln.kq[(c + 2) & 7] + ((c + 2) >> 3) * 256);
+      for (int r = 0; r < 16; ++r) s[r] = -INFINITY;
+      return;
+    }
+    const int64_t k0 = (int64_t)t * kBkF;
+    const bool seg_full = !seg || (use_bits && ((sm.bits.full[t >> 5] >> (t & 31)) & 1u));
+    if (seg_full && k0 + kBkF <= p.Lk && !(p.causal && k0 + kBkF - 1 > p.q_offset + pw)) return;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) s = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], qf[c][e], s, 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      // lane holds keys k0 + 8(r/4) + 4g + r%4 of its row
-      if (need_mask) {
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int kk = 8 * r4 + 4 * g;
+      int4 ids = {0, 0, 0, 0};
+      if (!seg_full) ids = *(const int4*)(sm.segk[st] + kk);
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int kk = 8 * r4 + 4 * g;
-          int4 ids = {0, 0, 0, 0};
-          if (!seg_full) ids = *(const int4*)(sm.segk[st] + kk);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int64_t key = k0 + kk + e;
-            bool vis = key < p.Lk;
-            if (p.causal) vis = vis && key <= p.q_offset + row;
-            const int id = e == 0 ? ids.x : e == 1 ? ids.y : e == 2 ? ids.z : ids.w;
-            if (!seg_full) vis = vis && id == sq;
-            s[4 * r4 + e] = vis ? s[4 * r4 + e] : -INFINITY;
-          }
-        }
-      }
-      float mx = s[0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
-      mx = xor32_max(mx);
-      const float mxs = mx * sl2;
-      if (__builtin_amdgcn_ballot_w64(mxs > m_run + kLazyF)) {
-        const float m_new = fmaxf(m_run, mxs);
-        const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
-#pragma unroll
-        for (int n = 0; n < 8; ++n) acc[n] *= alpha;
-        l_part *= alpha;
-        m_run = m_new;
-      }
-      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-      float pr[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        pr[r] = fast_exp2(fmaf(s[r], sl2, -m_use));
-        l_part += pr[r];
-      }
-      // O^T += V^T P^T: MFMA tt contracts key 8(tt/4) + 4g + tt%4 (P register tt).
-      // The 8 V values of key step tt (one per d block) are read one step ahead.
-      float vcur[8], vnxt[8];
-#pragma unroll
-      for (int n = 0; n < 8; ++n) vcur[n] = *(const float*)(Vs + ln.vq[n & 1][0] + n * 128);
-#pragma unroll
-      for (int tt = 0; tt < 16; ++tt) {
-        if (tt + 1 < 16) {
-          const int u = tt + 1;
-#pragma unroll
-          for (int n = 0; n < 8; ++n) vnxt[n] = *(const float*)(Vs + ln.vq[n & 1][u & 3] + (u >> 2) * 8192 + n * 128);
-        }
-#pragma unroll
-        for (int n = 0; n < 8; ++n) acc[n] = __builtin_amdgcn_mfma_f32_32x32x2f32(vcur[n], pr[tt], acc[n], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int n = 0; n < 8; ++n) vcur[n] = vnxt[n];
+      for (int e = 0; e < 4; ++e) {
+        const int64_t key = k0 + kk + e;
+        bool vis = key < p.Lk;
+        if (p.causal) vis = vis && key <= lim;
+        const int id = e == 0 ? ids.x : e == 1 ? ids.y : e == 2 ? ids.z : ids.w;
+        if (!seg_full) vis = vis && id == sq;
+        s[4 * r4 + e] = vis ? s[4 * r4 + e] : -INFINITY;
       }
     }
-    t = tn;
-    st ^= 1;
+  };
+  // the lazy update of the running max from a tile's row max (raw scores)
+  auto lazy_update = [&](float mx) {
+    const float mxs = xor32_max(mx) * sl2;
+    if (__builtin_amdgcn_ballot_w64(mxs > m_run + kLazyF)) {
+      const float m_new = fmaxf(m_run, mxs);
+      const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
+#pragma unroll
+      for (int n = 0; n < 8; ++n) acc[n] *= alpha;
+      l_part *= alpha;
+      m_run = m_new;
+    }
+  };
+
+  int cur = use_bits ? seg_next(sm.bits, t_lo, t_hi) : t_lo;
+  if (cur < t_hi) {
+    int nxt = next_tile(cur), nn = next_tile(nxt);
+    // K(#0), K(#1) and V(#0) into stages 0, 1 and 0 (V(#1) is copied in step 0)
+    {
+      const PartCopyF k0 = k_copy(0, cur), k1 = k_copy(1, nxt), v0 = v_copy(0, cur);
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        k0.row(it, wave, ln.ldk[it & 3]);
+        k1.row(it, wave, ln.ldk[it & 3]);
+        v0.row(it, wave, ln.ldv[it & 1]);
+      }
+      if (seg) {
+        k0.ids(wave, lane);
+        k1.ids(wave, lane);
+      }
+    }
+    wait_vm0();
+    __syncthreads();
+    f32x16 s_cur = {};
+    {
+      const char* Ks = sm.k[0];
+#pragma unroll
+      for (int c = 0; c < 32; ++c) {
+        const f32x4 a = *(const f32x4*)(Ks + ln.kq[c & 7] + (c >> 3) * 256);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s_cur = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], qf[c][e], s_cur, 0, 0, 0);
+      }
+    }
+    mask_if_needed(s_cur, cur, 0);
+    {
+      float mx = s_cur[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s_cur[r]);
+      lazy_update(mx);  // nothing accumulated yet
+    }
+
+    for (int i = 0; cur < t_hi; ++i) {
+      const int st = i & 1, st1 = st ^ 1;
+      wait_vm0();       // K(nxt) and V(cur), copied last step, have landed
+      __syncthreads();  // ... for every wave; K stage st and V stage st1 are free
+      const int n3 = next_tile(nn);
+      const PartCopyF kc = k_copy(st, nn);   // K(#i+2) into K(#i)'s stage
+      const PartCopyF vc = v_copy(st1, nxt);  // V(#i+1) into V(#i-1)'s stage
+      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+
+      // phase A: S^T(nxt) = K Q^T from K stage st1; the exps of s_cur at every
+      // other chunk; the copies between the chunks
+      float pr[16];
+      float lsum = 0.f;
+      f32x16 s_nxt = {};
+      {
+        const char* Ks = sm.k[st1];
+        f32x4 kf0 = *(const f32x4*)(Ks + ln.kq[0]);
+        f32x4 kf1 = *(const f32x4*)(Ks + ln.kq[1]);
+#pragma unroll
+        for (int c = 0; c < 32; ++c) {
+          const f32x4 a = kf0;
+          kf0 = kf1;
+          if (c + 2 < 32) kf1 = *(const f32x4*)(Ks + ln.kq[(c + 2) & 7] + ((c + 2) >> 3) * 256);
+          asm volatile("" : "+a"(qf[c]));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s_nxt = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], qf[c][e], s_nxt, 0, 0, 0);
+          if ((c & 1) == 0) {
+            const int r = c >> 1;
+            pr[r] = fast_exp2(fmaf(s_cur[r], sl2, -m_use));
+            lsum += pr[r];
+          }
+          if ((c & 3) == 1) kc.row(c >> 2, wave, ln.ldk[(c >> 2) & 3]);
+          if ((c & 3) == 3) vc.row(c >> 2, wave, ln.ldv[(c >> 2) & 1]);
+          if (c == 2 && seg) kc.ids(wave, lane);
+          GQA_SEGMENT_END_F();
+        }
+      }
+      l_part += lsum;
+
+      // phase B: O^T += V^T P^T from V stage st (MFMA tt contracts key
+      // 8 (tt / 4) + 4 g + tt % 4, P register tt; the 8 V values of key step
+      // tt are read one step ahead), with the mask and row max of s_nxt
+      mask_if_needed(s_nxt, nxt, st1);
+      float mx = -INFINITY;
+      {
+        const char* Vs = sm.v[st];
+        float vcur[8], vnxt[8];
+#pragma unroll
+        for (int n = 0; n < 8; ++n) vcur[n] = *(const float*)(Vs + ln.vq[n & 1][0] + n * 128);
+#pragma unroll
+        for (int tt = 0; tt < 16; ++tt) {
+          if (tt + 1 < 16) {
+            const int u = tt + 1;
+#pragma unroll
+            for (int n = 0; n < 8; ++n)
+              vnxt[n] = *(const float*)(Vs + ln.vq[n & 1][u & 3] + (u >> 2) * 8192 + n * 128);
+          }
+#pragma unroll
+          for (int n = 0; n < 8; ++n) acc[n] = __builtin_amdgcn_mfma_f32_32x32x2f32(vcur[n], pr[tt], acc[n], 0, 0, 0);
+          mx = fmaxf(mx, s_nxt[tt]);
+          GQA_SEGMENT_END_F();
+#pragma unroll
+          for (int n = 0; n < 8; ++n) vcur[n] = vnxt[n];
+        }
+      }
+      lazy_update(mx);
+      s_cur = s_nxt;
+      cur = nxt;
+      nxt = nn;
+      nn = n3;
+    }
   }
 
   const float l_tot = xor32_sum(l_part);

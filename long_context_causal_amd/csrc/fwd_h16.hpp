@@ -350,6 +350,15 @@ struct H16Wave {
     return SEG && use_bits && t < n_tiles && ((sm.bits.full[t >> 5] >> (t & 31)) & 1u);
   }
   __device__ __forceinline__ void mask_if_needed(f32x16* s, int t, int st) {
+    if (t >= n_tiles) {
+      // past the range (the last step's "next" tile, or the tile after a key
+      // split): nothing visible; the zeros its copy wrote are no scores
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[j][r] = -INFINITY;
+      return;
+    }
     const int64_t k0 = (int64_t)t * kBkB;
     const bool seg_elem = SEG && !full_bit(t);
     if (seg_elem || k0 + kBkB > p.Lk || (p.causal && k0 + kBkB - 1 > p.q_offset + pw)) {
