@@ -179,14 +179,8 @@ __global__ __launch_bounds__(W * 64) void fwd_f32_kernel(FwdParams p) {
   auto v_copy = [&](int st, int t) {
     return part_copy_f(vbase + (uint32_t)st * kTileBytesF, 0u, vb, nullptr, t, t < t_hi, p.Lk);
   };
-  // S^T of tile t from K stage st (32 chunks x 4 products, K read two chunks ahead)
+  // element mask of tile t's scores (its ids in K stage st), where the tile needs one
   auto mask_if_needed = [&](f32x16& s, int t, int st) {
-    if (t >= t_hi) {
-      // past the range: nothing visible (the zeros its copy wrote are no scores)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = -INFINITY;
-      return;
-    }
     const int64_t k0 = (int64_t)t * kBkF;
     const bool seg_full = !seg || (use_bits && ((sm.bits.full[t >> 5] >> (t & 31)) & 1u));
     if (seg_full && k0 + kBkF <= p.Lk && !(p.causal && k0 + kBkF - 1 > p.q_offset + pw)) return;
@@ -321,7 +315,9 @@ __global__ __launch_bounds__(W * 64) void fwd_f32_kernel(FwdParams p) {
           for (int n = 0; n < 8; ++n) vcur[n] = vnxt[n];
         }
       }
-      lazy_update(mx);
+      // a "next" tile past the range (the last step's, also the tile after a
+      // key split) holds the zeros of its copy, no scores: its max stays -inf
+      lazy_update(nxt < t_hi ? mx : -INFINITY);
       s_cur = s_nxt;
       cur = nxt;
       nxt = nn;

@@ -350,15 +350,6 @@ struct H16Wave {
     return SEG && use_bits && t < n_tiles && ((sm.bits.full[t >> 5] >> (t & 31)) & 1u);
   }
   __device__ __forceinline__ void mask_if_needed(f32x16* s, int t, int st) {
-    if (t >= n_tiles) {
-      // past the range (the last step's "next" tile, or the tile after a key
-      // split): nothing visible; the zeros its copy wrote are no scores
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[j][r] = -INFINITY;
-      return;
-    }
     const int64_t k0 = (int64_t)t * kBkB;
     const bool seg_elem = SEG && !full_bit(t);
     if (seg_elem || k0 + kBkB > p.Lk || (p.causal && k0 + kBkB - 1 > p.q_offset + pw)) {
@@ -391,7 +382,9 @@ struct H16Wave {
         const int r = u - 2;
         mx = fmaxf(mx, fmaxf(s_nxt[0][r], s_nxt[1][r]));
       }
-      if (u == 19) mx = xor32_max(mx);
+      // a "next" tile past the range (the last step's, also the tile after a
+      // key split) holds the zeros of its copy, no scores: its max stays -inf
+      if (u == 19) mx = nxt < n_tiles ? xor32_max(mx) : -INFINITY;
       if (u == 21) alpha = lazy_max_update(mx, rs, sl2);
       GQA_SEGMENT_END();
     }

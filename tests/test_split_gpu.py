@@ -91,3 +91,30 @@ def test_full_size(dtype, Lq, Lk):
     # decode rows over the 64k state (bf16) and one 256-row branch over the 30k prefix (fp32)
     x = synth.gqa(1, 16, 4, Lq, Lk, seed=260, dtype=dtype, q_offset=Lk - Lq)
     check_split(x, "full size Lq=%d Lk=%d %s" % (Lq, Lk, dtype))
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_split_scores_far_below_zero(dtype):
+    """All scores near -2,000, so each row's max is near -167 in log2 units.
+    Every split but the last ends before a key tile that exists; that tile
+    must stay unscored. Scoring the zeros of its copy would lift the running
+    max to 0 and rescale O and l by about 2^-167, which underflows to zero.
+
+    Bars: the fp32 rounding of these score sums is up to 1.2e-3, about 36
+    times that of N(0,1) inputs (sum |q_d k_d| is about 2,000 against about
+    160), so the fp32 bars are scaled by 64. For the 16-bit types the rounding
+    of P dominates the output error; their bars are scaled by 2, for the
+    score rounding that reaches lse."""
+    x0 = synth.gqa(1, 16, 4, 16, 1000, seed=230, causal=False)
+    q = np.abs(x0.q) + np.float32(2.0)
+    k = -(np.abs(x0.k) + np.float32(2.0))
+    x = synth.Inputs(q, k, x0.v, dtype, causal=False)
+    print("case: scores far below zero", dtype, flush=True)
+    qd, kd, vd = to_dev(x)
+    o, lse = gqa.fwd_split(qd, kd, vd, causal=False, n_split=4)
+    o1, l1 = gqa.fwd(qd, kd, vd, causal=False)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attn(x.q, x.k, x.v, causal=False)
+    scale = 64.0 if dtype == "f32" else 2.0
+    compare(o, lse, o_ref, l_ref, dtype, label="far below zero, split 4", tol_scale=scale)
+    compare(o1, l1, o_ref, l_ref, dtype, label="far below zero, unsplit", tol_scale=scale)
