@@ -36,8 +36,9 @@ def dev_inputs(x, torch):
 
 
 def time_calls(fn, steps, warmup, torch):
-    """Wall time per step (host clock around K synchronized steps) and the mean
-    per-call GPU time from HIP events recorded on the launch stream."""
+    """Wall time per step (host clock around K synchronized steps) and the mean,
+    min and max per-call GPU time from HIP events recorded on the launch stream
+    (the median is left in time_calls.last_median)."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -50,6 +51,7 @@ def time_calls(fn, steps, warmup, torch):
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
     ev_ms = [a.elapsed_time(b) for a, b in evs]
+    time_calls.last_median = float(np.median(ev_ms))
     return wall_ms, float(np.mean(ev_ms)), float(np.min(ev_ms)), float(np.max(ev_ms))
 
 
@@ -78,7 +80,8 @@ def run_fwd_workload(name, x, steps, warmup, torch, gqa, work, seg=None):
     del q, k, v, o, lse
     torch.cuda.empty_cache()
     return dict(workload=name, flops=fl, wall_ms=wall_ms, kernel_ms=ev_ms, kernel_ms_min=ev_min,
-                kernel_ms_max=ev_max, tflops=fl / (wall_ms * 1e-3) / 1e12, kernel_tflops=fl / (ev_ms * 1e-3) / 1e12,
+                kernel_ms_max=ev_max, kernel_ms_median=time_calls.last_median, tflops=fl / (wall_ms * 1e-3) / 1e12,
+                kernel_tflops=fl / (ev_ms * 1e-3) / 1e12,
                 peak_gib=peak / 2 ** 30, library_alloc_bytes=int(free0 - free1),
                 bytes=work.hbm_bytes(B, Hq, Hkv_, Lq, Lk, Dh, 4 if x.dtype == "f32" else 2, seg is not None))
 
@@ -113,7 +116,8 @@ def run_bwd_workload(name, x, steps, warmup, torch, gqa, work, synth, seg=None):
     del q, k, v, do, o, lse, dq, dk, dv, delta, sid
     torch.cuda.empty_cache()
     return dict(workload=name, flops=fl, exec_flops=ex, wall_ms=wall_ms, kernel_ms=ev_ms, kernel_ms_min=ev_min,
-                kernel_ms_max=ev_max, tflops=fl / (wall_ms * 1e-3) / 1e12, kernel_tflops=fl / (ev_ms * 1e-3) / 1e12,
+                kernel_ms_max=ev_max, kernel_ms_median=time_calls.last_median, tflops=fl / (wall_ms * 1e-3) / 1e12,
+                kernel_tflops=fl / (ev_ms * 1e-3) / 1e12,
                 exec_tflops=ex / (ev_ms * 1e-3) / 1e12,
                 bytes=work.bwd_hbm_bytes(B, Hq, Hkv_, Lq, Lk, Dh, 4 if x.dtype == "f32" else 2, seg is not None))
 
@@ -145,7 +149,8 @@ def run_split_workload(name, x, steps, warmup, torch, gqa, work):
     del q, k, v, o, lse, ws
     torch.cuda.empty_cache()
     return dict(workload=name, n_split=n_split, flops=fl, wall_ms=wall_ms, kernel_ms=ms_split,
-                kernel_ms_min=ev_min, kernel_ms_max=ev_max, unsplit_ms=ms_plain, speedup=ms_plain / ms_split,
+                kernel_ms_min=ev_min, kernel_ms_max=ev_max, kernel_ms_median=time_calls.last_median,
+                unsplit_ms=ms_plain, speedup=ms_plain / ms_split,
                 tflops=fl / (wall_ms * 1e-3) / 1e12, kernel_tflops=fl / (ms_split * 1e-3) / 1e12,
                 kv_bytes=kv_bytes, kv_gbs=kv_bytes / (ms_split * 1e-3) / 1e9)
 
@@ -184,7 +189,8 @@ def run_branch(steps, warmup, torch, gqa, work, synth):
     del q, kp, vp, ks, vs, o1, o2, l1, l2
     torch.cuda.empty_cache()
     return dict(workload="branch f32 S=30468 n=40 m=256 (prefix call + segmented suffix call + merge)",
-                flops=fl, wall_ms=wall_ms, kernel_ms=ev_ms, tflops=fl / (wall_ms * 1e-3) / 1e12,
+                flops=fl, wall_ms=wall_ms, kernel_ms=ev_ms, kernel_ms_min=ev_min, kernel_ms_max=ev_max,
+                kernel_ms_median=time_calls.last_median, tflops=fl / (wall_ms * 1e-3) / 1e12,
                 kernel_tflops=fl / (ev_ms * 1e-3) / 1e12, peak_gib=peak / 2 ** 30)
 
 
@@ -455,6 +461,8 @@ def main():
         "peak_gib": round(prim["peak_gib"], 3),
         "math_path_gib": round(math_gib, 2),
         "library_alloc_bytes": prim["library_alloc_bytes"],
+        "kernel_ms_stats": {"mean": round(prim["kernel_ms"], 4), "median": round(prim["kernel_ms_median"], 4),
+                            "min": round(prim["kernel_ms_min"], 4), "max": round(prim["kernel_ms_max"], 4)},
         "roofline": {"bound": "mfma", "achieved": round(prim["kernel_tflops"], 3), "peak": peak_t,
                      "unit": "TFLOP/s", "frac": round(prim["kernel_tflops"] / peak_t, 4),
                      "traffic": stored_traffic(name), "kernel_ms": round(prim["kernel_ms"], 4),
