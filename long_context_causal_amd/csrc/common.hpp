@@ -114,24 +114,9 @@ __device__ __forceinline__ int wave_max_i(int x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Async global -> LDS copies (global_load_lds): lane l's 16 (or 4) bytes from
-// gbase + voff land at LDS byte lds + 16 l (or 4 l); gbase and lds must be the
-// same in every lane of the wave. They are issued through inline asm on
-// purpose: the compiler then does not treat them as LDS stores whose
-// completion every later LDS read must wait for, which would serialise the
-// prefetch ring. Completion is ensured by the explicit s_waitcnt vmcnt waits
-// and workgroup barriers of the kernels. The instruction writes no VGPR;
-// M0 (the LDS base) is set in the same asm block, one wait state ahead.
+// LDS byte address of a __shared__ object.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
-}
-__device__ __forceinline__ void g2lds16(const char* gbase, uint32_t voff, const void* lds) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :: "s"(lds_addr(lds)), "v"(voff), "s"(gbase) : "memory");
-}
-__device__ __forceinline__ void g2lds4(const char* gbase, uint32_t voff, const void* lds) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
-               :: "s"(lds_addr(lds)), "v"(voff), "s"(gbase) : "memory");
 }
 __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 // The same wait as a builtin, which the compiler's own wait insertion sees: after
@@ -142,11 +127,19 @@ __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" :
 // expcnt 7, lgkmcnt 15.)
 __device__ __forceinline__ void wait_vm0_known() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// The same async copy through a buffer resource (MUBUF with the LDS bit): the
-// resource bounds the read, and lanes whose offset falls at or past its size
-// read zeros, so a tile that runs past the end of a tensor needs no clamping.
-// Resource words: 48-bit base address (stride 0), size in bytes, and the
-// format word of a raw 32-bit buffer on this family.
+// Async global -> LDS copies through a buffer resource (MUBUF with the LDS
+// bit): lane l's 16 (or 4) bytes from the resource base + voff land at LDS
+// byte lds + 16 l (or 4 l); the resource and lds must be the same in every
+// lane of the wave. The resource bounds the read, and lanes whose offset falls
+// at or past its size read zeros, so a tile that runs past the end of a tensor
+// needs no clamping. Resource words: 48-bit base address (stride 0), size in
+// bytes, and the format word of a raw 32-bit buffer on this family.
+// The copies are issued through inline asm on purpose: the compiler then does
+// not treat them as LDS stores whose completion every later LDS read must wait
+// for, which would serialise the prefetch ring. Completion is ensured by the
+// explicit s_waitcnt vmcnt waits and workgroup barriers of the kernels. The
+// instruction writes no VGPR; M0 (the LDS base) is set in the same asm block,
+// one wait state ahead.
 typedef __attribute__((ext_vector_type(4))) int rsrc_t;
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   const uint64_t a = (uint64_t)(uintptr_t)base;
@@ -163,13 +156,6 @@ __device__ __forceinline__ rsrc_t uniform_rsrc(rsrc_t r) {
 __device__ __forceinline__ void buf2lds16(rsrc_t rsrc, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc) : "memory");
-}
-// The same copy without a memory clobber, for copies into a stage that no
-// code reads before the next explicit wait and barrier (those carry the
-// clobber and order the LDS accesses).
-__device__ __forceinline__ void buf2lds16_nc(rsrc_t rsrc, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc));
 }
 __device__ __forceinline__ void buf2lds4(rsrc_t rsrc, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
