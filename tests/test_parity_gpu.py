@@ -10,7 +10,7 @@ import torch
 import long_context_causal_amd as gqa
 import oracle
 import synth
-from gpu_util import TOL_O, compare, dev_tensor, run, seg_dev, to_dev
+from gpu_util import DEV, TOL_LSE, TOL_O, compare, dev_tensor, run, seg_dev, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -89,6 +89,31 @@ def test_unsorted_segments_and_empty_rows(dtype):
         x = synth.gqa(2, 16, 4, L, seed=14, dtype=dtype, causal=causal)
         x.seg_q, x.seg_k = sq, sk
         check(x, "random segments %s causal=%s" % (dtype, causal))
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("causal", [True, False])
+def test_packed_segments_equal_per_segment_calls(dtype, causal):
+    """Packed segments with ids give, row for row, what each segment gives as
+    a call of its own (B = 1, Lq = Lk = its length, no ids). The segments
+    start off the 64-key tile grid, so the sums run in another order: equal
+    within the forward's bars, not bitwise."""
+    L = 2000
+    lens = synth.segment_lengths(L, 100, 700, seed=16)
+    bounds = synth.segment_bounds(lens)
+    ids = torch.from_numpy(synth.segment_ids(lens)[None]).to(DEV)
+    x = synth.gqa(1, 16, 4, L, seed=17, dtype=dtype, causal=causal)
+    q, k, v = to_dev(x)
+    o, lse = gqa.fwd(q, k, v, causal=causal, seg_q=ids, seg_k=ids)
+    print("case: packed vs per-segment %s causal=%s, %d segments" % (dtype, causal, len(lens)), flush=True)
+    for a, b in bounds:
+        sl = slice(a, b)
+        o_s, l_s = gqa.fwd(q[:, :, sl].contiguous(), k[:, :, sl].contiguous(), v[:, :, sl].contiguous(),
+                           causal=causal)
+        torch.cuda.synchronize()
+        do = float((o[:, :, sl].float() - o_s.float()).abs().max())
+        dl = float((lse[:, :, sl] - l_s).abs().max())
+        assert do <= TOL_O[dtype] and dl <= TOL_LSE, "segment [%d, %d): |do| %.3g |dlse| %.3g" % (a, b, do, dl)
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
