@@ -194,6 +194,47 @@ def run_branch(steps, warmup, torch, gqa, work, synth):
                 kernel_tflops=fl / (ev_ms * 1e-3) / 1e12, peak_gib=peak / 2 ** 30)
 
 
+def zigzag_chunks(L, n_ranks):
+    """Rank r's row ranges of a zig-zag context-parallel split: chunks r and
+    2N - 1 - r of 2N near-equal chunks (the same rule as tests/test_shard_gpu.py)."""
+    edges = [(L * i) // (2 * n_ranks) for i in range(2 * n_ranks + 1)]
+    return [[(edges[r], edges[r + 1]), (edges[2 * n_ranks - 1 - r], edges[2 * n_ranks - r])] for r in range(n_ranks)]
+
+
+def run_shards(x, whole_ms, rank_counts, steps, warmup, torch, gqa):
+    """Context-parallel shards of the causal forward, run one after another on
+    one GPU: for N ranks (zig-zag rows), rank r's work is two calls (rows
+    [a, b), keys [0, b), q_offset = a). Reported per N: each rank's kernel time
+    (HIP events), the largest (an N-GPU run's compute time, transfers left out),
+    its ratio to the mean (load balance) and to the whole call (speed-up over one
+    GPU, transfers left out)."""
+    q, k, v = dev_inputs(x, torch)
+    L = q.shape[2]
+    out = []
+    for n in rank_counts:
+        ranks = zigzag_chunks(L, n)
+        per_rank = []
+        for rng in ranks:
+            parts = []
+            for a, b in rng:
+                parts.append((q[:, :, a:b].contiguous(), k[:, :, :b].contiguous(), v[:, :, :b].contiguous(), a))
+            fn = lambda parts=parts: [gqa.fwd(qq, kk, vv, q_offset=a) for qq, kk, vv, a in parts]
+            fn()
+            torch.cuda.synchronize()
+            _, ms, _, _ = time_calls(fn, steps, warmup, torch)
+            per_rank.append(ms)
+            del parts
+            torch.cuda.empty_cache()
+        mx, mean = max(per_rank), sum(per_rank) / len(per_rank)
+        out.append({"ranks": n, "rank_kernel_ms": [round(t, 3) for t in per_rank], "max_rank_ms": round(mx, 3),
+                    "max_over_mean": round(mx / mean, 4), "sum_over_whole": round(sum(per_rank) / whole_ms, 4),
+                    "speedup_over_one_gpu": round(whole_ms / mx, 3)})
+    del q, k, v
+    torch.cuda.empty_cache()
+    return {"workload": "context-parallel shards, causal GQA fwd fp32 L=%d, zig-zag rows, one GPU in turn" % L,
+            "whole_call_ms": round(whole_ms, 3), "splits": out}
+
+
 def cpu_baseline(x, target_s=15.0):
     """The oracle (fp64, OpenMP over rows) on a bounded sample of query rows of
     the same workload, all heads; rows spread evenly over the sequence."""
@@ -332,7 +373,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only", default=None,
                     help="run one workload: f32-15231, f32-30468, f32-60926, bf16-60926, f16-60926, "
-                         "bwd-f32-30468, bwd-bf16-60926, split-decode-bf16, split-branch-f32")
+                         "bwd-f32-30468, bwd-bf16-60926, split-decode-bf16, split-branch-f32, cp-f32-30468")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (3 times) to calibrate HBM byte counters")
     ap.add_argument("--pmc-report", nargs=4, metavar=("FETCH_DB", "WRITE_DB", "KERNEL_SUBSTR", "WORKLOAD"),
@@ -385,6 +426,13 @@ def main():
         xs = synth.gqa(1, HQ, HKV, Lq_, Lk_, seed=0, dtype=dts, q_offset=Lk_ - Lq_)
         print(json.dumps(run_split_workload(nm, xs, args.steps, args.warmup, torch, gqa, work)), flush=True)
         return
+    if args.only == "cp-f32-30468":
+        # a profiling aid: the context-parallel shards alone, beside the whole call
+        xs = synth.gqa(1, HQ, HKV, 30468, seed=0, dtype="f32")
+        whole = run_fwd_workload(workloads["f32-30468"][0], xs, args.steps, args.warmup, torch, gqa, work)
+        print(json.dumps(run_shards(xs, whole["kernel_ms"], (2, 4, 8), args.steps, args.warmup, torch, gqa)),
+              flush=True)
+        return
     if args.only in bwd_workloads:
         # a profiling aid: the backward alone, its record on one line
         nm, Ls, dts = bwd_workloads[args.only]
@@ -401,6 +449,7 @@ def main():
     peak_t = work.PEAK_TFLOPS[dt]
 
     secondary = []
+    shards = None
     if not args.quick and args.only is None:
         for key in ("f32-15231", "f32-60926", "bf16-60926", "f16-60926"):
             nm, Ls, dts = workloads[key]
@@ -435,6 +484,8 @@ def main():
                              work, synth, seg=ids)
         secondary.append(r)
         del xs
+        # context-parallel shards of the headline workload, N = 2, 4, 8 ranks
+        shards = run_shards(x, prim["kernel_ms"], (2, 4, 8), 3, 1, torch, gqa)
     for r in [prim] + secondary:
         dts = "bf16" if "bf16" in r["workload"] else "f16" if "fp16" in r["workload"] else "f32"
         r["pct_mfma_peak"] = 100.0 * r["kernel_tflops"] / work.PEAK_TFLOPS[dts]
@@ -470,6 +521,8 @@ def main():
     }
     if secondary:
         out["secondary"] = [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()} for r in secondary]
+    if shards is not None:
+        out["context_parallel_shards"] = shards
     if args.copy_probe:
         n = 1 << 28  # 2^28 fp32 = 1 GiB read + 1 GiB written per copy
         src = torch.ones(n, dtype=torch.float32, device="cuda:0")
