@@ -182,6 +182,9 @@ def merge(o1, lse1, o2, lse2, *, out=None, out_lse=None, stream=None):
     dt = _dtype_code(o1)
     out = torch.empty_like(o1) if out is None else out
     out_lse = torch.empty_like(lse1) if out_lse is None else out_lse
+    if out.shape != o1.shape or out.dtype != o1.dtype or out_lse.shape != lse1.shape or \
+            out_lse.dtype != torch.float32:
+        raise ValueError("out must match o1 and out_lse must match lse1 (float32)")
     rc = merge_raw(o1.data_ptr(), lse1.data_ptr(), o2.data_ptr(), lse2.data_ptr(), out.data_ptr(),
                    out_lse.data_ptr(), lse1.numel(), o1.shape[-1], dt, _stream_ptr(stream))
     if rc != 0:
@@ -247,10 +250,15 @@ def fwd_split(q, k, v, *, causal=True, q_offset=0, seg_q=None, seg_k=None, n_spl
         raise TypeError("q, k and v must share a dtype")
     B, Hq, Lq, D = q.shape
     Hkv, Lk = k.shape[1], k.shape[2]
+    if k.shape[0] != B or k.shape[3] != D:
+        raise ValueError("q and k/v disagree in batch or head size")
     if (seg_q is None) != (seg_k is None):
         raise ValueError("give both segment-id tensors or neither")
-    if seg_q is not None and (seg_q.dtype != torch.int32 or seg_k.dtype != torch.int32):
-        raise TypeError("segment ids must be int32")
+    if seg_q is not None:
+        if seg_q.dtype != torch.int32 or seg_k.dtype != torch.int32:
+            raise TypeError("segment ids must be int32")
+        if seg_q.numel() != B * Lq or seg_k.numel() != B * Lk:
+            raise ValueError("segment ids must be [B,Lq] and [B,Lk]")
     dt = _dtype_code(q)
     if n_split is None:
         n_split = split_count(B, Hq, Hkv, Lq, Lk, dt)

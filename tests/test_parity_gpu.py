@@ -223,3 +223,23 @@ def test_stream_argument_is_honoured():
         out = gqa.fwd(q, k, v)
     s.synchronize()
     assert torch.equal(ref[0], out[0]) and torch.equal(ref[1], out[1])
+
+
+def test_binding_rejects_mismatched_buffers():
+    """The Python binding checks what the C interface cannot see: output
+    buffers of the wrong shape or type, and mismatched segment ids, raise before
+    any launch."""
+    x = synth.gqa(1, 16, 4, 64, seed=18)
+    q, k, v = to_dev(x)
+    o, lse = gqa.fwd(q, k, v)
+    with pytest.raises(ValueError):
+        gqa.merge(o, lse, o, lse, out=torch.empty_like(o)[:, :, :32])
+    with pytest.raises(ValueError):
+        gqa.merge(o, lse, o, lse, out_lse=torch.empty(1, 16, 63, device=DEV))
+    with pytest.raises(ValueError):
+        gqa.fwd(q, k, v, out=torch.empty(1, 16, 64, 256, dtype=torch.bfloat16, device=DEV))
+    ids = torch.zeros((1, 64), dtype=torch.int32, device=DEV)
+    with pytest.raises(ValueError):
+        gqa.fwd_split(q, k, v, seg_q=ids, seg_k=ids[:, :32].contiguous())
+    with pytest.raises(ValueError):
+        gqa.fwd_split(q, k[:, :, :, :128].contiguous(), v[:, :, :, :128].contiguous())
