@@ -52,6 +52,16 @@ def test_batch_two_and_lq_ne_lk_noncausal(dtype):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("Lq,Lk,q_offset", [(700, 300, 0), (300, 700, 0), (200, 150, 40)])
+def test_causal_lq_ne_lk(dtype, Lq, Lk, q_offset):
+    """Causal with Lq != Lk: rows whose limit q_offset + i reaches past the
+    last key see every key (Lq > Lk), and with Lq < Lk the keys past the last
+    row's limit are unseen by every row."""
+    x = synth.gqa(1, 16, 4, Lq, Lk, seed=Lq + Lk + q_offset, dtype=dtype, q_offset=q_offset)
+    check(x, "causal Lq%d Lk%d off%d %s" % (Lq, Lk, q_offset, dtype))
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
 def test_branch_offset(dtype):
     # one branch: m = 256 rows at positions S.. over S + m keys
     S, m = 1000, 256
