@@ -122,19 +122,23 @@ struct PartCopy {
   uint32_t lds;    // LDS stage
   uint32_t s_lds;  // LDS stage of the ids
   __device__ __forceinline__ void rows(const uint32_t* ld, int it, int wave) const {
-    buf2lds16(r, ld[it], lds + (uint32_t)(kCopiesB * wave + it) * 1024u);
+    buf2lds16_imm(r, ld[it], lds + (uint32_t)(kCopiesB * wave) * 1024u, (uint32_t)it * 1024u);
   }
   __device__ __forceinline__ void ids(int wave, int lane) const {
     if (wave == kWavesB - 1) buf2lds4(rs, (uint32_t)lane * 4u, s_lds);  // uniform branch; 64 ids
   }
 };
 
+// Key counts in 32 bits: Lk < 2^31 (the entry point checks it), and a valid
+// tile starts below Lk. The tile's byte offset needs 64 bits.
 __device__ __forceinline__ PartCopy part_copy(uint32_t lds, uint32_t s_lds, const char* base, const int32_t* skb,
-                                              int64_t t, bool valid, int64_t Lk) {
-  const int64_t keys = valid ? min((int64_t)kBkB, Lk - t * kBkB) : 0;
+                                              int t, bool valid, int64_t Lk) {
+  const uint32_t rem = (uint32_t)Lk - (uint32_t)t * (uint32_t)kBkB;
+  const uint32_t keys = valid ? min(rem, (uint32_t)kBkB) : 0u;
+  const uint64_t tv = valid ? (uint64_t)(uint32_t)t : 0u;
   PartCopy c;
-  c.r = make_rsrc(base + (valid ? t * kTileBytesB : 0), (uint32_t)keys * (kD * 2));
-  c.rs = make_rsrc(skb != nullptr ? skb + (valid ? t * kBkB : 0) : nullptr, skb != nullptr ? (uint32_t)keys * 4u : 0u);
+  c.r = make_rsrc(base + tv * kTileBytesB, keys * (kD * 2));
+  c.rs = make_rsrc(skb != nullptr ? skb + tv * kBkB : nullptr, skb != nullptr ? keys * 4u : 0u);
   c.lds = lds;
   c.s_lds = s_lds;
   return c;
@@ -207,14 +211,15 @@ __device__ __forceinline__ float softmax_max(const f32x16* s, RowState& rs, floa
 // exp of score e - 1 taken and score e - 2 summed (and paired and rounded), so
 // no VALU instruction waits on the result of the one before it (the wave
 // issues in order, and an exp result takes several cycles); slots 32 and 33
-// drain the pipeline. Score e is s[e / 16][e % 16]; P pair f / 2 goes to pk,
-// and key quarter h of the PV product takes pk[4 h .. 4 h + 3].
+// drain the pipeline. Score e is s[e] (s[16 j + r] is element r of key half
+// j); P pair f / 2 goes to pk, and key quarter h of the PV product takes
+// pk[4 h .. 4 h + 3].
 template <typename E>
 struct ExpPipe {
   float t[32], x[32];
   float lsum = 0.f, lrsum = 0.f;
-  __device__ __forceinline__ void slot(int e, const f32x16* s, float sl2, float m_use, unsigned* pk) {
-    if (e < 32) t[e] = fmaf(s[e >> 4][e & 15], sl2, -m_use);
+  __device__ __forceinline__ void slot(int e, const float* s, float sl2, float m_use, unsigned* pk) {
+    if (e < 32) t[e] = fmaf(s[e], sl2, -m_use);
     if (e >= 1 && e <= 32) x[e - 1] = fast_exp2(t[e - 1]);
     if (e >= 2) {
       const int f = e - 2;
@@ -246,10 +251,11 @@ __device__ __forceinline__ V8 k_frag(int q, lds_cchar* const* kb) {
 // D = 256, two key halves) with slots 0..31 of the current tile's exps, the
 // tile copies (K and ids of the tile two ahead, V of the tile one ahead: early
 // enough that they land before the next barrier), and the first V fragments
-// of phase B (already resident).
+// of phase B (already resident). Q stays in AGPRs, where the products read it
+// (the empty asm pins it there; the VGPRs go to the scores, P and fragments).
 template <typename E>
-__device__ __forceinline__ void phase_a(int kst, const typename Elem<E>::v8* qf, const LanesB& ln, f32x16* s_nxt,
-                                        const f32x16* s_cur, float sl2, float m_use, unsigned* pk, ExpPipe<E>& ep,
+__device__ __forceinline__ void phase_a(int kst, typename Elem<E>::v8* qf, const LanesB& ln, f32x16* s_nxt,
+                                        const float* s_cur, float sl2, float m_use, unsigned* pk, ExpPipe<E>& ep,
                                         const PartCopy& kc, const PartCopy& vc, bool seg, int wave, int lane,
                                         lds_cchar* const* vb, typename Elem<E>::v8* vf) {
   typedef typename Elem<E>::v8 V8;
@@ -262,6 +268,7 @@ __device__ __forceinline__ void phase_a(int kst, const typename Elem<E>::v8* qf,
 #pragma unroll
   for (int q = 0; q < 32; ++q) {
     const int j = q & 1, c = q >> 1;
+    if (j == 0) asm volatile("" : "+a"(qf[c]));
     s_nxt[j] = Elem<E>::mfma(kf[q % 3], qf[c], c == 0 ? f32x16{} : s_nxt[j]);
     if (q + 3 < 32) kf[q % 3] = k_frag<V8>(q + 3, kb);
     ep.slot(q, s_cur, sl2, m_use, pk);
@@ -322,7 +329,7 @@ struct H16Wave {
   RingBase rb;
   V8 qf[16];
   f32x16 acc[8];
-  f32x16 s_cur[2];
+  float s_cur[32];  // scores of the tile being finished, in VGPRs (see phase_b)
   RowState rs;
   const char* kb;
   const char* vb;
@@ -365,8 +372,11 @@ struct H16Wave {
   // products ahead) with the last exp slots of this tile, the row max of the
   // next scores s_nxt (masked first where needed; ids in K stage kst1) spread
   // over the products, and the lazy update of the running max. Returns alpha.
+  // The max pass is the one read of the scores from the products' AGPRs: the
+  // values it reads are pinned in VGPRs and returned in sn, and the next
+  // step's exps take them from there.
   __device__ __forceinline__ float phase_b(int kst1, f32x16* s_nxt, unsigned* pk, ExpPipe<E>& ep,
-                                           lds_cchar* const* vbs, V8* vf) {
+                                           lds_cchar* const* vbs, V8* vf, float* sn) {
     const float sl2 = p.scale_log2;
     const float m_cur = rs.m_use;
     mask_if_needed(s_nxt, nxt, kst1);
@@ -380,7 +390,11 @@ struct H16Wave {
       if (u < 2) ep.slot(32 + u, s_cur, sl2, m_cur, pk);
       if (u >= 2 && u < 18) {
         const int r = u - 2;
-        mx = fmaxf(mx, fmaxf(s_nxt[0][r], s_nxt[1][r]));
+        float a0 = s_nxt[0][r], a1 = s_nxt[1][r];
+        asm volatile("" : "+v"(a0), "+v"(a1));
+        sn[r] = a0;
+        sn[16 + r] = a1;
+        mx = fmaxf(fmaxf(mx, a0), a1);
       }
       // a "next" tile past the range (the last step's, also the tile after a
       // key split) holds the zeros of its copy, no scores: its max stays -inf
@@ -413,10 +427,11 @@ struct H16Wave {
     for (int j = 0; j < 4; ++j) vbs[j] = ln.v[j] + st * kTileBytesB;
     V8 vf[kVPre];
     phase_a<E>(st1, qf, ln, s_nxt, s_cur, p.scale_log2, rs.m_use, pk, ep, kc, vc, SEG, wave, lane, vbs, vf);
-    const float alpha = phase_b(st1, s_nxt, pk, ep, vbs, vf);
+    float sn[32];
+    const float alpha = phase_b(st1, s_nxt, pk, ep, vbs, vf, sn);
     rescale(acc, rs, alpha);
-    s_cur[0] = s_nxt[0];
-    s_cur[1] = s_nxt[1];
+#pragma unroll
+    for (int r = 0; r < 32; ++r) s_cur[r] = sn[r];
     cur = nxt;
     nxt = nn;
     nn = n3;
@@ -462,7 +477,10 @@ __global__ __launch_bounds__(kWavesB * 64) void fwd_h16_kernel(FwdParams p) {
   {
     const V8* qr = (const V8*)((const char*)p.q + (hq + row_c) * kD * 2);
 #pragma unroll
-    for (int c = 0; c < 16; ++c) wv.qf[c] = qr[2 * c + wv.g];
+    for (int c = 0; c < 16; ++c) {
+      wv.qf[c] = qr[2 * c + wv.g];
+      asm volatile("" : "+a"(wv.qf[c]));
+    }
   }
 #pragma unroll
   for (int n = 0; n < 8; ++n) {
@@ -491,9 +509,18 @@ __global__ __launch_bounds__(kWavesB * 64) void fwd_h16_kernel(FwdParams p) {
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    qk_only<E>(0, wv.qf, wv.ln, wv.s_cur);
-    wv.mask_if_needed(wv.s_cur, wv.cur, 0);
-    (void)softmax_max(wv.s_cur, wv.rs, p.scale_log2);  // nothing accumulated yet: no rescale
+    f32x16 s0[2];
+    qk_only<E>(0, wv.qf, wv.ln, s0);
+    wv.mask_if_needed(s0, wv.cur, 0);
+    (void)softmax_max(s0, wv.rs, p.scale_log2);  // nothing accumulated yet: no rescale
+    // into VGPRs, as phase_b leaves the scores of every later tile (a
+    // loop-carried value that enters in AGPRs would go round them each step)
+#pragma unroll
+    for (int r = 0; r < 32; ++r) {
+      float a = s0[r >> 4][r & 15];
+      asm volatile("" : "+v"(a));
+      wv.s_cur[r] = a;
+    }
     for (int i = 0; wv.cur < wv.n_tiles; ++i) wv.step(i);
   }
 
