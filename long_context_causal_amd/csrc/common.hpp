@@ -159,10 +159,13 @@ __device__ __forceinline__ void buf2lds16(rsrc_t rsrc, uint32_t voff, uint32_t l
 }
 // The same with the LDS address lds + imm, imm a constant once the caller is
 // inlined and unrolled: the add writes M0 directly (one scalar instruction
-// per copy instead of an add and a move).
+// per copy instead of an add and a move). The add also sets SCC (its carry),
+// hence the clobber: without it the compiler may keep a carry live across the
+// block, between the two halves of a 64-bit address add, and the high half
+// then loses it.
 __device__ __forceinline__ void buf2lds16_imm(rsrc_t rsrc, uint32_t voff, uint32_t lds, uint32_t imm) {
   asm volatile("s_add_u32 m0, %0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc), "i"(imm) : "memory");
+               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc), "i"(imm) : "memory", "scc");
 }
 __device__ __forceinline__ void buf2lds4(rsrc_t rsrc, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"

@@ -167,7 +167,7 @@ struct RowState {
 
 // Element mask of one 32-key half of a tile: lane holds keys key0 + 8 j + 4 g + i
 // (s[4 j + i]) of row `row`; segk_lane points at the half's key ids + 4 g.
-__device__ __forceinline__ void mask_half(f32x16& s, int64_t key0, int g, int64_t Lk, int causal, int64_t lim,
+__device__ __forceinline__ void mask_half(float* s, int64_t key0, int g, int64_t Lk, int causal, int64_t lim,
                                           bool seg_elem, lds_cchar* segk_lane, int sq) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -198,12 +198,13 @@ __device__ __forceinline__ float lazy_max_update(float mx, RowState& rs, float s
   return alpha;
 }
 
-// Row max of a tile (both halves; the lanes l and l ^ 32 share a row) and the lazy update.
-__device__ __forceinline__ float softmax_max(const f32x16* s, RowState& rs, float sl2) {
-  float mx = fmaxf(s[0][0], s[1][0]);
+// Max of a tile's 32 scores in this lane (the lanes l and l ^ 32 share a row:
+// the row max is xor32_max of it).
+__device__ __forceinline__ float lane_max(const float* s) {
+  float mx = -INFINITY;
 #pragma unroll
-  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
-  return lazy_max_update(xor32_max(mx), rs, sl2);
+  for (int r = 0; r < 16; ++r) mx = fmaxf(fmaxf(mx, s[r]), s[16 + r]);
+  return mx;
 }
 
 // The exps of one tile (32 scores per lane), software-pipelined over the
@@ -356,33 +357,38 @@ struct H16Wave {
   __device__ __forceinline__ bool full_bit(int t) const {
     return SEG && use_bits && t < n_tiles && ((sm.bits.full[t >> 5] >> (t & 31)) & 1u);
   }
-  __device__ __forceinline__ void mask_if_needed(f32x16* s, int t, int st) {
+  // Masks the 32 scores per lane of tile t (s[16 j + r]: element r of key
+  // half j) where some key of the tile is hidden from some row of the wave;
+  // returns whether it did.
+  __device__ __forceinline__ bool mask_if_needed(float* s, int t, int st) {
     const int64_t k0 = (int64_t)t * kBkB;
     const bool seg_elem = SEG && !full_bit(t);
     if (seg_elem || k0 + kBkB > p.Lk || (p.causal && k0 + kBkB - 1 > p.q_offset + pw)) {
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        mask_half(s[j], k0 + 32 * j, g, p.Lk, p.causal, lim, seg_elem,
+        mask_half(s + 16 * j, k0 + 32 * j, g, p.Lk, p.causal, lim, seg_elem,
                   (lds_cchar*)sm.segk[st] + 128 * j + 16 * g, sq);
+      return true;
     }
+    return false;
   }
 
   // Phase B: O^T += V^T P^T for the tile whose V fragments vf[] start in
   // flight (32 MFMAs: 4 key quarters x 8 d blocks, fragments read kVPre
   // products ahead) with the last exp slots of this tile, the row max of the
-  // next scores s_nxt (masked first where needed; ids in K stage kst1) spread
-  // over the products, and the lazy update of the running max. Returns alpha.
-  // The max pass is the one read of the scores from the products' AGPRs: the
-  // values it reads are pinned in VGPRs and returned in sn, and the next
-  // step's exps take them from there.
-  __device__ __forceinline__ float phase_b(int kst1, f32x16* s_nxt, unsigned* pk, ExpPipe<E>& ep,
+  // next scores s_nxt spread over the products, and the lazy update of the
+  // running max. Returns alpha. The max pass is the one read of the scores
+  // from the products' AGPRs: two per product, pinned in VGPRs and returned
+  // in sn (the next step's exps take them from there). Where the tile needs a
+  // mask (ids in K stage kst1), it applies to those VGPR copies and the lane
+  // max is taken again: masking the AGPRs first would put all 32 reads in one
+  // run at the start of the phase, the products starved behind them.
+  __device__ __forceinline__ float phase_b(int kst1, const f32x16* s_nxt, unsigned* pk, ExpPipe<E>& ep,
                                            lds_cchar* const* vbs, V8* vf, float* sn) {
     const float sl2 = p.scale_log2;
     const float m_cur = rs.m_use;
-    mask_if_needed(s_nxt, nxt, kst1);
     float mx = -INFINITY, alpha = 1.f;
-#pragma unroll
-    for (int u = 0; u < 32; ++u) {
+    auto product = [&](int u) {
       const int n = u & 7, h = u >> 3;
       const V8 ph = __builtin_bit_cast(V8, u32x4{pk[4 * h], pk[4 * h + 1], pk[4 * h + 2], pk[4 * h + 3]});
       acc[n] = Elem<E>::mfma(vf[u % kVPre], ph, acc[n]);
@@ -401,7 +407,15 @@ struct H16Wave {
       if (u == 19) mx = nxt < n_tiles ? xor32_max(mx) : -INFINITY;
       if (u == 21) alpha = lazy_max_update(mx, rs, sl2);
       GQA_SEGMENT_END();
-    }
+    };
+    // the mask sits between two unrolled loops, not inside one: inside, its
+    // code (the segment-id form is large) counts in every iteration before
+    // u == 18 is folded, and the loop would stay rolled
+#pragma unroll
+    for (int u = 0; u < 19; ++u) product(u);
+    if (mask_if_needed(sn, nxt, kst1)) mx = lane_max(sn);
+#pragma unroll
+    for (int u = 19; u < 32; ++u) product(u);
     rs.l += ep.lsum;
     rs.lr += ep.lrsum;
     return alpha;
@@ -511,16 +525,18 @@ __global__ __launch_bounds__(kWavesB * 64) void fwd_h16_kernel(FwdParams p) {
     __syncthreads();
     f32x16 s0[2];
     qk_only<E>(0, wv.qf, wv.ln, s0);
-    wv.mask_if_needed(s0, wv.cur, 0);
-    (void)softmax_max(s0, wv.rs, p.scale_log2);  // nothing accumulated yet: no rescale
     // into VGPRs, as phase_b leaves the scores of every later tile (a
     // loop-carried value that enters in AGPRs would go round them each step)
+    float sc[32];
 #pragma unroll
     for (int r = 0; r < 32; ++r) {
-      float a = s0[r >> 4][r & 15];
-      asm volatile("" : "+v"(a));
-      wv.s_cur[r] = a;
+      sc[r] = s0[r >> 4][r & 15];
+      asm volatile("" : "+v"(sc[r]));
     }
+    wv.mask_if_needed(sc, wv.cur, 0);
+    (void)lazy_max_update(xor32_max(lane_max(sc)), wv.rs, p.scale_log2);  // nothing accumulated yet: no rescale
+#pragma unroll
+    for (int r = 0; r < 32; ++r) wv.s_cur[r] = sc[r];
     for (int i = 0; wv.cur < wv.n_tiles; ++i) wv.step(i);
   }
 
