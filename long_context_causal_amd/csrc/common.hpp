@@ -167,8 +167,14 @@ __device__ __forceinline__ void buf2lds16_imm(rsrc_t rsrc, uint32_t voff, uint32
   asm volatile("s_add_u32 m0, %0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc), "i"(imm) : "memory", "scc");
 }
+// The 4-byte copy takes its resource words through readfirstlane, a VALU
+// write of SGPRs that a vector-memory read of them must trail by 5 wait
+// states; the compiler inserts those only before loads it can see, so the
+// block brings its own (the M0 move and s_nop 3). The 16-byte copies pass
+// their resource as it is; tests/test_asm_hazards.py checks the compiled
+// kernels for a VALU-written SGPR within 5 wait states of any copy.
 __device__ __forceinline__ void buf2lds4(rsrc_t rsrc, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 3\n\tbuffer_load_dword %1, %2, 0 offen lds"
                :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(uniform_rsrc(rsrc)) : "memory");
 }
 
