@@ -273,18 +273,32 @@ __global__ __launch_bounds__(kWavesH * 64) void bwd_dq_h16_kernel(BwdParams bp) 
             if (seg_elem) id4[gn & 1] = *(const i32x4b*)(&sm.segk[st][32 * (gn >> 2) + 8 * (gn & 3) + 4 * g]);
           }
           const int rk = 32 * je + 8 * (re >> 2) + 4 * g + (re & 3);
-          const float x = fast_exp2(fmaf(s[je][re], sl2, -lse2));
+          float sv = s[je][re];
+          asm volatile("" : "+v"(sv));  // the score's VGPR copy, taken at its slot
+          const float x = fast_exp2(fmaf(sv, sl2, -lse2));
           pv[e] = (rk < kl && id4[grp & 1][re & 3] == sq) ? x : 0.f;
         }
         if ((c & 1) == 1) cv.block(8 * wave + (c >> 1), lane);
         __builtin_amdgcn_sched_barrier(0);
       }
+      // S keeps AGPRs of its own through the loop (dP's products do not
+      // reuse them)
+      asm volatile("" ::"a"(s[0]), "a"(s[1]));
     }
-    // dS^T = P^T (dP^T - delta), packed in pairs; key quarter h in dsk[4 h ..]
+    // dS^T = P^T (dP^T - delta), packed in pairs; key quarter h in dsk[4 h ..].
+    // Quarter 0 before the dQ products; quarters 1-3 beside the products of
+    // the quarter before (one pair every other product), each pair's dP read
+    // out of the AGPRs at its slot. Formed all at once, the 32 reads and the
+    // VALU work left the matrix core idle before the first dQ product.
     unsigned dsk[16];
+    auto ds_pair = [&](int f) {  // pair f: scores 2 f and 2 f + 1
+      const int e = 2 * f;
+      float d0 = dp[e >> 4][e & 15], d1 = dp[e >> 4][(e + 1) & 15];
+      asm volatile("" : "+v"(d0), "+v"(d1));
+      dsk[f] = Elem<E>::pack(pv[e] * (d0 - delta), pv[e + 1] * (d1 - delta));
+    };
 #pragma unroll
-    for (int e = 0; e < 32; e += 2)
-      dsk[e >> 1] = Elem<E>::pack(pv[e] * (dp[e >> 4][e & 15] - delta), pv[e + 1] * (dp[e >> 4][(e + 1) & 15] - delta));
+    for (int f = 0; f < 4; ++f) ds_pair(f);
     __builtin_amdgcn_sched_barrier(0);
 
     // dQ^T += K^T dS^T: 4 key quarters x 8 d blocks; K^T fragments through the
@@ -298,6 +312,7 @@ __global__ __launch_bounds__(kWavesH * 64) void bwd_dq_h16_kernel(BwdParams bp) 
       const int n = u & 7, hq4 = u >> 3;
       const V8 b = __builtin_bit_cast(V8, u32x4{dsk[4 * hq4], dsk[4 * hq4 + 1], dsk[4 * hq4 + 2], dsk[4 * hq4 + 3]});
       acc[n] = Elem<E>::mfma(kt[u % 3], b, acc[n]);
+      if (u < 24 && (u & 1) == 0) ds_pair(4 * (hq4 + 1) + ((u & 7) >> 1));
       __builtin_amdgcn_sched_barrier(0);
     }
     t = tn;
