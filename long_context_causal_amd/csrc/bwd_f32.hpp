@@ -102,8 +102,8 @@ __global__ __launch_bounds__(kWavesDQ * 64) void bwd_dq_f32_kernel(BwdParams bp)
   const int n_tiles = (int)((kv_end + kBkDQ - 1) / kBkDQ);
 
   const bool seg = p.seg_q != nullptr;
-  const bool use_bits = seg && n_tiles <= kMaxSegTiles;
-  if (use_bits) seg_scan<kWavesDQ, kBkDQ>(sm.bits, p, w, n_tiles);
+  const int sh = seg ? seg_shift(n_tiles) : 0;
+  if (seg) seg_scan<kWavesDQ, kBkDQ>(sm.bits, sh, p, w, n_tiles);
 
   const int64_t kv_head = (int64_t)w.b * p.Hkv + w.kvh;
   const rsrc_t rk = make_rsrc((const char*)p.k + kv_head * p.Lk * kD * 4, (uint32_t)(p.Lk * kD * 4));
@@ -147,17 +147,17 @@ __global__ __launch_bounds__(kWavesDQ * 64) void bwd_dq_f32_kernel(BwdParams bp)
 
   LanesBwdF ln;
   ln.init(lane);
-  int t = use_bits ? seg_next(sm.bits, 0, n_tiles) : 0;
+  int t = seg ? seg_next(sm.bits, sh, 0, n_tiles) : 0;
   int st = 0;
   if (t < n_tiles) dq_copy(sm, 0, rk, rv, rs, seg, t, wave, lane);
   while (t < n_tiles) {
-    const int tn = use_bits ? seg_next(sm.bits, t + 1, n_tiles) : t + 1;
+    const int tn = seg ? seg_next(sm.bits, sh, t + 1, n_tiles) : t + 1;
     wait_vm0();
     __syncthreads();
     if (tn < n_tiles) dq_copy(sm, st ^ 1, rk, rv, rs, seg, tn, wave, lane);
     const int64_t k0 = (int64_t)t * kBkDQ;
     if (!(p.causal && k0 > p.q_offset + pw + kRowsDQ - 1)) {
-      const bool seg_full = !seg || (use_bits && ((sm.bits.full[t >> 5] >> (t & 31)) & 1u));
+      const bool seg_full = !seg || seg_full_tile(sm.bits, sh, t);
       const bool need_mask = !seg_full || k0 + kBkDQ > p.Lk || (p.causal && k0 + kBkDQ - 1 > p.q_offset + pw);
       const char* Ks = sm.k[st];
       const char* Vs = sm.v[st];
@@ -293,10 +293,10 @@ __global__ __launch_bounds__(kWavesDKV * 64) void bwd_dkv_f32_kernel(BwdParams b
   const int n_rb = (int)((p.Lq + kRowsDKV - 1) / kRowsDKV);
 
   const bool seg = p.seg_q != nullptr;
-  const bool use_bits = seg && n_rb <= kMaxSegTiles;
-  if (use_bits)
-    seg_scan_ids<kWavesDKV * 64, kRowsDKV>(sm.bits, p.seg_k + (int64_t)b * p.Lk, j0, kKeysBlockDKV, p.Lk,
-                                           p.seg_q + (int64_t)b * p.Lq, p.Lq, n_rb);
+  const int sh = seg ? seg_shift(n_rb) : 0;
+  if (seg)
+    seg_scan_ids<kWavesDKV * 64, kRowsDKV>(sm.bits, sh, p.seg_k + (int64_t)b * p.Lk, j0, kKeysBlockDKV, p.Lk,
+                                           p.seg_q + (int64_t)b * p.Lq, p.Lq, n_rb, rb0);
   const int sk = seg ? p.seg_k[(int64_t)b * p.Lk + key_c] : 0;
 
   // K of the lane's key in registers: chunk 4 c + g (d = 16 c + 4 g + e). V of
@@ -333,7 +333,7 @@ __global__ __launch_bounds__(kWavesDKV * 64) void bwd_dkv_f32_kernel(BwdParams b
   // key block starts at the last rows, so the workgroups that run together on
   // an XCD (one kv head) stream the same Q / dO tiles at about the same time
   // and share them in that XCD's L2.
-  int rb = use_bits ? seg_prev(sm.bits, n_rb - 1, rb0) : n_rb - 1;
+  int rb = seg ? seg_prev(sm.bits, sh, n_rb - 1, rb0) : n_rb - 1;
   int hh = 0;
   int st = 0;
   if (rb >= rb0) {
@@ -344,7 +344,7 @@ __global__ __launch_bounds__(kWavesDKV * 64) void bwd_dkv_f32_kernel(BwdParams b
     int rbn = rb, hhn = hh + 1;
     if (hhn == n_rep) {
       hhn = 0;
-      rbn = use_bits ? seg_prev(sm.bits, rb - 1, rb0) : rb - 1;
+      rbn = seg ? seg_prev(sm.bits, sh, rb - 1, rb0) : rb - 1;
     }
     wait_vm0();
     __syncthreads();
@@ -354,7 +354,7 @@ __global__ __launch_bounds__(kWavesDKV * 64) void bwd_dkv_f32_kernel(BwdParams b
     }
     const int64_t i0 = (int64_t)rb * kRowsDKV;
     if (!(p.causal && kw0 > p.q_offset + i0 + kRowsDKV - 1)) {
-      const bool seg_full = !seg || (use_bits && ((sm.bits.full[rb >> 5] >> (rb & 31)) & 1u));
+      const bool seg_full = !seg || seg_full_tile(sm.bits, sh, rb);
       const bool need_mask =
           !seg_full || i0 + kRowsDKV > p.Lq || (p.causal && kw0 + kKeysDKV - 1 > p.q_offset + i0);
       const char* Qs = sm.q[st];

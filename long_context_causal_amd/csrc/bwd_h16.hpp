@@ -133,8 +133,8 @@ __global__ __launch_bounds__(kWavesH * 64) void bwd_dq_h16_kernel(BwdParams bp) 
   const int64_t p_end = min(w.p0 + (int64_t)p.ppc, p.Lq);
   const int64_t kv_end = p.causal ? min(p.Lk, p.q_offset + p_end) : p.Lk;
   const int n_tiles = (int)((kv_end + kBkH - 1) / kBkH);
-  const bool use_bits = SEG && n_tiles <= kMaxSegTiles;
-  if (SEG && use_bits) seg_scan<kWavesH, kBkH>(sm.bits, p, w, n_tiles);
+  const int sh = SEG ? seg_shift(n_tiles) : 0;
+  if (SEG) seg_scan<kWavesH, kBkH>(sm.bits, sh, p, w, n_tiles);
 
   const int64_t kv_head = (int64_t)w.b * p.Hkv + w.kvh;
   const char* kbase = (const char*)p.k + kv_head * p.Lk * kRowB16;
@@ -190,7 +190,7 @@ __global__ __launch_bounds__(kWavesH * 64) void bwd_dq_h16_kernel(BwdParams bp) 
                    SEG ? (uint32_t)keys * 4u : 0u);
   };
 
-  int t = (SEG && use_bits) ? seg_next(sm.bits, 0, n_tiles) : 0;
+  int t = SEG ? seg_next(sm.bits, sh, 0, n_tiles) : 0;
   int st = 0;
   if (t < n_tiles) {
     Copy16 ck, cv;
@@ -204,7 +204,7 @@ __global__ __launch_bounds__(kWavesH * 64) void bwd_dq_h16_kernel(BwdParams bp) 
     if (SEG && wave == kWavesH - 1) buf2lds4(rs, (uint32_t)lane * 4u, sst_lds);
   }
   while (t < n_tiles) {
-    const int tn = (SEG && use_bits) ? seg_next(sm.bits, t + 1, n_tiles) : t + 1;
+    const int tn = SEG ? seg_next(sm.bits, sh, t + 1, n_tiles) : t + 1;
     wait_vm0();
     __syncthreads();
     Copy16 ck, cv;
@@ -217,7 +217,7 @@ __global__ __launch_bounds__(kWavesH * 64) void bwd_dq_h16_kernel(BwdParams bp) 
     // mask of the tile in 32 bits: key 32 j + 8 (r / 4) + 4 g + r % 4 of the
     // tile is visible to the lane's row iff it is below kl (causal and Lk) and
     // (with ids) its id equals the row's
-    const bool seg_elem = SEG && !(use_bits && ((sm.bits.full[t >> 5] >> (t & 31)) & 1u));
+    const bool seg_elem = SEG && !seg_full_tile(sm.bits, sh, t);
     const int64_t kend = p.causal ? min(p.Lk, p.q_offset + row + 1) : p.Lk;
     const int kl = (int)max((int64_t)0, min((int64_t)kBkH, kend - k0));
 
@@ -368,10 +368,10 @@ __global__ __launch_bounds__(kWavesH * 64) void bwd_dkv_h16_kernel(BwdParams bp)
   const int64_t r_first = p.causal ? max((int64_t)0, j0 - p.q_offset) : 0;
   const int rb0 = (int)(r_first / kRowsDKVH);
   const int n_rb = (int)((p.Lq + kRowsDKVH - 1) / kRowsDKVH);
-  const bool use_bits = SEG && n_rb <= kMaxSegTiles;
-  if (SEG && use_bits)
-    seg_scan_ids<kWavesH * 64, kRowsDKVH>(sm.bits, p.seg_k + (int64_t)b * p.Lk, j0, kKeysBlockDKVH, p.Lk,
-                                          p.seg_q + (int64_t)b * p.Lq, p.Lq, n_rb);
+  const int sh = SEG ? seg_shift(n_rb) : 0;
+  if (SEG)
+    seg_scan_ids<kWavesH * 64, kRowsDKVH>(sm.bits, sh, p.seg_k + (int64_t)b * p.Lk, j0, kKeysBlockDKVH, p.Lk,
+                                          p.seg_q + (int64_t)b * p.Lq, p.Lq, n_rb, rb0);
   const int sk = SEG ? p.seg_k[(int64_t)b * p.Lk + key_c] : 0;
 
   // K of the lane's key (B-operand layout: chunk 2 c + g); V of the block's
@@ -429,7 +429,7 @@ __global__ __launch_bounds__(kWavesH * 64) void bwd_dkv_h16_kernel(BwdParams bp)
     if (SEG) buf2lds4(make_rsrc(p.seg_q + (int64_t)b * p.Lq, nb), off, lds_addr(sm.segq[st]));
   };
 
-  int rb = (SEG && use_bits) ? seg_prev(sm.bits, n_rb - 1, rb0) : n_rb - 1;
+  int rb = SEG ? seg_prev(sm.bits, sh, n_rb - 1, rb0) : n_rb - 1;
   int hh = 0;
   int st = 0;
   if (rb >= rb0) {
@@ -446,7 +446,7 @@ __global__ __launch_bounds__(kWavesH * 64) void bwd_dkv_h16_kernel(BwdParams bp)
     int rbn = rb, hhn = hh + 1;
     if (hhn == n_rep) {
       hhn = 0;
-      rbn = (SEG && use_bits) ? seg_prev(sm.bits, rb - 1, rb0) : rb - 1;
+      rbn = SEG ? seg_prev(sm.bits, sh, rb - 1, rb0) : rb - 1;
     }
     const bool have_next = rbn >= rb0;
     wait_vm0();
@@ -459,7 +459,7 @@ __global__ __launch_bounds__(kWavesH * 64) void bwd_dkv_h16_kernel(BwdParams bp)
 
     // mask limits of the tile (32-bit): row ri of the tile sees the lane's key
     // iff lim <= ri < nrow and (with ids) the row's id equals the key's
-    const bool seg_elem = SEG && !(use_bits && ((sm.bits.full[rb >> 5] >> (rb & 31)) & 1u));
+    const bool seg_elem = SEG && !seg_full_tile(sm.bits, sh, rb);
     const bool need_mask = seg_elem || i0 + kRowsDKVH > p.Lq || (p.causal && kw0 + kKeysDKVH - 1 > p.q_offset + i0);
     const int lim = (p.causal && need_mask)
                         ? (int)max((int64_t)-1, min((int64_t)kRowsDKVH, key - p.q_offset - i0))

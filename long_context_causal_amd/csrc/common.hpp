@@ -20,7 +20,6 @@ constexpr int kD = 256;             // head dimension the kernels are built for
 constexpr float kInvSqrtD = 0.0625f;  // 1/sqrt(kD), exact
 static_assert(kD == 256, "kInvSqrtD is 1/sqrt(256)");
 constexpr int kRowsPerWave = 32;    // query rows (one head, 32 positions) per wave
-constexpr int kMaxSegTiles = 16384; // key tiles a workgroup can classify for segment skipping
 
 // Arguments of one forward launch (passed by value).
 struct FwdParams {
@@ -179,35 +178,81 @@ __device__ __forceinline__ void buf2lds4(rsrc_t rsrc, uint32_t voff, uint32_t ld
 }
 
 // ---------------------------------------------------------------------------
-// Segment scan. With segment ids, a key tile is visible to the workgroup when
-// the id range of its keys meets the id range of the workgroup's query rows; it
-// is "full" (no element mask needed for the segment part) when both ranges are
-// the same single id. Ranges are exact for any ids and tight for sorted
-// (packed) ids, and the per-tile state is two bits, so the metadata grows with
-// L / tile, never with (L / tile)^2.
+// Segment classification. With segment ids, a key tile is visible to the
+// workgroup when the id range of its keys meets the id range of the
+// workgroup's query rows, and "full" (no element mask needed for the segment
+// part) when both ranges are the same single id. The ranges are exact for any
+// ids and tight for sorted (packed) ids. The state is two bits per group of
+// 2^shift consecutive tiles, shift the smallest that fits the tile count into
+// kSegGroups groups: one tile per bit up to 32,768 tiles (2M keys in 64-key
+// tiles), then groups of 2, 4, ... tiles, so the metadata is a fixed 8 KB of
+// LDS at any length and never grows as (L / tile)^2 (the block-mask tables of
+// splash attention do, and overflowed at 1M tokens: maxtext pull request 4929,
+// problem statement). A group is visible if any of its tiles is; a tile of a
+// visible group that holds no visible key is processed with the element mask
+// and contributes nothing.
 // ---------------------------------------------------------------------------
+constexpr int kSegGroups = 32768;  // bits per map (visible, full)
 struct SegBits {
-  unsigned vis[kMaxSegTiles / 32];
-  unsigned full[kMaxSegTiles / 32];
+  unsigned vis[kSegGroups / 32];
+  unsigned full[kSegGroups / 32];
   int qmin, qmax;
 };
 
-// Generic form: `own` are the ids of this workgroup's own entries [own0,
-// own0 + own_n) of a sequence of own_len (entries past the end are ignored);
-// the scanned side `other` (other_len entries) is cut into tiles of BT.
+// log2 of the tiles per group for a map of n_tiles tiles.
+__device__ __forceinline__ int seg_shift(int n_tiles) {
+  int s = 0;
+  while (((int64_t)(n_tiles - 1) >> s) >= kSegGroups) ++s;
+  return s;
+}
+
+// Min and max over each aligned group of `lanes` lanes (a power of two,
+// 1..64); every lane of a group ends with its group's values. The steps pair
+// lane l with l ^ 1 and l ^ 2 (quad permutes), then with its mirror in the
+// half row and in the row (after the earlier steps those hold the values of
+// l ^ 4 and l ^ 8), then l ^ 16 and l ^ 32 (row swaps).
+__device__ __forceinline__ void group_minmax(int& lo, int& hi, int lanes) {
+  if (lanes >= 2) { lo = min(lo, __builtin_amdgcn_mov_dpp(lo, 0xB1, 0xF, 0xF, false));
+                    hi = max(hi, __builtin_amdgcn_mov_dpp(hi, 0xB1, 0xF, 0xF, false)); }
+  if (lanes >= 4) { lo = min(lo, __builtin_amdgcn_mov_dpp(lo, 0x4E, 0xF, 0xF, false));
+                    hi = max(hi, __builtin_amdgcn_mov_dpp(hi, 0x4E, 0xF, 0xF, false)); }
+  if (lanes >= 8) { lo = min(lo, __builtin_amdgcn_mov_dpp(lo, 0x141, 0xF, 0xF, false));
+                    hi = max(hi, __builtin_amdgcn_mov_dpp(hi, 0x141, 0xF, 0xF, false)); }
+  if (lanes >= 16) { lo = min(lo, __builtin_amdgcn_mov_dpp(lo, 0x140, 0xF, 0xF, false));
+                     hi = max(hi, __builtin_amdgcn_mov_dpp(hi, 0x140, 0xF, 0xF, false)); }
+  if (lanes >= 32) {
+    const auto a = __builtin_amdgcn_permlane16_swap((unsigned)lo, (unsigned)lo, false, false);
+    const auto b = __builtin_amdgcn_permlane16_swap((unsigned)hi, (unsigned)hi, false, false);
+    lo = min((int)a[0], (int)a[1]);
+    hi = max((int)b[0], (int)b[1]);
+  }
+  if (lanes >= 64) {
+    const auto a = __builtin_amdgcn_permlane32_swap((unsigned)lo, (unsigned)lo, false, false);
+    const auto b = __builtin_amdgcn_permlane32_swap((unsigned)hi, (unsigned)hi, false, false);
+    lo = min((int)a[0], (int)a[1]);
+    hi = max((int)b[0], (int)b[1]);
+  }
+}
+
+typedef __attribute__((ext_vector_type(4), aligned(4))) int i32x4_a4;  // 4-byte aligned 16-byte load
+
+// Classifies the tiles of the scanned side for one workgroup. `own` are the
+// ids of the workgroup's own entries [own0, own0 + own_n) of a sequence of
+// own_len (entries past the end are ignored); the scanned side `other`
+// (other_len entries) is cut into tiles of BT entries, tiles [0, n_tiles);
+// groups wholly below tile t_first are left invisible (the caller never
+// visits them). sh = seg_shift(n_tiles). The ids are read with 16-byte loads
+// that consecutive lanes take from consecutive addresses, 16 loads per lane
+// in flight; each wave owns a contiguous run of map words.
 template <int NT, int BT>
-__device__ void seg_scan_ids(SegBits& sb, const int32_t* own, int64_t own0, int own_n, int64_t own_len,
-                             const int32_t* other, int64_t other_len, int n_tiles) {
+__device__ void seg_scan_ids(SegBits& sb, int sh, const int32_t* own, int64_t own0, int own_n, int64_t own_len,
+                             const int32_t* other, int64_t other_len, int n_tiles, int t_first = 0) {
+  static_assert(BT == 16 || BT == 32 || BT == 64, "tiles of 16, 32 or 64 entries");
   constexpr int W = NT / 64;
-  constexpr int KPL = BT < 32 ? BT : 32;  // consecutive entries each lane reduces per pass
-  constexpr int LPT = BT / KPL;           // lanes that share one tile
-  static_assert(BT % KPL == 0, "tile must be a whole number of lane chunks");
+  constexpr int kLoads = 16;  // 16-byte loads in flight per lane
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
-  const int words = (n_tiles + 31) >> 5;
-  for (int i = tid; i < words; i += NT) { sb.vis[i] = 0u; sb.full[i] = 0u; }
   if (tid == 0) { sb.qmin = INT32_MAX; sb.qmax = INT32_MIN; }
   __syncthreads();
-  // id range of this workgroup's own entries
   {
     int lo = INT32_MAX, hi = INT32_MIN;
     for (int r = tid; r < own_n; r += NT) {
@@ -220,27 +265,73 @@ __device__ void seg_scan_ids(SegBits& sb, const int32_t* own, int64_t own0, int 
   }
   __syncthreads();
   const int qmin = sb.qmin, qmax = sb.qmax;
-  const int64_t n_other = (int64_t)n_tiles * BT;
-  for (int64_t base = (int64_t)wave * 64 * KPL; base < n_other; base += (int64_t)W * 64 * KPL) {
-    const int64_t k0 = base + (int64_t)lane * KPL;
-    int v[KPL];
+  const int64_t lim = min(other_len, (int64_t)n_tiles * BT);  // entries past it count as absent
+  const int64_t ge = (int64_t)BT << sh;                        // entries per group (>= 16)
+  const int n_groups = (int)(((int64_t)n_tiles - 1) >> sh) + 1;
+  const int n_words = (n_groups + 31) >> 5;
+  const int w_first = min(n_words, (min(t_first, n_tiles) >> sh) >> 5);  // words below it stay zero
+  const int per_wave = (n_words - w_first + W - 1) / W;
+  const int wb = w_first + wave * per_wave, we = min(n_words, wb + per_wave);
+  for (int wd = tid; wd < w_first; wd += NT) { sb.vis[wd] = 0u; sb.full[wd] = 0u; }
+  // a load covers 256 entries; a group spans na loads and lg lanes of each
+  const int na = ge > 256 ? (int)(ge >> 8) : 1;
+  const int lg = ge >= 256 ? 64 : (int)(ge >> 2);
+  const int gpl = ge >= 256 ? 1 : (int)(256 >> (31 - __builtin_clz((unsigned)ge)));  // groups per load
+  if (wb < we) {
+    const int64_t e_begin = (int64_t)wb * 32 * ge, e_end = (int64_t)we * 32 * ge;
+    unsigned vword = 0u, fword = 0u;
+    int bit = 0, wd = wb, ldn = 0;  // next bit of word wd; loads into the current group
+    int lo_acc = INT32_MAX, hi_acc = INT32_MIN;
+    for (int64_t e = e_begin; e < e_end; e += 256 * kLoads) {
+      int lo4[kLoads], hi4[kLoads];
 #pragma unroll
-    for (int e = 0; e < KPL; ++e) v[e] = (k0 + e < other_len) ? other[k0 + e] : qmin;
-    int lo = INT32_MAX, hi = INT32_MIN;
-    const int nvalid = (int)max((int64_t)0, min((int64_t)KPL, other_len - k0));
+      for (int u = 0; u < kLoads; ++u) {
+        const int64_t x = e + 256 * u + 4 * lane;
+        if (x + 4 <= lim) {
+          const i32x4_a4 v = *(const i32x4_a4*)(other + x);
+          lo4[u] = min(min(v[0], v[1]), min(v[2], v[3]));
+          hi4[u] = max(max(v[0], v[1]), max(v[2], v[3]));
+        } else {
+          lo4[u] = INT32_MAX;
+          hi4[u] = INT32_MIN;
 #pragma unroll
-    for (int e = 0; e < KPL; ++e) {
-      if (e < nvalid) { lo = min(lo, v[e]); hi = max(hi, v[e]); }
-    }
+          for (int c = 0; c < 4; ++c)
+            if (x + c < lim) { const int s = other[x + c]; lo4[u] = min(lo4[u], s); hi4[u] = max(hi4[u], s); }
+        }
+      }
 #pragma unroll
-    for (int s = 1; s < LPT; s <<= 1) {
-      lo = min(lo, __shfl_xor(lo, s));
-      hi = max(hi, __shfl_xor(hi, s));
-    }
-    const int64_t t = k0 / BT;
-    if ((lane % LPT) == 0 && t < n_tiles && lo <= hi) {
-      if (lo <= qmax && hi >= qmin) atomicOr(&sb.vis[t >> 5], 1u << (t & 31));
-      if (lo == hi && qmin == qmax && lo == qmin) atomicOr(&sb.full[t >> 5], 1u << (t & 31));
+      for (int u = 0; u < kLoads; ++u) {
+        if (e + 256 * u >= e_end) break;  // uniform
+        lo_acc = min(lo_acc, lo4[u]);
+        hi_acc = max(hi_acc, hi4[u]);
+        if (++ldn < na) continue;
+        ldn = 0;
+        int lo = lo_acc, hi = hi_acc;
+        lo_acc = INT32_MAX;
+        hi_acc = INT32_MIN;
+        group_minmax(lo, hi, lg);
+        const bool v_ok = lo <= hi && lo <= qmax && hi >= qmin;
+        const bool f_ok = lo <= hi && lo == hi && qmin == qmax && lo == qmin;
+        const uint64_t vm = __builtin_amdgcn_ballot_w64(v_ok), fm = __builtin_amdgcn_ballot_w64(f_ok);
+        // group j of this load sits at lanes j lg ..; gpl divides 32, so the
+        // load's groups fall in one map word
+        unsigned vf = 0u, ff = 0u;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const unsigned on = j < gpl ? 1u : 0u;
+          vf |= ((unsigned)(vm >> (j * lg)) & on) << j;
+          ff |= ((unsigned)(fm >> (j * lg)) & on) << j;
+        }
+        vword |= vf << bit;
+        fword |= ff << bit;
+        bit += gpl;
+        if (bit == 32) {
+          if (lane == 0) { sb.vis[wd] = vword; sb.full[wd] = fword; }
+          vword = fword = 0u;
+          bit = 0;
+          ++wd;
+        }
+      }
     }
   }
   __syncthreads();
@@ -248,32 +339,51 @@ __device__ void seg_scan_ids(SegBits& sb, const int32_t* own, int64_t own0, int 
 
 // The forward's use: own = the workgroup's query rows, scanned = key tiles of BK.
 template <int W, int BK>
-__device__ void seg_scan(SegBits& sb, const FwdParams& p, const Work& w, int n_tiles) {
-  seg_scan_ids<W * 64, BK>(sb, p.seg_q + (int64_t)w.b * p.Lq, w.p0, p.ppc, p.Lq, p.seg_k + (int64_t)w.b * p.Lk,
+__device__ void seg_scan(SegBits& sb, int sh, const FwdParams& p, const Work& w, int n_tiles) {
+  seg_scan_ids<W * 64, BK>(sb, sh, p.seg_q + (int64_t)w.b * p.Lq, w.p0, p.ppc, p.Lq, p.seg_k + (int64_t)w.b * p.Lk,
                            p.Lk, n_tiles);
 }
 
-// First visible tile index >= t (n_tiles if none).
-__device__ __forceinline__ int seg_next(const SegBits& sb, int t, int n_tiles) {
-  while (t < n_tiles) {
-    unsigned m = sb.vis[t >> 5] >> (t & 31);
-    if (m) return t + __builtin_ctz(m);
-    t = (t | 31) + 1;
+// First tile >= t of a visible group (n_tiles if none): t itself when its
+// group is visible, else the first tile of the next visible group.
+__device__ __forceinline__ int seg_next(const SegBits& sb, int sh, int t, int n_tiles) {
+  if (t >= n_tiles) return n_tiles;
+  const int g0 = t >> sh, ng = ((n_tiles - 1) >> sh) + 1;
+  int g = g0;
+  while (g < ng) {
+    const unsigned m = sb.vis[g >> 5] >> (g & 31);
+    if (m) {
+      const int r = g + __builtin_ctz(m);
+      if (r >= ng) return n_tiles;
+      return r == g0 ? t : min(n_tiles, r << sh);
+    }
+    g = (g | 31) + 1;
   }
   return n_tiles;
 }
 
-// Last visible tile index <= t and >= lo (lo - 1 if none).
-__device__ __forceinline__ int seg_prev(const SegBits& sb, int t, int lo) {
-  while (t >= lo) {
-    const unsigned m = sb.vis[t >> 5] << (31 - (t & 31));
+// Last tile <= t and >= lo of a visible group (lo - 1 if none): t itself when
+// its group is visible, else the last tile of the previous visible group.
+__device__ __forceinline__ int seg_prev(const SegBits& sb, int sh, int t, int lo) {
+  if (t < lo) return lo - 1;
+  const int g0 = t >> sh, glo = lo >> sh;
+  int g = g0;
+  while (g >= glo) {
+    const unsigned m = sb.vis[g >> 5] << (31 - (g & 31));
     if (m) {
-      const int r = t - __builtin_clz(m);
-      return r >= lo ? r : lo - 1;
+      const int r = g - __builtin_clz(m);
+      if (r < glo) return lo - 1;
+      return r == g0 ? t : ((r + 1) << sh) - 1;
     }
-    t = (t & ~31) - 1;
+    g = (g & ~31) - 1;
   }
   return lo - 1;
+}
+
+// Is every key of tile t's group of the workgroup's single query id?
+__device__ __forceinline__ bool seg_full_tile(const SegBits& sb, int sh, int t) {
+  const int g = t >> sh;
+  return (sb.full[g >> 5] >> (g & 31)) & 1u;
 }
 
 }  // namespace gqa

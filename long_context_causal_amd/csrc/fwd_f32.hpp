@@ -131,8 +131,8 @@ __global__ __launch_bounds__(W * 64) void fwd_f32_kernel(FwdParams p) {
   const int n_tiles = (int)((kv_end + kBkF - 1) / kBkF);
 
   const bool seg = p.seg_q != nullptr;
-  const bool use_bits = seg && n_tiles <= kMaxSegTiles;
-  if (use_bits) seg_scan<W, kBkF>(sm.bits, p, w, n_tiles);
+  const int sh = seg ? seg_shift(n_tiles) : 0;
+  if (seg) seg_scan<W, kBkF>(sm.bits, sh, p, w, n_tiles);
   // tiles [t_lo, t_hi): all of them, or this workgroup's key split
   const bool split = p.n_split > 1;
   const int t_lo = split ? w.split * p.split_tiles : 0;
@@ -170,7 +170,7 @@ __global__ __launch_bounds__(W * 64) void fwd_f32_kernel(FwdParams p) {
 
   auto next_tile = [&](int t) -> int {
     if (t >= t_hi) return t_hi;
-    return use_bits ? seg_next(sm.bits, t + 1, t_hi) : t + 1;
+    return seg ? seg_next(sm.bits, sh, t + 1, t_hi) : t + 1;
   };
   auto k_copy = [&](int st, int t) {
     return part_copy_f(kbase + (uint32_t)st * kTileBytesF, sbase + (uint32_t)st * (2 * kBkF * 4), kb, skb, t,
@@ -182,7 +182,7 @@ __global__ __launch_bounds__(W * 64) void fwd_f32_kernel(FwdParams p) {
   // element mask of tile t's scores (its ids in K stage st), where the tile needs one
   auto mask_if_needed = [&](f32x16& s, int t, int st) {
     const int64_t k0 = (int64_t)t * kBkF;
-    const bool seg_full = !seg || (use_bits && ((sm.bits.full[t >> 5] >> (t & 31)) & 1u));
+    const bool seg_full = !seg || seg_full_tile(sm.bits, sh, t);
     if (seg_full && k0 + kBkF <= p.Lk && !(p.causal && k0 + kBkF - 1 > p.q_offset + pw)) return;
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
@@ -213,7 +213,7 @@ __global__ __launch_bounds__(W * 64) void fwd_f32_kernel(FwdParams p) {
     }
   };
 
-  int cur = use_bits ? seg_next(sm.bits, t_lo, t_hi) : t_lo;
+  int cur = seg ? seg_next(sm.bits, sh, t_lo, t_hi) : t_lo;
   if (cur < t_hi) {
     int nxt = next_tile(cur), nn = next_tile(nxt);
     // K(#0), K(#1) and V(#0) into stages 0, 1 and 0 (V(#1) is copied in step 0)

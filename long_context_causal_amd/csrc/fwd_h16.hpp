@@ -337,14 +337,14 @@ struct H16Wave {
   const int32_t* skb;
   int64_t pw, lim;
   int wave, lane, g, sq, n_tiles;
-  bool use_bits;
+  int sh;  // log2 of the key tiles per segment-map group
   int cur, nxt, nn;  // visible tiles: being finished, QK this step, next after that
 
   __device__ __forceinline__ H16Wave(const FwdParams& p_, SmemB& sm_) : p(p_), sm(sm_) {}
 
   __device__ __forceinline__ int next_tile(int t) const {
     if (t >= n_tiles) return n_tiles;
-    if constexpr (SEG) return use_bits ? seg_next(sm.bits, t + 1, n_tiles) : t + 1;
+    if constexpr (SEG) return seg_next(sm.bits, sh, t + 1, n_tiles);
     return t + 1;
   }
   __device__ __forceinline__ PartCopy k_copy(int st, int t) const {
@@ -355,7 +355,7 @@ struct H16Wave {
     return part_copy(rb.v + (uint32_t)st * kTileBytesB, 0u, vb, nullptr, t, t < n_tiles, p.Lk);
   }
   __device__ __forceinline__ bool full_bit(int t) const {
-    return SEG && use_bits && t < n_tiles && ((sm.bits.full[t >> 5] >> (t & 31)) & 1u);
+    return SEG && t < n_tiles && seg_full_tile(sm.bits, sh, t);
   }
   // Masks the 32 scores per lane of tile t (s[16 j + r]: element r of key
   // half j) where some key of the tile is hidden from some row of the wave;
@@ -471,8 +471,8 @@ __global__ __launch_bounds__(kWavesB * 64) void fwd_h16_kernel(FwdParams p) {
   const int64_t kv_end = p.causal ? min(p.Lk, p.q_offset + p_end) : p.Lk;
   wv.n_tiles = (int)((kv_end + kBkB - 1) / kBkB);
 
-  wv.use_bits = SEG && wv.n_tiles <= kMaxSegTiles;
-  if (SEG && wv.use_bits) seg_scan<kWavesB, kBkB>(sm.bits, p, w, wv.n_tiles);
+  wv.sh = SEG ? seg_shift(wv.n_tiles) : 0;
+  if (SEG) seg_scan<kWavesB, kBkB>(sm.bits, wv.sh, p, w, wv.n_tiles);
   // tiles [t_lo, n_tiles): all of them, or this workgroup's key split (tiles
   // at or past the new n_tiles count as past the end)
   const bool split = p.n_split > 1;
@@ -505,7 +505,7 @@ __global__ __launch_bounds__(kWavesB * 64) void fwd_h16_kernel(FwdParams p) {
   wv.ln.init(wv.wave, wv.lane, (lds_cchar*)sm.k[0], (lds_cchar*)sm.v[0]);
   wv.rb = RingBase{lds_addr(sm.k[0]), lds_addr(sm.v[0]), lds_addr(sm.segk[0])};
 
-  wv.cur = SEG && wv.use_bits ? seg_next(sm.bits, t_lo, wv.n_tiles) : t_lo;
+  wv.cur = SEG ? seg_next(sm.bits, wv.sh, t_lo, wv.n_tiles) : t_lo;
   if (wv.cur < wv.n_tiles) {
     wv.nxt = wv.next_tile(wv.cur);
     wv.nn = wv.next_tile(wv.nxt);

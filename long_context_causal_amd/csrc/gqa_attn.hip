@@ -55,6 +55,10 @@ static int fwd_plan(gqa::FwdParams& p, const void* q, const void* k, const void*
       overlap(lse, lse_bytes, o, qo_bytes) || overlap(lse, lse_bytes, q, qo_bytes) ||
       overlap(lse, lse_bytes, k, kv_bytes) || overlap(lse, lse_bytes, v, kv_bytes))
     return GQA_ERR_ALIAS;
+  // every workgroup reads the ids while earlier ones already write o and lse
+  if (seg_q && (overlap(o, qo_bytes, seg_q, B * Lq * 4) || overlap(o, qo_bytes, seg_k, B * Lk * 4) ||
+                overlap(lse, lse_bytes, seg_q, B * Lq * 4) || overlap(lse, lse_bytes, seg_k, B * Lk * 4)))
+    return GQA_ERR_ALIAS;
 
   const int W = dtype == GQA_F32 ? gqa::kWavesF32 : gqa::kWavesH16;
   p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
@@ -243,7 +247,8 @@ GQA_API int gqa_attn_merge(const void* o1, const float* lse1, const void* o2, co
   // outputs may be exactly an input (in place) but must not partially overlap one
   if ((o != o1 && overlap(o, ob, o1, ob)) || (o != o2 && overlap(o, ob, o2, ob)) ||
       (lse != lse1 && overlap(lse, lb, lse1, lb)) || (lse != lse2 && overlap(lse, lb, lse2, lb)) ||
-      overlap(o, ob, lse, lb) || overlap(o, ob, lse1, lb) || overlap(o, ob, lse2, lb))
+      overlap(o, ob, lse, lb) || overlap(o, ob, lse1, lb) || overlap(o, ob, lse2, lb) ||
+      overlap(lse, lb, o1, ob) || overlap(lse, lb, o2, ob))
     return GQA_ERR_ALIAS;
   hipStream_t s = (hipStream_t)stream;
   (void)hipGetLastError();

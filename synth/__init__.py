@@ -162,14 +162,17 @@ class Branch:
         return q, k, v, ids
 
 
-def sample_rows(L: int, *, bounds=None, n_random: int = 512, seed: int = 2, upto: int = 4096) -> np.ndarray:
+def sample_rows(L: int, *, bounds=None, n_random: int = 512, seed: int = 2, upto: int = 4096,
+                tail: int = 4096) -> np.ndarray:
     """Sorted, distinct query rows to check at large L: the first and last rows,
-    every multiple of 16/32/64/128 below `upto` and its neighbours, the first and
-    last rows (and neighbours) of each (start, end) in `bounds`, and `n_random`
-    rows from default_rng(seed)."""
+    every multiple of 16/32/64/128 below `upto` and within the last `tail` rows,
+    each with its neighbours, the first and last rows (and neighbours) of each
+    (start, end) in `bounds`, and `n_random` rows from default_rng(seed)."""
     s = {0, 1, 2, L - 2, L - 1}
     for step in (16, 32, 64, 128):
         for x in range(0, min(upto, L), step):
+            s.update((x - 1, x, x + 1))
+        for x in range(max(0, L - tail) // step * step, L + 1, step):
             s.update((x - 1, x, x + 1))
     for a, b in (bounds or []):
         s.update((a - 1, a, a + 1, b - 2, b - 1, b))

@@ -60,9 +60,10 @@ def run(x, **kw):
 def compare(o, lse, o_ref, lse_ref, dtype, rows=None, label="", tol_scale=1.0):
     """Element-wise check; o/lse device outputs, refs fp64 (optionally on a row subset).
 
-    The bars are those stated for N(0,1) inputs (logit standard deviation 1). For
-    stress inputs whose logits are `tol_scale` times larger, the fp32 rounding of
-    the score dot products grows in proportion, and so do both bars."""
+    The bars are those stated for N(0,1) inputs (logit standard deviation 1).
+    `tol_scale` widens both: fp32 stress inputs whose logits are tol_scale times
+    larger pass it, since the fp32 rounding of the score dot products grows in
+    proportion; 16-bit inputs keep 1 (their error is the rounding of P and O)."""
     o_h = o.float().cpu().numpy().astype(np.float64)
     l_h = lse.cpu().numpy().astype(np.float64)
     if rows is not None:

@@ -60,6 +60,9 @@ def test_version_and_strerror():
     (dict(q=Q + 2), 4), (dict(k=K + 8), 4), (dict(v=V + 4), 4), (dict(o=O + 2), 4), (dict(lse=LSE + 2), 4),
     (dict(seg_q=SQ + 2, seg_k=SK), 4),
     (dict(o=Q + 4096), 6), (dict(o=K), 6), (dict(lse=O + 64), 6), (dict(lse=V), 6),
+    # o or lse over the segment ids, which every workgroup reads while others write
+    (dict(seg_q=SQ, seg_k=SK, o=SQ - 4096), 6), (dict(seg_q=SQ, seg_k=SK, o=SK + 256), 6),
+    (dict(seg_q=SQ, seg_k=SK, lse=SQ + 4), 6), (dict(seg_q=SQ, seg_k=SK, lse=SK - 64), 6),
 ])
 def test_fwd_rejects_before_launch(over, code):
     assert call(**over) == code
@@ -69,6 +72,8 @@ def test_fwd_rejects_before_launch(over, code):
     (dict(o1=None), 1), (dict(lse=None), 1), (dict(rows=0), 2), (dict(D=0), 2), (dict(D=12), 3),
     (dict(dtype=5), 3), (dict(o1=O + 8), 4), (dict(lse2=LSE + 2), 4), (dict(o=Q + 16), 6),
     (dict(lse=SQ + 4), 6), (dict(o=K + 512), 6),
+    # the merged lse over o1 or o2, which other rows still read
+    (dict(lse=Q + 64), 6), (dict(lse=K + 1024), 6),
 ])
 def test_merge_rejects_before_launch(over, code):
     a = dict(o1=Q, lse1=SQ, o2=K, lse2=SK, o=O, lse=LSE, rows=100, D=256, dtype=gqa.GQA_F32, stream=None)

@@ -33,11 +33,16 @@ def test_small_config_fp32_scaled():
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("scale", [1.0, 8.0])
 def test_unscaled_and_peaky(dtype, scale):
-    # logit std 1 and a "peaky" variant: only Q is scaled (x8 gives logit std 8)
+    """Logit std 1 and a "peaky" variant: only Q is scaled (x8 gives logit std 8).
+
+    fp32: the rounding of the fp32 score dot products grows with the logits
+    (|do| ~ u |s| |v - o|), so both bars scale with them. bf16 / fp16: the
+    error is the rounding of P and of O to the input type, which does not grow
+    with the logits, so the stated bars hold as they are."""
     x = synth.gqa(1, 16, 4, 512, seed=3, dtype=dtype)
     if scale != 1.0:
         x = synth.Inputs(x.q * np.float32(scale), x.k, x.v, dtype)
-    check(x, "L512 %s qscale %g" % (dtype, scale), tol_scale=scale)
+    check(x, "L512 %s qscale %g" % (dtype, scale), tol_scale=scale if dtype == "f32" else 1.0)
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
