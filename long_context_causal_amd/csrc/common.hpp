@@ -146,15 +146,16 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 }
 // lds: LDS byte address of the wave's 1 KB (or 256 B) destination. It and the
 // resource words go through readfirstlane: they are wave-uniform, and this
-// keeps them in SGPRs even where the compiler cannot prove that (inside a
-// branch on the lane index, for one).
+// keeps them in SGPRs even where the compiler has placed a uniform value in
+// VGPRs (inside a branch on the lane index, for one); where they already are
+// in SGPRs the compiler drops the readfirstlane.
 __device__ __forceinline__ rsrc_t uniform_rsrc(rsrc_t r) {
   return rsrc_t{__builtin_amdgcn_readfirstlane(r[0]), __builtin_amdgcn_readfirstlane(r[1]),
                 __builtin_amdgcn_readfirstlane(r[2]), __builtin_amdgcn_readfirstlane(r[3])};
 }
 __device__ __forceinline__ void buf2lds16(rsrc_t rsrc, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc) : "memory");
+               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(uniform_rsrc(rsrc)) : "memory");
 }
 // The same with the LDS address lds + imm, imm a constant once the caller is
 // inlined and unrolled: the add writes M0 directly (one scalar instruction
@@ -164,7 +165,8 @@ __device__ __forceinline__ void buf2lds16(rsrc_t rsrc, uint32_t voff, uint32_t l
 // then loses it.
 __device__ __forceinline__ void buf2lds16_imm(rsrc_t rsrc, uint32_t voff, uint32_t lds, uint32_t imm) {
   asm volatile("s_add_u32 m0, %0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc), "i"(imm) : "memory", "scc");
+               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(uniform_rsrc(rsrc)), "i"(imm)
+               : "memory", "scc");
 }
 // The 4-byte copy takes its resource words through readfirstlane, a VALU
 // write of SGPRs that a vector-memory read of them must trail by 5 wait
@@ -236,102 +238,147 @@ __device__ __forceinline__ void group_minmax(int& lo, int& hi, int lanes) {
 
 typedef __attribute__((ext_vector_type(4), aligned(4))) int i32x4_a4;  // 4-byte aligned 16-byte load
 
+// The bits at lanes 0, 4, 8, ..., 60 of a wave mask, packed into bits 0..15.
+__device__ __forceinline__ unsigned pack_quads(uint64_t m) {
+  m &= 0x1111111111111111ull;
+  m = (m | (m >> 3)) & 0x0303030303030303ull;
+  m = (m | (m >> 6)) & 0x000F000F000F000Full;
+  m = (m | (m >> 12)) & 0x000000FF000000FFull;
+  m = (m | (m >> 24)) & 0xFFFFull;
+  return (unsigned)m;
+}
+
 // Classifies the tiles of the scanned side for one workgroup. `own` are the
 // ids of the workgroup's own entries [own0, own0 + own_n) of a sequence of
 // own_len (entries past the end are ignored); the scanned side `other`
 // (other_len entries) is cut into tiles of BT entries, tiles [0, n_tiles);
 // groups wholly below tile t_first are left invisible (the caller never
-// visits them). sh = seg_shift(n_tiles). The ids are read with 16-byte loads
-// that consecutive lanes take from consecutive addresses, 16 loads per lane
-// in flight; each wave owns a contiguous run of map words.
+// visits them). sh = seg_shift(n_tiles).
+// Layout of the reads: a batch is 16 consecutive tiles, tile 16 b + q read by
+// the four lanes of quad q, each lane 16 contiguous bytes of each 16-entry
+// chunk of the tile, so a load instruction covers 64 contiguous bytes per tile
+// and 16 tiles; 16 loads per lane are in flight, then the tile ranges come
+// from two quad steps. With one tile per map bit the 16 tiles' bits of a
+// batch come from one ballot; larger groups reduce further across lanes (and
+// across batches) and set their bits with LDS atomics. Each wave owns a
+// contiguous run of map words.
 template <int NT, int BT>
 __device__ void seg_scan_ids(SegBits& sb, int sh, const int32_t* own, int64_t own0, int own_n, int64_t own_len,
                              const int32_t* other, int64_t other_len, int n_tiles, int t_first = 0) {
   static_assert(BT == 16 || BT == 32 || BT == 64, "tiles of 16, 32 or 64 entries");
   constexpr int W = NT / 64;
-  constexpr int kLoads = 16;  // 16-byte loads in flight per lane
+  constexpr int kCh = BT / 16;     // 16-entry chunks per tile: loads per batch
+  constexpr int kNB = 16 / kCh;    // batches per pass (16 loads per lane in flight)
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+  const int q = lane >> 2, r = lane & 3;
   if (tid == 0) { sb.qmin = INT32_MAX; sb.qmax = INT32_MIN; }
   __syncthreads();
   {
     int lo = INT32_MAX, hi = INT32_MIN;
-    for (int r = tid; r < own_n; r += NT) {
-      const int64_t i = own0 + r;
-      if (i < own_len) { const int s = own[i]; lo = min(lo, s); hi = max(hi, s); }
+    for (int i = tid; i < own_n; i += NT) {
+      const int64_t x = own0 + i;
+      if (x < own_len) { const int s = own[x]; lo = min(lo, s); hi = max(hi, s); }
     }
     lo = wave_min_i(lo);
     hi = wave_max_i(hi);
     if (lane == 0) { atomicMin(&sb.qmin, lo); atomicMax(&sb.qmax, hi); }
   }
+  const int n_groups = (int)(((int64_t)n_tiles - 1) >> sh) + 1;
+  const int n_words = (n_groups + 31) >> 5;
+  for (int wd = tid; wd < n_words; wd += NT) { sb.vis[wd] = 0u; sb.full[wd] = 0u; }
   __syncthreads();
   const int qmin = sb.qmin, qmax = sb.qmax;
   const int64_t lim = min(other_len, (int64_t)n_tiles * BT);  // entries past it count as absent
-  const int64_t ge = (int64_t)BT << sh;                        // entries per group (>= 16)
-  const int n_groups = (int)(((int64_t)n_tiles - 1) >> sh) + 1;
-  const int n_words = (n_groups + 31) >> 5;
-  const int w_first = min(n_words, (min(t_first, n_tiles) >> sh) >> 5);  // words below it stay zero
+  const int w_first = min(n_words, (min(t_first, n_tiles) >> sh) >> 5);
   const int per_wave = (n_words - w_first + W - 1) / W;
   const int wb = w_first + wave * per_wave, we = min(n_words, wb + per_wave);
-  for (int wd = tid; wd < w_first; wd += NT) { sb.vis[wd] = 0u; sb.full[wd] = 0u; }
-  // a load covers 256 entries; a group spans na loads and lg lanes of each
-  const int na = ge > 256 ? (int)(ge >> 8) : 1;
-  const int lg = ge >= 256 ? 64 : (int)(ge >> 2);
-  const int gpl = ge >= 256 ? 1 : (int)(256 >> (31 - __builtin_clz((unsigned)ge)));  // groups per load
-  if (wb < we) {
-    const int64_t e_begin = (int64_t)wb * 32 * ge, e_end = (int64_t)we * 32 * ge;
+  if (lim < 4) {
+    // fewer than 4 entries (one tile, one group): the first lane classifies them
+    if (tid == 0) {
+      int lo = INT32_MAX, hi = INT32_MIN;
+      for (int64_t x = 0; x < lim; ++x) { lo = min(lo, other[x]); hi = max(hi, other[x]); }
+      if (lo <= qmax && hi >= qmin) sb.vis[0] = 1u;
+      if (lo == hi && qmin == qmax && lo == qmin) sb.full[0] = 1u;
+    }
+  } else if (wb < we) {
+    const int64_t tb = (int64_t)wb << (5 + sh), te = min((int64_t)n_tiles, (int64_t)we << (5 + sh));
+    const int gq = sh < 4 ? 4 << sh : 64;   // lanes per group within a batch (16 tiles = 64 lanes)
+    const int nbg = sh > 4 ? 1 << (sh - 4) : 1;  // batches per group
     unsigned vword = 0u, fword = 0u;
-    int bit = 0, wd = wb, ldn = 0;  // next bit of word wd; loads into the current group
-    int lo_acc = INT32_MAX, hi_acc = INT32_MIN;
-    for (int64_t e = e_begin; e < e_end; e += 256 * kLoads) {
-      int lo4[kLoads], hi4[kLoads];
+    int bg = 0, lo_acc = INT32_MAX, hi_acc = INT32_MIN;
+    constexpr int64_t kPass = 16 * kNB;  // tiles per pass
+    // the 16 loads of the pass at tile t0 (windows past lim pulled back to end at it)
+    auto load = [&](i32x4_a4* vv, int64_t t0) {
 #pragma unroll
-      for (int u = 0; u < kLoads; ++u) {
-        const int64_t x = e + 256 * u + 4 * lane;
-        if (x + 4 <= lim) {
-          const i32x4_a4 v = *(const i32x4_a4*)(other + x);
-          lo4[u] = min(min(v[0], v[1]), min(v[2], v[3]));
-          hi4[u] = max(max(v[0], v[1]), max(v[2], v[3]));
+      for (int b = 0; b < kNB; ++b)
+#pragma unroll
+        for (int j = 0; j < kCh; ++j) {
+          const int64_t x = (t0 + 16 * b + q) * BT + 16 * j + 4 * r;
+          vv[b * kCh + j] = *(const i32x4_a4*)(other + (x + 4 <= lim ? x : lim - 4));
+        }
+    };
+    auto process = [&](i32x4_a4* vv, int64_t t0) {
+      // one statement that takes every loaded value of the pass: all 16 loads
+      // are issued before it and waited for once
+      asm volatile("" : "+v"(vv[0]), "+v"(vv[1]), "+v"(vv[2]), "+v"(vv[3]), "+v"(vv[4]), "+v"(vv[5]),
+                   "+v"(vv[6]), "+v"(vv[7]), "+v"(vv[8]), "+v"(vv[9]), "+v"(vv[10]), "+v"(vv[11]),
+                   "+v"(vv[12]), "+v"(vv[13]), "+v"(vv[14]), "+v"(vv[15]));
+#pragma unroll
+      for (int b = 0; b < kNB; ++b) {
+        const int64_t tbat = t0 + 16 * b;
+        if (tbat >= te) break;  // uniform
+        int lo = INT32_MAX, hi = INT32_MIN;
+#pragma unroll
+        for (int j = 0; j < kCh; ++j) {
+          const int64_t x = (tbat + q) * BT + 16 * j + 4 * r;
+          const int64_t d = x + 4 <= lim ? 0 : x - (lim - 4);  // window entries below this lane's own
+          const i32x4_a4 v = vv[b * kCh + j];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            lo = c >= d ? min(lo, v[c]) : lo;
+            hi = c >= d ? max(hi, v[c]) : hi;
+          }
+        }
+        // the quad's tile: lanes l ^ 1 and l ^ 2
+        lo = min(lo, __builtin_amdgcn_mov_dpp(lo, 0xB1, 0xF, 0xF, false));
+        hi = max(hi, __builtin_amdgcn_mov_dpp(hi, 0xB1, 0xF, 0xF, false));
+        lo = min(lo, __builtin_amdgcn_mov_dpp(lo, 0x4E, 0xF, 0xF, false));
+        hi = max(hi, __builtin_amdgcn_mov_dpp(hi, 0x4E, 0xF, 0xF, false));
+        if (sh == 0) {
+          // one tile per bit: the batch's 16 bits from one ballot (all four
+          // lanes of a quad agree), half a map word
+          const bool v_ok = lo <= hi && lo <= qmax && hi >= qmin;
+          const bool f_ok = lo <= hi && lo == hi && qmin == qmax && lo == qmin;
+          const int half = (int)(tbat >> 4) & 1;
+          vword |= pack_quads(__builtin_amdgcn_ballot_w64(v_ok)) << (16 * half);
+          fword |= pack_quads(__builtin_amdgcn_ballot_w64(f_ok)) << (16 * half);
+          if (half == 1 || tbat + 16 >= te) {
+            if (lane == 0) { sb.vis[tbat >> 5] = vword; sb.full[tbat >> 5] = fword; }
+            vword = fword = 0u;
+          }
         } else {
-          lo4[u] = INT32_MAX;
-          hi4[u] = INT32_MIN;
-#pragma unroll
-          for (int c = 0; c < 4; ++c)
-            if (x + c < lim) { const int s = other[x + c]; lo4[u] = min(lo4[u], s); hi4[u] = max(hi4[u], s); }
+          // groups of 2^sh tiles: gq lanes of this batch (and nbg batches)
+          group_minmax(lo, hi, gq);
+          lo_acc = min(lo_acc, lo);
+          hi_acc = max(hi_acc, hi);
+          if (++bg < nbg && tbat + 16 < te) continue;  // the range's last group may be cut short
+          bg = 0;
+          lo = lo_acc;
+          hi = hi_acc;
+          lo_acc = INT32_MAX;
+          hi_acc = INT32_MIN;
+          if ((lane & (gq - 1)) == 0 && lo <= hi) {
+            const int gi = (int)((tbat + q) >> sh);
+            if (lo <= qmax && hi >= qmin) atomicOr(&sb.vis[gi >> 5], 1u << (gi & 31));
+            if (lo == hi && qmin == qmax && lo == qmin) atomicOr(&sb.full[gi >> 5], 1u << (gi & 31));
+          }
         }
       }
-#pragma unroll
-      for (int u = 0; u < kLoads; ++u) {
-        if (e + 256 * u >= e_end) break;  // uniform
-        lo_acc = min(lo_acc, lo4[u]);
-        hi_acc = max(hi_acc, hi4[u]);
-        if (++ldn < na) continue;
-        ldn = 0;
-        int lo = lo_acc, hi = hi_acc;
-        lo_acc = INT32_MAX;
-        hi_acc = INT32_MIN;
-        group_minmax(lo, hi, lg);
-        const bool v_ok = lo <= hi && lo <= qmax && hi >= qmin;
-        const bool f_ok = lo <= hi && lo == hi && qmin == qmax && lo == qmin;
-        const uint64_t vm = __builtin_amdgcn_ballot_w64(v_ok), fm = __builtin_amdgcn_ballot_w64(f_ok);
-        // group j of this load sits at lanes j lg ..; gpl divides 32, so the
-        // load's groups fall in one map word
-        unsigned vf = 0u, ff = 0u;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const unsigned on = j < gpl ? 1u : 0u;
-          vf |= ((unsigned)(vm >> (j * lg)) & on) << j;
-          ff |= ((unsigned)(fm >> (j * lg)) & on) << j;
-        }
-        vword |= vf << bit;
-        fword |= ff << bit;
-        bit += gpl;
-        if (bit == 32) {
-          if (lane == 0) { sb.vis[wd] = vword; sb.full[wd] = fword; }
-          vword = fword = 0u;
-          bit = 0;
-          ++wd;
-        }
-      }
+    };
+    i32x4_a4 vv[16];
+    for (int64_t t0 = tb; t0 < te; t0 += kPass) {
+      load(vv, t0);
+      process(vv, t0);
     }
   }
   __syncthreads();
@@ -344,6 +391,14 @@ __device__ void seg_scan(SegBits& sb, int sh, const FwdParams& p, const Work& w,
                            p.Lk, n_tiles);
 }
 
+// The map word holding group g, in a scalar register: the tile index derived
+// from it then feeds scalar address arithmetic (the tile copies take their
+// buffer resource from SGPRs written by scalar instructions, never straight
+// from a VALU write, which a copy would have to trail by 5 wait states).
+__device__ __forceinline__ unsigned map_word(const unsigned* bits, int g) {
+  return __builtin_amdgcn_readfirstlane(bits[g >> 5]);
+}
+
 // First tile >= t of a visible group (n_tiles if none): t itself when its
 // group is visible, else the first tile of the next visible group.
 __device__ __forceinline__ int seg_next(const SegBits& sb, int sh, int t, int n_tiles) {
@@ -351,7 +406,7 @@ __device__ __forceinline__ int seg_next(const SegBits& sb, int sh, int t, int n_
   const int g0 = t >> sh, ng = ((n_tiles - 1) >> sh) + 1;
   int g = g0;
   while (g < ng) {
-    const unsigned m = sb.vis[g >> 5] >> (g & 31);
+    const unsigned m = map_word(sb.vis, g) >> (g & 31);
     if (m) {
       const int r = g + __builtin_ctz(m);
       if (r >= ng) return n_tiles;
@@ -369,7 +424,7 @@ __device__ __forceinline__ int seg_prev(const SegBits& sb, int sh, int t, int lo
   const int g0 = t >> sh, glo = lo >> sh;
   int g = g0;
   while (g >= glo) {
-    const unsigned m = sb.vis[g >> 5] << (31 - (g & 31));
+    const unsigned m = map_word(sb.vis, g) << (31 - (g & 31));
     if (m) {
       const int r = g - __builtin_clz(m);
       if (r < glo) return lo - 1;
@@ -378,6 +433,37 @@ __device__ __forceinline__ int seg_prev(const SegBits& sb, int sh, int t, int lo
     g = (g & ~31) - 1;
   }
   return lo - 1;
+}
+
+// First group in [g, ng) whose bit in `bits` is `val` (ng if none).
+__device__ __forceinline__ int seg_find(const unsigned* bits, int g, int ng, bool val) {
+  while (g < ng) {
+    unsigned w = map_word(bits, g);
+    if (!val) w = ~w;
+    w >>= (g & 31);
+    if (w) {
+      const int r = g + __builtin_ctz(w);
+      return r < ng ? r : ng;
+    }
+    g = (g | 31) + 1;
+  }
+  return ng;
+}
+
+// The first run of set bits of a map (vis or full) at or after tile t, in
+// tiles: [lo, hi), lo >= t; lo = hi = n_tiles if there is none. A kernel that
+// visits tiles in increasing order keeps the run and reads the map again only
+// once it has passed the run's end.
+__device__ __forceinline__ void seg_run(const unsigned* bits, int sh, int t, int n_tiles, int& lo, int& hi) {
+  const int ng = ((n_tiles - 1) >> sh) + 1;
+  const int gs = seg_find(bits, t >> sh, ng, true);
+  if (gs >= ng) {
+    lo = hi = n_tiles;
+    return;
+  }
+  const int gz = seg_find(bits, gs, ng, false);
+  lo = max(t, gs << sh);
+  hi = min(n_tiles, gz << sh);
 }
 
 // Is every key of tile t's group of the workgroup's single query id?

@@ -168,9 +168,22 @@ __global__ __launch_bounds__(W * 64) void fwd_f32_kernel(FwdParams p) {
   ln.init(wave, lane);
   const uint32_t kbase = lds_addr(sm.k[0]), vbase = lds_addr(sm.v[0]), sbase = lds_addr(sm.segk[0]);
 
+  // the first visible tile after t (t_hi if none) and the segment state
+  // (full: no id mask) of tile t; both are asked in increasing t, and the map
+  // is read only past the end of the run found last
+  int vr_lo = 0, vr_hi = 0, fr_lo = 0, fr_hi = 0;
   auto next_tile = [&](int t) -> int {
-    if (t >= t_hi) return t_hi;
-    return seg ? seg_next(sm.bits, sh, t + 1, t_hi) : t + 1;
+    const int u = t + 1;
+    if (u >= t_hi) return t_hi;
+    if (!seg) return u;
+    if (u >= vr_hi) seg_run(sm.bits.vis, sh, u, t_hi, vr_lo, vr_hi);
+    return max(u, vr_lo);
+  };
+  auto is_full = [&](int t) -> bool {
+    if (!seg) return true;
+    if (t >= t_hi) return false;
+    if (t >= fr_hi) seg_run(sm.bits.full, sh, t, t_hi, fr_lo, fr_hi);
+    return t >= fr_lo;
   };
   auto k_copy = [&](int st, int t) {
     return part_copy_f(kbase + (uint32_t)st * kTileBytesF, sbase + (uint32_t)st * (2 * kBkF * 4), kb, skb, t,
@@ -180,9 +193,8 @@ __global__ __launch_bounds__(W * 64) void fwd_f32_kernel(FwdParams p) {
     return part_copy_f(vbase + (uint32_t)st * kTileBytesF, 0u, vb, nullptr, t, t < t_hi, p.Lk);
   };
   // element mask of tile t's scores (its ids in K stage st), where the tile needs one
-  auto mask_if_needed = [&](f32x16& s, int t, int st) {
+  auto mask_if_needed = [&](f32x16& s, int t, bool seg_full, int st) {
     const int64_t k0 = (int64_t)t * kBkF;
-    const bool seg_full = !seg || seg_full_tile(sm.bits, sh, t);
     if (seg_full && k0 + kBkF <= p.Lk && !(p.causal && k0 + kBkF - 1 > p.q_offset + pw)) return;
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
@@ -213,9 +225,11 @@ __global__ __launch_bounds__(W * 64) void fwd_f32_kernel(FwdParams p) {
     }
   };
 
-  int cur = seg ? seg_next(sm.bits, sh, t_lo, t_hi) : t_lo;
+  int cur = next_tile(t_lo - 1);
   if (cur < t_hi) {
     int nxt = next_tile(cur), nn = next_tile(nxt);
+    const bool f_cur = is_full(cur);
+    bool f_nxt = is_full(nxt), f_nn = is_full(nn);
     // K(#0), K(#1) and V(#0) into stages 0, 1 and 0 (V(#1) is copied in step 0)
     {
       const PartCopyF k0 = k_copy(0, cur), k1 = k_copy(1, nxt), v0 = v_copy(0, cur);
@@ -225,10 +239,8 @@ __global__ __launch_bounds__(W * 64) void fwd_f32_kernel(FwdParams p) {
         k1.row(it, wave, ln.ldk[it & 3]);
         v0.row(it, wave, ln.ldv[it & 1]);
       }
-      if (seg) {
-        k0.ids(wave, lane);
-        k1.ids(wave, lane);
-      }
+      if (!f_cur) k0.ids(wave, lane);
+      if (!f_nxt) k1.ids(wave, lane);
     }
     wait_vm0();
     __syncthreads();
@@ -242,7 +254,7 @@ __global__ __launch_bounds__(W * 64) void fwd_f32_kernel(FwdParams p) {
         for (int e = 0; e < 4; ++e) s_cur = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], qf[c][e], s_cur, 0, 0, 0);
       }
     }
-    mask_if_needed(s_cur, cur, 0);
+    mask_if_needed(s_cur, cur, f_cur, 0);
     {
       float mx = s_cur[0];
 #pragma unroll
@@ -255,6 +267,7 @@ __global__ __launch_bounds__(W * 64) void fwd_f32_kernel(FwdParams p) {
       wait_vm0();       // K(nxt) and V(cur), copied last step, have landed
       __syncthreads();  // ... for every wave; K stage st and V stage st1 are free
       const int n3 = next_tile(nn);
+      const bool f3 = is_full(n3);
       const PartCopyF kc = k_copy(st, nn);   // K(#i+2) into K(#i)'s stage
       const PartCopyF vc = v_copy(st1, nxt);  // V(#i+1) into V(#i-1)'s stage
       const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
@@ -283,7 +296,7 @@ __global__ __launch_bounds__(W * 64) void fwd_f32_kernel(FwdParams p) {
           }
           if ((c & 3) == 1) kc.row(c >> 2, wave, ln.ldk[(c >> 2) & 3]);
           if ((c & 3) == 3) vc.row(c >> 2, wave, ln.ldv[(c >> 2) & 1]);
-          if (c == 2 && seg) kc.ids(wave, lane);
+          if (c == 2 && !f_nn) kc.ids(wave, lane);  // the tile needs its key ids
           GQA_SEGMENT_END_F();
         }
       }
@@ -292,7 +305,7 @@ __global__ __launch_bounds__(W * 64) void fwd_f32_kernel(FwdParams p) {
       // phase B: O^T += V^T P^T from V stage st (MFMA tt contracts key
       // 8 (tt / 4) + 4 g + tt % 4, P register tt; the 8 V values of key step
       // tt are read one step ahead), with the mask and row max of s_nxt
-      mask_if_needed(s_nxt, nxt, st1);
+      mask_if_needed(s_nxt, nxt, f_nxt, st1);
       float mx = -INFINITY;
       {
         const char* Vs = sm.v[st];
@@ -322,6 +335,8 @@ __global__ __launch_bounds__(W * 64) void fwd_f32_kernel(FwdParams p) {
       cur = nxt;
       nxt = nn;
       nn = n3;
+      f_nxt = f_nn;
+      f_nn = f3;
     }
   }
 

@@ -275,7 +275,7 @@ __device__ __forceinline__ void phase_a(int kst, typename Elem<E>::v8* qf, const
     ep.slot(q, s_cur, sl2, m_use, pk);
     if ((q & 3) == 1) kc.rows(ln.ldk, q >> 2, wave);
     if ((q & 3) == 3) vc.rows(ln.ldv, q >> 2, wave);
-    if (q == 2 && seg) kc.ids(wave, lane);
+    if (q == 2 && seg) kc.ids(wave, lane);  // seg: the tile needs its key ids (not full)
     if (q >= 32 - kVPre) vf[q - (32 - kVPre)] = v_frag<V8>(q - (32 - kVPre), 0, vb);
     GQA_SEGMENT_END();
   }
@@ -339,13 +339,31 @@ struct H16Wave {
   int wave, lane, g, sq, n_tiles;
   int sh;  // log2 of the key tiles per segment-map group
   int cur, nxt, nn;  // visible tiles: being finished, QK this step, next after that
+  bool f_nxt, f_nn;  // their segment state: every key of the workgroup's one query id (no id mask)
+  int vr_lo, vr_hi;  // the run of visible tiles at or after the last lookup
+  int fr_lo, fr_hi;  // the run of full tiles at or after the last lookup
 
   __device__ __forceinline__ H16Wave(const FwdParams& p_, SmemB& sm_) : p(p_), sm(sm_) {}
 
-  __device__ __forceinline__ int next_tile(int t) const {
-    if (t >= n_tiles) return n_tiles;
-    if constexpr (SEG) return seg_next(sm.bits, sh, t + 1, n_tiles);
-    return t + 1;
+  // The first visible tile after t (n_tiles if none). Calls come in increasing
+  // t; the map is read only past the end of the current run.
+  __device__ __forceinline__ int next_tile(int t) {
+    const int u = t + 1;
+    if (u >= n_tiles) return n_tiles;
+    if constexpr (SEG) {
+      if (u >= vr_hi) seg_run(sm.bits.vis, sh, u, n_tiles, vr_lo, vr_hi);
+      return max(u, vr_lo);
+    }
+    return u;
+  }
+  // Is tile t full (no id mask needed)? Calls come in increasing t.
+  __device__ __forceinline__ bool is_full(int t) {
+    if constexpr (SEG) {
+      if (t >= n_tiles) return false;
+      if (t >= fr_hi) seg_run(sm.bits.full, sh, t, n_tiles, fr_lo, fr_hi);
+      return t >= fr_lo;
+    }
+    return true;
   }
   __device__ __forceinline__ PartCopy k_copy(int st, int t) const {
     return part_copy(rb.k + (uint32_t)st * kTileBytesB, rb.s + (uint32_t)st * (kBkB * 4), kb, SEG ? skb : nullptr,
@@ -354,15 +372,12 @@ struct H16Wave {
   __device__ __forceinline__ PartCopy v_copy(int st, int t) const {
     return part_copy(rb.v + (uint32_t)st * kTileBytesB, 0u, vb, nullptr, t, t < n_tiles, p.Lk);
   }
-  __device__ __forceinline__ bool full_bit(int t) const {
-    return SEG && t < n_tiles && seg_full_tile(sm.bits, sh, t);
-  }
   // Masks the 32 scores per lane of tile t (s[16 j + r]: element r of key
-  // half j) where some key of the tile is hidden from some row of the wave;
-  // returns whether it did.
-  __device__ __forceinline__ bool mask_if_needed(float* s, int t, int st) {
+  // half j; `full`: its segment state) where some key of the tile is hidden
+  // from some row of the wave; returns whether it did.
+  __device__ __forceinline__ bool mask_if_needed(float* s, int t, bool full, int st) {
     const int64_t k0 = (int64_t)t * kBkB;
-    const bool seg_elem = SEG && !full_bit(t);
+    const bool seg_elem = SEG && !full;
     if (seg_elem || k0 + kBkB > p.Lk || (p.causal && k0 + kBkB - 1 > p.q_offset + pw)) {
 #pragma unroll
       for (int j = 0; j < 2; ++j)
@@ -413,7 +428,7 @@ struct H16Wave {
     // u == 18 is folded, and the loop would stay rolled
 #pragma unroll
     for (int u = 0; u < 19; ++u) product(u);
-    if (mask_if_needed(sn, nxt, kst1)) mx = lane_max(sn);
+    if (mask_if_needed(sn, nxt, f_nxt, kst1)) mx = lane_max(sn);
 #pragma unroll
     for (int u = 19; u < 32; ++u) product(u);
     rs.l += ep.lsum;
@@ -431,6 +446,7 @@ struct H16Wave {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // K(nxt) and V(cur), copied last step, have landed
     __syncthreads();                                    // ... for every wave; K stage st and V stage st1 are free
     const int n3 = next_tile(nn);
+    const bool f3 = is_full(n3);
     const PartCopy kc = k_copy(st, nn);   // K(#i+2) into K(#i)'s stage
     const PartCopy vc = v_copy(st1, nxt);  // V(#i+1) into V(#i-1)'s stage
     unsigned pk[16];
@@ -440,7 +456,8 @@ struct H16Wave {
 #pragma unroll
     for (int j = 0; j < 4; ++j) vbs[j] = ln.v[j] + st * kTileBytesB;
     V8 vf[kVPre];
-    phase_a<E>(st1, qf, ln, s_nxt, s_cur, p.scale_log2, rs.m_use, pk, ep, kc, vc, SEG, wave, lane, vbs, vf);
+    phase_a<E>(st1, qf, ln, s_nxt, s_cur, p.scale_log2, rs.m_use, pk, ep, kc, vc, SEG && !f_nn, wave, lane, vbs,
+               vf);
     float sn[32];
     const float alpha = phase_b(st1, s_nxt, pk, ep, vbs, vf, sn);
     rescale(acc, rs, alpha);
@@ -449,6 +466,8 @@ struct H16Wave {
     cur = nxt;
     nxt = nn;
     nn = n3;
+    f_nxt = f_nn;
+    f_nn = f3;
   }
 };
 
@@ -471,6 +490,15 @@ __global__ __launch_bounds__(kWavesB * 64) void fwd_h16_kernel(FwdParams p) {
   const int64_t kv_end = p.causal ? min(p.Lk, p.q_offset + p_end) : p.Lk;
   wv.n_tiles = (int)((kv_end + kBkB - 1) / kBkB);
 
+  // Q of the lane's row, B-operand layout: Q[row][16 c + 8 g .. + 7] (loads
+  // issued here, first, so that their latency passes during the segment scan)
+  const int64_t hq = ((int64_t)w.b * p.Hq + h) * p.Lq;
+  {
+    const V8* qr = (const V8*)((const char*)p.q + (hq + row_c) * kD * 2);
+#pragma unroll
+    for (int c = 0; c < 16; ++c) wv.qf[c] = qr[2 * c + wv.g];
+  }
+
   wv.sh = SEG ? seg_shift(wv.n_tiles) : 0;
   if (SEG) seg_scan<kWavesB, kBkB>(sm.bits, wv.sh, p, w, wv.n_tiles);
   // tiles [t_lo, n_tiles): all of them, or this workgroup's key split (tiles
@@ -486,16 +514,6 @@ __global__ __launch_bounds__(kWavesB * 64) void fwd_h16_kernel(FwdParams p) {
   wv.sq = SEG ? p.seg_q[(int64_t)w.b * p.Lq + row_c] : 0;
   wv.lim = p.q_offset + row;  // last key this row may see (causal)
 
-  // Q in registers, B-operand layout: lane holds Q[row][16 c + 8 g .. + 7].
-  const int64_t hq = ((int64_t)w.b * p.Hq + h) * p.Lq;
-  {
-    const V8* qr = (const V8*)((const char*)p.q + (hq + row_c) * kD * 2);
-#pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      wv.qf[c] = qr[2 * c + wv.g];
-      asm volatile("" : "+a"(wv.qf[c]));
-    }
-  }
 #pragma unroll
   for (int n = 0; n < 8; ++n) {
     wv.acc[n] = f32x16{};
@@ -505,10 +523,14 @@ __global__ __launch_bounds__(kWavesB * 64) void fwd_h16_kernel(FwdParams p) {
   wv.ln.init(wv.wave, wv.lane, (lds_cchar*)sm.k[0], (lds_cchar*)sm.v[0]);
   wv.rb = RingBase{lds_addr(sm.k[0]), lds_addr(sm.v[0]), lds_addr(sm.segk[0])};
 
-  wv.cur = SEG ? seg_next(sm.bits, wv.sh, t_lo, wv.n_tiles) : t_lo;
+  wv.vr_lo = wv.vr_hi = wv.fr_lo = wv.fr_hi = 0;
+  wv.cur = wv.next_tile(t_lo - 1);
   if (wv.cur < wv.n_tiles) {
     wv.nxt = wv.next_tile(wv.cur);
     wv.nn = wv.next_tile(wv.nxt);
+    const bool f_cur = wv.is_full(wv.cur);
+    wv.f_nxt = wv.is_full(wv.nxt);
+    wv.f_nn = wv.is_full(wv.nn);
     // K(#0), K(#1) and V(#0) into stages 0, 1 and 0 (V(#1) is copied in step 0)
     const PartCopy k0 = wv.k_copy(0, wv.cur), k1 = wv.k_copy(1, wv.nxt), v0 = wv.v_copy(0, wv.cur);
 #pragma unroll
@@ -518,9 +540,16 @@ __global__ __launch_bounds__(kWavesB * 64) void fwd_h16_kernel(FwdParams p) {
       v0.rows(wv.ln.ldv, it, wv.wave);
     }
     if (SEG) {
-      k0.ids(wv.wave, wv.lane);
-      k1.ids(wv.wave, wv.lane);
+      if (!f_cur) k0.ids(wv.wave, wv.lane);
+      if (!wv.f_nxt) k1.ids(wv.wave, wv.lane);
     }
+    // Q pinned in AGPRs (its 16 loads went out before the segment scan and the
+    // tile copies; one statement takes them all, so they are waited for once,
+    // together with the copies)
+    asm volatile("" : "+a"(wv.qf[0]), "+a"(wv.qf[1]), "+a"(wv.qf[2]), "+a"(wv.qf[3]), "+a"(wv.qf[4]),
+                 "+a"(wv.qf[5]), "+a"(wv.qf[6]), "+a"(wv.qf[7]), "+a"(wv.qf[8]), "+a"(wv.qf[9]),
+                 "+a"(wv.qf[10]), "+a"(wv.qf[11]), "+a"(wv.qf[12]), "+a"(wv.qf[13]), "+a"(wv.qf[14]),
+                 "+a"(wv.qf[15]));
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     f32x16 s0[2];
@@ -533,7 +562,7 @@ __global__ __launch_bounds__(kWavesB * 64) void fwd_h16_kernel(FwdParams p) {
       sc[r] = s0[r >> 4][r & 15];
       asm volatile("" : "+v"(sc[r]));
     }
-    wv.mask_if_needed(sc, wv.cur, 0);
+    wv.mask_if_needed(sc, wv.cur, f_cur, 0);
     (void)lazy_max_update(xor32_max(lane_max(sc)), wv.rs, p.scale_log2);  // nothing accumulated yet: no rescale
 #pragma unroll
     for (int r = 0; r < 32; ++r) wv.s_cur[r] = sc[r];

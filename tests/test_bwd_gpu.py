@@ -118,6 +118,16 @@ def test_bwd_random_segments_empty_rows(dtype, causal):
 
 
 @pytest.mark.parametrize("dtype", BWD_DTYPES)
+@pytest.mark.parametrize("L", [1, 2, 3, 5])
+def test_bwd_tiny_with_segments(dtype, L):
+    """Fewer id entries than one 16-byte load: the id scan's small-array path."""
+    x = synth.gqa(1, 16, 4, L, seed=60 + L, dtype=dtype)
+    ids = np.array([[0, 0, 1, 1, 1][:L]], dtype=np.int32)
+    x.seg_q = x.seg_k = ids
+    check_bwd(x, "bwd L%d with ids %s" % (L, dtype))
+
+
+@pytest.mark.parametrize("dtype", BWD_DTYPES)
 def test_bwd_deterministic(dtype):
     x = synth.gqa(1, 16, 4, 700, seed=160, dtype=dtype)
     g = synth.Grad(x.q.shape, seed=161, dtype=dtype)

@@ -107,6 +107,19 @@ def test_unsorted_segments_and_empty_rows(dtype):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("L", [1, 2, 3, 5])
+def test_tiny_with_segments(dtype, L):
+    """Fewer id entries than one 16-byte load (the id scan's small-array path),
+    causal and not, with a query id that no key has."""
+    for causal in (True, False):
+        x = synth.gqa(1, 16, 4, L, seed=50 + L, dtype=dtype, causal=causal)
+        x.seg_k = np.array([[0, 0, 1, 1, 1][:L]], dtype=np.int32)
+        x.seg_q = x.seg_k.copy()
+        x.seg_q[0, 0] = 7
+        check(x, "L%d with ids %s causal=%s" % (L, dtype, causal))
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("causal", [True, False])
 def test_packed_segments_equal_per_segment_calls(dtype, causal):
     """Packed segments with ids give, row for row, what each segment gives as
