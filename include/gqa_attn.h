@@ -35,8 +35,10 @@
  * 202, "The change": bf16 and fp16 calls keep the fused kernels).
  *
  * Ownership and threading. The caller allocates every buffer. The library
- * allocates no device memory, keeps no pointer after returning and never
- * synchronises: work is enqueued on `stream` (a hipStream_t; NULL is the
+ * allocates no device memory (its code object holds one static array of
+ * GQA_NOALLOC_SCRATCH_BYTES per GPU, used only by gqa_attn_fwd_split_noalloc,
+ * placed by the HIP runtime when the code object loads), keeps no pointer
+ * after returning and never synchronises: work is enqueued on `stream` (a hipStream_t; NULL is the
  * default stream) and outputs are valid once the stream reaches that point.
  * Every element of o and lse is written. o must not overlap q, k or v.
  * Calls are reentrant and deterministic (same inputs give the same bits).
@@ -154,6 +156,29 @@ int gqa_attn_fwd_split(const void* q, const void* k, const void* v, void* o, flo
                        int64_t q_offset, const int32_t* seg_q, const int32_t* seg_k,
                        int causal, int dtype, int n_split, void* workspace, int64_t workspace_bytes,
                        void* stream);
+
+/*
+ * Split-KV forward that allocates nothing and takes no workspace: for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc). Same operation, arguments
+ * and result as gqa_attn_fwd_split with the same n_split (the same kernels on
+ * the same split), but the partial results go to a static device array of
+ * GQA_NOALLOC_SCRATCH_BYTES that the library's code object holds on each GPU
+ * it runs on, placed by the HIP runtime when the code object loads there and
+ * kept until the process ends. The call itself makes no allocation.
+ * n_split: 0 picks gqa_attn_split_count()'s count, lowered to what the array
+ * holds; 1 .. 1024 as in gqa_attn_fwd_split, and GQA_ERR_WORKSPACE when
+ * n_split * B * Hq * Lq * (D + 1) * 4 bytes of partials exceed the array
+ * (checked before any HIP call; nothing is enqueued). Every call on one GPU
+ * uses that GPU's single array: calls whose work overlaps in time on one GPU
+ * (other streams, other host threads) race and must be ordered by the caller.
+ * GQA_ERR_LAUNCH also when the runtime cannot report the array's address.
+ */
+#define GQA_NOALLOC_SCRATCH_BYTES (64ll << 20)
+int gqa_attn_fwd_split_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                               int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
+                               int64_t q_offset, const int32_t* seg_q, const int32_t* seg_k,
+                               int causal, int dtype, int n_split, void* stream);
 
 /* Bytes of workspace gqa_attn_fwd_split needs for n_split ranges:
  * n_split * B * Hq * Lq * (D + 1) * 4. Returns 0 for invalid arguments. */

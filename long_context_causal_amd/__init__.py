@@ -18,8 +18,9 @@ LIB_PATH = os.path.join(_HERE, "libgqa_attn.so")
 GQA_F32, GQA_BF16, GQA_F16 = 0, 1, 2
 STATUS = {0: "GQA_OK", 1: "GQA_ERR_NULL", 2: "GQA_ERR_SHAPE", 3: "GQA_ERR_UNSUPPORTED",
           4: "GQA_ERR_ALIGN", 5: "GQA_ERR_LAUNCH", 6: "GQA_ERR_ALIAS", 7: "GQA_ERR_WORKSPACE"}
-EXPORTS = ("gqa_attn_fwd", "gqa_attn_merge", "gqa_attn_bwd", "gqa_attn_fwd_split", "gqa_attn_split_workspace",
-           "gqa_attn_split_count", "gqa_attn_strerror", "gqa_attn_version")
+EXPORTS = ("gqa_attn_fwd", "gqa_attn_merge", "gqa_attn_bwd", "gqa_attn_fwd_split", "gqa_attn_fwd_split_noalloc",
+           "gqa_attn_split_workspace", "gqa_attn_split_count", "gqa_attn_strerror", "gqa_attn_version")
+NOALLOC_SCRATCH_BYTES = 64 << 20  # GQA_NOALLOC_SCRATCH_BYTES
 
 _lib = None
 
@@ -48,6 +49,9 @@ def load_library():
         lib.gqa_attn_fwd_split.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i64, i64, i64, p, p, c_int, c_int,
                                            c_int, p, i64, p]
         lib.gqa_attn_fwd_split.restype = c_int
+        lib.gqa_attn_fwd_split_noalloc.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i64, i64, i64, p, p, c_int,
+                                                   c_int, c_int, p]
+        lib.gqa_attn_fwd_split_noalloc.restype = c_int
         lib.gqa_attn_split_workspace.argtypes = [i64, i64, i64, i64, c_int]
         lib.gqa_attn_split_workspace.restype = i64
         lib.gqa_attn_split_count.argtypes = [i64, i64, i64, i64, i64, c_int]
@@ -88,6 +92,13 @@ def fwd_split_raw(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, D, q_offset, seg_q, seg_k
     return load_library().gqa_attn_fwd_split(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, D, q_offset, seg_q, seg_k,
                                              int(causal), int(dtype), int(n_split), workspace, workspace_bytes,
                                              stream)
+
+
+def fwd_split_noalloc_raw(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, D, q_offset, seg_q, seg_k, causal, dtype, n_split,
+                          stream) -> int:
+    """Direct call of gqa_attn_fwd_split_noalloc with integer pointers; returns the status code."""
+    return load_library().gqa_attn_fwd_split_noalloc(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, D, q_offset, seg_q, seg_k,
+                                                     int(causal), int(dtype), int(n_split), stream)
 
 
 def split_workspace(B, Hq, Lq, D, n_split) -> int:
@@ -273,6 +284,40 @@ def fwd_split(q, k, v, *, causal=True, q_offset=0, seg_q=None, seg_k=None, n_spl
                        Lk, D, int(q_offset), None if seg_q is None else seg_q.data_ptr(),
                        None if seg_k is None else seg_k.data_ptr(), causal, dt, n_split, workspace.data_ptr(),
                        workspace.numel() * workspace.element_size(), _stream_ptr(stream))
+    if rc != 0:
+        raise GqaError(rc, strerror(rc))
+    return out, lse
+
+
+def fwd_split_noalloc(q, k, v, out, lse, *, causal=True, q_offset=0, seg_q=None, seg_k=None, n_split=0,
+                      stream=None):
+    """Split-KV forward through the allocation-free entry point: the partial
+    results use the library's static per-GPU scratch, so neither the call nor
+    this binding allocates (out and lse are the caller's). n_split = 0 takes
+    the library's count that fits the scratch. Calls overlapping on one GPU race."""
+    import torch
+    _check_dev(q, k, v, seg_q, seg_k, out, lse)
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("q must be [B,Hq,Lq,D] and k, v [B,Hkv,Lk,D]")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k and v must share a dtype")
+    B, Hq, Lq, D = q.shape
+    Hkv, Lk = k.shape[1], k.shape[2]
+    if k.shape[0] != B or k.shape[3] != D:
+        raise ValueError("q and k/v disagree in batch or head size")
+    if (seg_q is None) != (seg_k is None):
+        raise ValueError("give both segment-id tensors or neither")
+    if seg_q is not None:
+        if seg_q.dtype != torch.int32 or seg_k.dtype != torch.int32:
+            raise TypeError("segment ids must be int32")
+        if seg_q.numel() != B * Lq or seg_k.numel() != B * Lk:
+            raise ValueError("segment ids must be [B,Lq] and [B,Lk]")
+    if out.shape != q.shape or out.dtype != q.dtype or lse.shape != (B, Hq, Lq) or lse.dtype != torch.float32:
+        raise ValueError("out must match q and lse must be [B,Hq,Lq] float32")
+    rc = fwd_split_noalloc_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Hq,
+                               Hkv, Lq, Lk, D, int(q_offset), None if seg_q is None else seg_q.data_ptr(),
+                               None if seg_k is None else seg_k.data_ptr(), causal, _dtype_code(q), n_split,
+                               _stream_ptr(stream))
     if rc != 0:
         raise GqaError(rc, strerror(rc))
     return out, lse

@@ -6,6 +6,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "merge.hpp"
@@ -126,20 +128,12 @@ GQA_API int64_t gqa_attn_split_workspace(int64_t B, int64_t Hq, int64_t Lq, int6
   return (int64_t)n_split * B * Hq * Lq * (D + 1) * 4;
 }
 
-GQA_API int gqa_attn_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
-                                  int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
-                                  int64_t q_offset, const int32_t* seg_q, const int32_t* seg_k,
-                                  int causal, int dtype, int n_split, void* workspace, int64_t workspace_bytes,
-                                  void* stream) {
-  gqa::FwdParams p{};
-  const int rc = fwd_plan(p, q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, D, q_offset, seg_q, seg_k, causal, dtype);
-  if (rc != GQA_OK) return rc;
-  if (n_split < 1 || n_split > kMaxSplits) return GQA_ERR_UNSUPPORTED;
-  int split_tiles, n_eff;
-  split_shape(Lk, dtype, n_split, &split_tiles, &n_eff);
-  hipStream_t s = (hipStream_t)stream;
-  (void)hipGetLastError();
-  if (n_eff <= 1) return launch_fwd(p, dtype, s) == hipSuccess ? GQA_OK : GQA_ERR_LAUNCH;
+// The split-KV launch pair on a workspace that the caller (gqa_attn_fwd_split)
+// or the library (gqa_attn_fwd_split_noalloc) provides. `p` is a checked plan.
+static int fwd_split_run(gqa::FwdParams& p, const void* q, const void* k, const void* v, void* o, float* lse,
+                         int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
+                         const int32_t* seg_q, const int32_t* seg_k, int dtype, int split_tiles, int n_eff,
+                         void* workspace, int64_t workspace_bytes, hipStream_t s) {
   // workspace: fp32 partial O [n_eff][rows][D], then lse parts [n_eff][rows]
   const int64_t rows = B * Hq * Lq;
   const int64_t need = (int64_t)n_eff * rows * (D + 1) * 4;
@@ -157,6 +151,7 @@ GQA_API int gqa_attn_fwd_split(const void* q, const void* k, const void* v, void
   p.split_tiles = split_tiles;
   p.o_part = (float*)workspace;
   p.lse_part = (float*)workspace + n_eff * rows * D;
+  (void)hipGetLastError();
   if (launch_fwd(p, dtype, s) != hipSuccess) return GQA_ERR_LAUNCH;
   const dim3 grid((unsigned)rows);  // one workgroup per row (rows < 2^31, checked above)
   if (dtype == GQA_F32)
@@ -169,6 +164,90 @@ GQA_API int gqa_attn_fwd_split(const void* q, const void* k, const void* v, void
     hipLaunchKernelGGL(gqa::merge_splits_kernel<_Float16>, grid, dim3(256), 0, s, p.o_part, p.lse_part, n_eff,
                        (_Float16*)o, lse, rows);
   return hipGetLastError() == hipSuccess ? GQA_OK : GQA_ERR_LAUNCH;
+}
+
+GQA_API int gqa_attn_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
+                                  int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
+                                  int64_t q_offset, const int32_t* seg_q, const int32_t* seg_k,
+                                  int causal, int dtype, int n_split, void* workspace, int64_t workspace_bytes,
+                                  void* stream) {
+  gqa::FwdParams p{};
+  const int rc = fwd_plan(p, q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, D, q_offset, seg_q, seg_k, causal, dtype);
+  if (rc != GQA_OK) return rc;
+  if (n_split < 1 || n_split > kMaxSplits) return GQA_ERR_UNSUPPORTED;
+  int split_tiles, n_eff;
+  split_shape(Lk, dtype, n_split, &split_tiles, &n_eff);
+  hipStream_t s = (hipStream_t)stream;
+  if (n_eff <= 1) {
+    (void)hipGetLastError();
+    return launch_fwd(p, dtype, s) == hipSuccess ? GQA_OK : GQA_ERR_LAUNCH;
+  }
+  return fwd_split_run(p, q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, D, seg_q, seg_k, dtype, split_tiles, n_eff, workspace,
+                       workspace_bytes, s);
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free split-KV forward. Its partial results live in `scratch`, a
+// file-scope device array: every GPU the library runs on holds one copy (the
+// runtime places it when the code object loads on that device) until the
+// process ends. Host code never uses the array's name as an address (on the
+// host it names a stand-in): the device address of each GPU's copy comes from
+// hipGetSymbolAddress, taken once per device with that device current, and
+// is passed to the kernels like the caller's workspace in gqa_attn_fwd_split.
+// All calls on one GPU share its copy, so calls that overlap in time on one
+// GPU race; nothing in it needs to start at zero.
+// ---------------------------------------------------------------------------
+namespace {
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kScratchDevices];  // device address of `scratch` per device (null until taken)
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[GQA_NOALLOC_SCRATCH_BYTES];
+
+// Device address of the current device's copy of `scratch` (taken on the first
+// call on that device).
+static int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices) return GQA_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return GQA_ERR_LAUNCH;
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return GQA_OK;
+}
+
+GQA_API int gqa_attn_fwd_split_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                                       int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
+                                       int64_t q_offset, const int32_t* seg_q, const int32_t* seg_k,
+                                       int causal, int dtype, int n_split, void* stream) {
+  gqa::FwdParams p{};
+  const int rc = fwd_plan(p, q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, D, q_offset, seg_q, seg_k, causal, dtype);
+  if (rc != GQA_OK) return rc;
+  if (n_split < 0 || n_split > kMaxSplits) return GQA_ERR_UNSUPPORTED;
+  const int64_t row_bytes = B * Hq * Lq * (D + 1) * 4;  // one split's partials
+  if (n_split == 0) {
+    // the recommended count, lowered to what the scratch holds
+    n_split = gqa_attn_split_count(B, Hq, Hkv, Lq, Lk, dtype);
+    const int64_t fit = GQA_NOALLOC_SCRATCH_BYTES / row_bytes;
+    if (n_split > fit) n_split = fit < 1 ? 1 : (int)fit;
+  }
+  int split_tiles, n_eff;
+  split_shape(Lk, dtype, n_split, &split_tiles, &n_eff);
+  hipStream_t s = (hipStream_t)stream;
+  if (n_eff <= 1) {
+    (void)hipGetLastError();
+    return launch_fwd(p, dtype, s) == hipSuccess ? GQA_OK : GQA_ERR_LAUNCH;
+  }
+  if ((int64_t)n_eff * row_bytes > GQA_NOALLOC_SCRATCH_BYTES) return GQA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const int rs = scratch_address(&ws);
+  if (rs != GQA_OK) return rs;
+  return fwd_split_run(p, q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, D, seg_q, seg_k, dtype, split_tiles, n_eff, ws,
+                       GQA_NOALLOC_SCRATCH_BYTES, s);
 }
 
 GQA_API int gqa_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -275,9 +354,10 @@ GQA_API const char* gqa_attn_strerror(int code) {
     case GQA_ERR_ALIGN: return "misaligned pointer: tensors need 16-byte alignment, lse and segment ids 4-byte";
     case GQA_ERR_LAUNCH: return "kernel launch failed";
     case GQA_ERR_ALIAS: return "output overlaps an input";
-    case GQA_ERR_WORKSPACE: return "workspace smaller than gqa_attn_split_workspace() for the split count";
+    case GQA_ERR_WORKSPACE: return "workspace smaller than gqa_attn_split_workspace() for the split count "
+                                   "(allocation-free call: the partials exceed GQA_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status code";
   }
 }
 
-GQA_API int gqa_attn_version(void) { return (1 << 16) | 3; }
+GQA_API int gqa_attn_version(void) { return (1 << 16) | 4; }

@@ -45,7 +45,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_strerror():
-    assert gqa.version() == (1, 3)
+    assert gqa.version() == (1, 4)
     msgs = [gqa.strerror(c) for c in range(8)]
     assert len(set(msgs)) == 8 and msgs[0] == "success"
     assert "unknown" in gqa.strerror(99)
@@ -127,6 +127,25 @@ def call_split(**over):
 ])
 def test_fwd_split_rejects_before_launch(over, code):
     assert call_split(**over) == code
+
+
+def call_noalloc(**over):
+    a = dict(GOOD, n_split=0)
+    a.update(over)
+    return gqa.fwd_split_noalloc_raw(*(a[n] for n in ("q", "k", "v", "o", "lse", "B", "Hq", "Hkv", "Lq", "Lk", "D",
+                                                      "q_offset", "seg_q", "seg_k", "causal", "dtype", "n_split",
+                                                      "stream")))
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), 1), (dict(Lq=0), 2), (dict(D=128), 3), (dict(q=Q + 2), 4), (dict(o=K), 6),
+    (dict(n_split=-1), 3), (dict(n_split=1025), 3),
+    # partials beyond the static scratch: 64 rows x 16 heads x 1024 splits x 257 fp32 = 1.08 GB
+    (dict(Lq=64, Lk=65536, n_split=1024), 7),
+    (dict(Lq=512, Lk=65536, n_split=8), 7),
+])
+def test_fwd_split_noalloc_rejects_before_launch(over, code):
+    assert call_noalloc(**over) == code
 
 
 def test_split_workspace_and_count():

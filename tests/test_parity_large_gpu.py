@@ -98,6 +98,11 @@ def test_memory_linear_in_L():
     applies to the attention pass, where the L x L math path needs 16 such
     matrices."""
     per_token = []
+    # load the library's code object on the device first (a tiny call)
+    t = torch.zeros(1, 16, 8, 256, device="cuda:0")
+    gqa.fwd(t, t[:, :4].contiguous(), t[:, :4].contiguous())
+    torch.cuda.synchronize()
+    del t
     for L in (15231, 30468, 60926):
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
