@@ -235,52 +235,136 @@ def run_shards(x, whole_ms, rank_counts, steps, warmup, torch, gqa):
             "whole_call_ms": round(whole_ms, 3), "splits": out}
 
 
-def cpu_baseline(x, target_s=15.0):
-    """The oracle (fp64, OpenMP over rows) on a bounded sample of query rows of
-    the same workload, all heads; rows spread evenly over the sequence."""
+def copy_probe(torch):
+    """A plain 1 GiB device copy, 3 times: the reference that scales the HBM
+    byte counters (FETCH_SIZE, WRITE_SIZE) read under the profiler."""
+    n = 1 << 28  # 2^28 fp32 = 1 GiB read + 1 GiB written per copy
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    return {"read": 4 * n, "written": 4 * n}
+
+
+def cpu_threads():
+    """Threads the oracle runs on: the OpenMP thread count the environment sets
+    (the host's CPU share for this GPU), else every CPU this process may run on."""
+    aff = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS")
+    n = int(env) if env and env.isdigit() and int(env) > 0 else aff
+    return min(n, aff), aff
+
+
+def oracle_rows(x, rows, threads, seg=None):
+    """Seconds for the oracle on query rows `rows` of every head of workload x,
+    and the visible (row, key) pairs of one head over those rows."""
     import oracle
-    import synth
+    from long_context_causal_amd import work
+    sq = None if seg is None else seg[None]
+    t0 = time.perf_counter()
+    oracle.attn(x.q, x.k, x.v, causal=x.causal, q_offset=x.q_offset, seg_q=sq, seg_k=sq, rows=rows, nthreads=threads)
+    dt = time.perf_counter() - t0
+    Lk = x.k.shape[2]
+    pairs = work.visible_pairs_rows(rows, Lk, causal=x.causal, q_offset=x.q_offset, seg_q=seg, seg_k=seg)
+    return dt, pairs
+
+
+def cpu_entry(name, x, threads, full_pairs, seg=None, target_s=4.0, full=False):
+    """The oracle on workload x: the whole workload (full=True), or evenly
+    spaced query rows (all heads, all their visible keys) sized to about
+    target_s seconds, with the whole workload's time extrapolated by visible
+    pairs and labelled so. Rates count 4 D flops per visible pair and head."""
     L = x.q.shape[2]
-    threads = len(os.sched_getaffinity(0))
-    threads = min(threads, 16)
+    Hq, Dh = x.q.shape[1], x.q.shape[3]
+    if full:
+        rows = np.arange(L, dtype=np.int64)
+    else:
+        calib = np.linspace(0, L - 1, 16).astype(np.int64)
+        dt, pr = oracle_rows(x, calib, threads, seg)
+        per_pair = dt / max(pr, 1)
+        n = int(max(16, min(L, target_s / max(per_pair * full_pairs / L, 1e-9))))
+        rows = np.linspace(0, L - 1, n).astype(np.int64)
+    dt, pr = oracle_rows(x, rows, threads, seg)
+    fl = 4 * Dh * Hq * pr
+    rec = dict(workload=name, threads=threads, rows=int(len(rows)), rows_total=int(L), seconds=round(dt, 3),
+               value=fl / dt / 1e12, unit="TFLOP/s")
+    if full:
+        rec["kind"] = "full"
+    else:
+        rec["kind"] = "sampled"
+        rec["full_seconds_extrapolated"] = round(dt * full_pairs / max(pr, 1), 1)
+        rec["note"] = "whole-workload time extrapolated from the sampled rows by visible (row, key) pairs"
+    return rec
 
-    def pairs(rows):
-        return int(np.sum(np.minimum(x.k.shape[2], x.q_offset + rows + 1)))
 
-    calib = np.linspace(0, L - 1, 16).astype(np.int64)
-    t0 = time.perf_counter()
-    oracle.attn(x.q, x.k, x.v, causal=True, rows=calib, nthreads=threads)
-    dt = time.perf_counter() - t0
-    n = int(max(16, min(L, 16 * target_s / max(dt, 1e-3))))
-    rows = np.linspace(0, L - 1, n).astype(np.int64)
-    t0 = time.perf_counter()
-    oracle.attn(x.q, x.k, x.v, causal=True, rows=rows, nthreads=threads)
-    dt = time.perf_counter() - t0
-    fl = 4 * D * HQ * pairs(rows)
-    # the whole small case (L = 512, inputs x 1/16) on one thread
+def cpu_baseline(x, threads, aff, target_s=12.0):
+    """The headline line's CPU figure: the oracle (fp64, OpenMP over rows) on a
+    bounded sample of evenly spaced query rows of the headline workload, all
+    heads, all their visible keys; plus the whole small case (L = 512, inputs
+    x 1/16) on one thread and on all threads."""
+    import synth
+    from long_context_causal_amd import work
+    L = x.q.shape[2]
+    full_pairs = work.visible_pairs(L, L)
+    rec = cpu_entry("causal GQA fwd fp32 L=%d" % L, x, threads, full_pairs, target_s=target_s)
     xs = synth.gqa(1, HQ, HKV, 512, seed=0, scale=1.0 / 16)
-    t0 = time.perf_counter()
-    oracle.attn(xs.q, xs.k, xs.v, causal=True, nthreads=1)
-    dt1 = time.perf_counter() - t0
-    fl1 = 4 * D * HQ * 512 * 513 // 2
-    return dict(value=fl / dt / 1e12, unit="TFLOP/s", cores=threads, kind="oracle",
-                sample="%d of %d query rows (evenly spaced) x 16 heads of the fp32 causal forward at L=%d, "
-                       "all their visible keys; %.1f s" % (n, L, L, dt),
-                cpu_model=cpu_model(),
-                one_thread_L512=dict(value=fl1 / dt1 / 1e12, unit="TFLOP/s", seconds=dt1,
-                                     sample="the whole fp32 causal forward at L=512, one thread"))
+    one = cpu_entry("causal GQA fwd fp32 L=512 (inputs x 1/16), one thread", xs, 1, 512 * 513 // 2, full=True)
+    allt = cpu_entry("causal GQA fwd fp32 L=512 (inputs x 1/16)", xs, threads, 512 * 513 // 2, full=True)
+    return dict(value=rec["value"], unit="TFLOP/s", cores=threads, kind="oracle",
+                sample="%d of %d query rows (evenly spaced) x 16 heads of the fp32 causal forward at L=%d, all "
+                       "their visible keys; %.1f s on %d threads" % (rec["rows"], L, L, rec["seconds"], threads),
+                full_seconds_extrapolated=rec["full_seconds_extrapolated"],
+                extrapolated="the whole workload's time, from the sample by visible (row, key) pairs",
+                affinity_cpus=aff, cpu_model=cpu_model(), one_thread_L512=one, all_threads_L512=allt)
+
+
+def cpu_branch(synth, threads, n_sample=2):
+    """The oracle on the shared-prefix branch workload (S = 30,468, 40 branches
+    of 256 rows): n_sample whole branches, each one call over concat(prefix,
+    branch) with q_offset = S; the 40-branch time extrapolated by visible pairs."""
+    import oracle
+    br = synth.Branch(S=30468, n=40, m=256, seed=0, dtype="f32")
+    S, m, n = br.S, br.m, br.n
+    t = 0.0
+    for b in range(n_sample):
+        k_cat = np.concatenate([br.k_p[None], br.k_b[b:b + 1]], axis=2)
+        v_cat = np.concatenate([br.v_p[None], br.v_b[b:b + 1]], axis=2)
+        t0 = time.perf_counter()
+        oracle.attn(br.q_b[b:b + 1], k_cat, v_cat, causal=True, q_offset=S, nthreads=threads)
+        t += time.perf_counter() - t0
+    pairs_per_branch = m * S + m * (m + 1) // 2
+    fl = 4 * D * HQ * pairs_per_branch * n_sample
+    return dict(workload="branch f32 S=30468 n=40 m=256", threads=threads, rows=n_sample * m, rows_total=n * m,
+                seconds=round(t, 3), value=fl / t / 1e12, unit="TFLOP/s", kind="sampled",
+                full_seconds_extrapolated=round(t * n / n_sample, 1),
+                note="%d of the 40 branches, whole; the 40-branch time extrapolated by visible pairs" % n_sample)
 
 
 def cpu_model():
-    """The host CPU's model name (/proc/cpuinfo), or None where it is not listed."""
+    """The host CPU's model name (/proc/cpuinfo, else lscpu), or None where
+    neither lists one."""
+    name = None
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
                 if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                    name = line.split(":", 1)[1].strip()
+                    break
     except OSError:
         pass
-    return None
+    try:
+        import subprocess
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                lname = line.split(":", 1)[1].strip()
+                if not name or len(lname) > len(name):
+                    name = lname
+    except (OSError, subprocess.SubprocessError):
+        pass
+    return name
 
 
 # Sources and translation unit of each forward kernel.
@@ -314,35 +398,113 @@ def kernel_source_hash(dtype: str) -> str:
     return h.hexdigest()[:16]
 
 
-def pmc_means(db_path):
-    """Mean per-dispatch counter value by (kernel name, counter) from a rocprofv3 database."""
+def pmc_dispatches(db_path):
+    """Per kernel dispatch of a rocprofv3 database: kernel name, duration (ns)
+    and each counter's value (summed over the counter's instances, except
+    GRBM_GUI_ACTIVE, one value per XCD, of which the largest is taken)."""
     import sqlite3
     from collections import defaultdict
     con = sqlite3.connect(db_path)
-    acc = defaultdict(list)
-    for name, cname, val in con.execute("select name, counter_name, counter_value from pmc_events"):
-        acc[(name, cname)].append(float(val))
-    return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
+    vals = defaultdict(lambda: defaultdict(list))
+    info = {}
+    for did, name, dur, cname, val in con.execute(
+            "select dispatch_id, name, duration, counter_name, counter_value from pmc_events"):
+        vals[did][cname].append(float(val))
+        info[did] = (name, float(dur))
+    out = []
+    for did in sorted(vals):
+        c = {k: (max(v) if k == "GRBM_GUI_ACTIVE" else sum(v)) for k, v in vals[did].items()}
+        out.append(dict(dispatch=did, name=info[did][0], duration_ns=info[did][1], counters=c))
+    return out
+
+
+def dispatch_groups(disp):
+    """Dispatches grouped by kernel name and size: within a name, durations
+    more than 4x apart fall in different groups (the branch form launches the
+    forward kernel for the long prefix part and the short suffix part). The
+    first dispatch of each name (code-object load) is left out when there are
+    others."""
+    from collections import defaultdict
+    byname = defaultdict(list)
+    for d in disp:
+        byname[d["name"]].append(d)
+    groups = []
+    for name, ds in byname.items():
+        ds = ds[1:] if len(ds) > 1 else ds
+        ds = sorted(ds, key=lambda d: d["duration_ns"])
+        cur = [ds[0]]
+        for d in ds[1:]:
+            if d["duration_ns"] > 4 * cur[-1]["duration_ns"]:
+                groups.append((name, cur))
+                cur = []
+            cur.append(d)
+        groups.append((name, cur))
+    return groups
+
+
+def group_means(ds):
+    keys = set().union(*(d["counters"] for d in ds))
+    return (sum(d["duration_ns"] for d in ds) / len(ds),
+            {k: sum(d["counters"].get(k, 0.0) for d in ds) / len(ds) for k in keys})
+
+
+def pmc_summary(dbs):
+    """Markdown rows per (kernel, size group) of rocprofv3 --pmc databases:
+    mean duration and counters per dispatch, and the derived figures (shader
+    clock = GRBM_GUI_ACTIVE / duration; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES /
+    (GRBM_GUI_ACTIVE x 1024 SIMDs); busy at 2.4 GHz = SQ_VALU_MFMA_BUSY_CYCLES /
+    (1024 x 2.4 GHz x duration); executed MFMA flops = MOPS x 512; L2 hit rate;
+    SQ_* cycle counters as fractions of SQ_WAVE_CYCLES)."""
+    lines = []
+    for db in dbs:
+        for name, ds in dispatch_groups(pmc_dispatches(db)):
+            dur, c = group_means(ds)
+            parts = ["%s x%d" % (name[:60], len(ds)), "%.3f ms" % (dur * 1e-6)]
+            if "GRBM_GUI_ACTIVE" in c and dur > 0:
+                parts.append("clock %.2f GHz" % (c["GRBM_GUI_ACTIVE"] / dur))
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in c and c.get("GRBM_GUI_ACTIVE"):
+                b = c["SQ_VALU_MFMA_BUSY_CYCLES"]
+                parts.append("MFMA busy %.1f%%" % (100 * b / (c["GRBM_GUI_ACTIVE"] * 1024)))
+                parts.append("busy at 2.4 GHz %.1f%%" % (100 * b / (1024 * 2.4 * dur)))
+            for m in ("SQ_INSTS_VALU_MFMA_MOPS_F32", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F16"):
+                if c.get(m):
+                    parts.append("%s x 512 = %.4g flops" % (m, c[m] * 512))
+            if "TCC_HIT_sum" in c and "TCC_MISS_sum" in c:
+                tot = c["TCC_HIT_sum"] + c["TCC_MISS_sum"]
+                parts.append("L2 hit %.1f%% (%.3g requests)" % (100 * c["TCC_HIT_sum"] / max(tot, 1), tot))
+            if c.get("SQ_WAVE_CYCLES"):
+                wc = c["SQ_WAVE_CYCLES"]
+                parts.append("SQ_WAVE_CYCLES %.4g" % wc)
+                for k in sorted(c):
+                    if k.startswith("SQ_") and k not in ("SQ_WAVE_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES") and \
+                            not k.startswith("SQ_INSTS_VALU_MFMA"):
+                        parts.append("%s %.1f%%" % (k, 100 * c[k] / wc))
+            for k in ("FETCH_SIZE", "WRITE_SIZE"):
+                if k in c:
+                    parts.append("%s %.6g KiB" % (k, c[k]))
+            lines.append("| " + " | ".join(parts) + " |")
+    return "\n".join(lines)
 
 
 def pmc_report(fetch_db, write_db, kernel_substr, workload, out_path):
     """HBM traffic per dispatch of the attention kernel from FETCH_SIZE and
     WRITE_SIZE (KiB per dispatch), each scaled by what the same counter reports
-    for a plain device copy of 1 GiB read + 1 GiB written in the same process."""
-    f, w = pmc_means(fetch_db), pmc_means(write_db)
+    for a plain device copy of 1 GiB read + 1 GiB written in the same process.
+    Where the kernel name matches dispatches of different sizes, the group of
+    the longest ones is taken (the dominant launch)."""
+    def pick(db, sub, counter):
+        gs = [(n, ds) for n, ds in dispatch_groups(pmc_dispatches(db)) if sub in n]
+        assert gs, (sub, counter)
+        n, ds = max(gs, key=lambda g: group_means(g[1])[0])
+        return group_means(ds)[1][counter], n
 
-    def pick(m, sub, counter):
-        hits = [(k, v) for k, v in m.items() if sub in k[0] and k[1] == counter]
-        assert len(hits) == 1, (sub, counter, list(m))
-        return hits[0][1][0], hits[0][0][0]
-
-    fk, kname = pick(f, kernel_substr, "FETCH_SIZE")
-    wk, _ = pick(w, kernel_substr, "WRITE_SIZE")
-    fc, _ = pick(f, "copyBuffer", "FETCH_SIZE")
-    wc, _ = pick(w, "copyBuffer", "WRITE_SIZE")
+    fk, kname = pick(fetch_db, kernel_substr, "FETCH_SIZE")
+    wk, _ = pick(write_db, kernel_substr, "WRITE_SIZE")
+    fc, _ = pick(fetch_db, "copyBuffer", "FETCH_SIZE")
+    wc, _ = pick(write_db, "copyBuffer", "WRITE_SIZE")
     gib = float(1 << 30)
     fetch_scale, write_scale = gib / (fc * 1024.0), gib / (wc * 1024.0)
-    rec = {"workload": workload, "kernel": kname, "kernel_src_sha": kernel_source_hash(kernel_dtype(kname)),
+    rec = {"workload": workload, "kernel": kname, "kernel_src_sha": kernel_source_hash(kernel_dtype(workload)),
            "fetch_kib_per_dispatch": fk, "write_kib_per_dispatch": wk,
            "copy_fetch_kib": fc, "copy_write_kib": wc, "fetch_scale": fetch_scale, "write_scale": write_scale,
            "traffic_bytes": fk * 1024.0 * fetch_scale + wk * 1024.0 * write_scale}
@@ -373,13 +535,19 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only", default=None,
                     help="run one workload: f32-15231, f32-30468, f32-60926, bf16-60926, f16-60926, "
-                         "bwd-f32-30468, bwd-bf16-60926, split-decode-bf16, split-branch-f32, cp-f32-30468")
+                         "seg-bf16-131072, noids-bf16-131072, branch-f32, bwd-f32-30468, bwd-bf16-60926, "
+                         "split-decode-bf16, split-branch-f32, cp-f32-30468")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (3 times) to calibrate HBM byte counters")
+    ap.add_argument("--pmc-summary", nargs="+", metavar="DB",
+                    help="print per-kernel counter means and derived figures of rocprofv3 --pmc databases")
     ap.add_argument("--pmc-report", nargs=4, metavar=("FETCH_DB", "WRITE_DB", "KERNEL_SUBSTR", "WORKLOAD"),
                     help="turn two rocprofv3 --pmc databases (FETCH_SIZE, WRITE_SIZE) into HBM bytes per "
                          "dispatch and store them in profiles/traffic.json under WORKLOAD")
     args = ap.parse_args()
+    if args.pmc_summary:
+        print(pmc_summary(args.pmc_summary))
+        return
     if args.pmc_report:
         fdb, wdb, sub, wl = args.pmc_report
         tmp = os.path.join(ROOT, "profiles", ".traffic_one.json")
@@ -442,6 +610,31 @@ def main():
         r["pct_mfma_peak_exec"] = 100.0 * r["exec_tflops"] / work.PEAK_TFLOPS[dts]
         print(json.dumps(r), flush=True)
         return
+    Lseg = 131072
+    if args.only in ("seg-bf16-131072", "noids-bf16-131072"):
+        # a profiling aid: the packed-segment workload (or its id-free comparator) alone
+        lens = synth.segment_lengths(Lseg, 2048, 32768, seed=1)
+        xs = synth.gqa(1, HQ, HKV, Lseg, seed=0, dtype="bf16")
+        seg = synth.segment_ids(lens) if args.only.startswith("seg") else None
+        nm = ("segmented bf16 L=131072, %d segments (2k-32k)" % len(lens) if seg is not None else
+              "single-segment comparator bf16 L=131072 (no ids)")
+        r = run_fwd_workload(nm, xs, args.steps, args.warmup, torch, gqa, work, seg=seg)
+        r["pct_mfma_peak"] = 100.0 * r["kernel_tflops"] / work.PEAK_TFLOPS["bf16"]
+        if args.copy_probe:
+            r["copy_probe_bytes"] = copy_probe(torch)
+        print(json.dumps(r), flush=True)
+        return
+    if args.only == "branch-f32":
+        # a profiling aid: the shared-prefix branch workload alone
+        r = run_branch(args.steps, args.warmup, torch, gqa, work, synth)
+        r["pct_mfma_peak"] = 100.0 * r["kernel_tflops"] / work.PEAK_TFLOPS["f32"]
+        if args.copy_probe:
+            r["copy_probe_bytes"] = copy_probe(torch)
+        print(json.dumps(r), flush=True)
+        return
+    threads, aff = cpu_threads()
+    cpu = not args.no_cpu
+    cpu_cfg = []
     primary_key = args.only or "f32-30468"
     name, L, dt = workloads[primary_key]
     x = synth.gqa(1, HQ, HKV, L, seed=0, dtype=dt)
@@ -451,13 +644,23 @@ def main():
     secondary = []
     shards = None
     if not args.quick and args.only is None:
+        if cpu:
+            # the whole small case on all threads and the oracle beside each workload below:
+            # whole where it takes seconds (L = 15,231), else sampled rows, extrapolated
+            xs = synth.gqa(1, HQ, HKV, 512, seed=0, scale=1.0 / 16)
+            cpu_cfg.append(cpu_entry("causal GQA fwd fp32 L=512 (inputs x 1/16)", xs, threads, 512 * 513 // 2,
+                                     full=True))
         for key in ("f32-15231", "f32-60926", "bf16-60926", "f16-60926"):
             nm, Ls, dts = workloads[key]
             xs = synth.gqa(1, HQ, HKV, Ls, seed=0, dtype=dts)
             r = run_fwd_workload(nm, xs, max(3, args.steps // 2), 2, torch, gqa, work)
+            if cpu and key != "f16-60926":
+                cpu_cfg.append(cpu_entry(nm, xs, threads, work.visible_pairs(Ls, Ls), full=(key == "f32-15231")))
             del xs
             secondary.append(r)
         secondary.append(run_branch(max(3, args.steps // 2), 2, torch, gqa, work, synth))
+        if cpu:
+            cpu_cfg.append(cpu_branch(synth, threads))
         # the backward (training): fp32 at L = 30,468 and bf16 at L = 60,926
         for nm, Ls, dts in bwd_workloads.values():
             xs = synth.gqa(1, HQ, HKV, Ls, seed=0, dtype=dts)
@@ -478,6 +681,8 @@ def main():
         r = run_fwd_workload("segmented bf16 L=131072, %d segments (2k-32k)" % len(lens), xs,
                              max(3, args.steps // 2), 2, torch, gqa, work, seg=ids)
         secondary.append(r)
+        if cpu:
+            cpu_cfg.append(cpu_entry(r["workload"], xs, threads, r["flops"] // (4 * D * HQ), seg=ids))
         r = run_fwd_workload("single-segment comparator bf16 L=131072 (no ids)", xs, 3, 1, torch, gqa, work)
         secondary.append(r)
         r = run_bwd_workload("segmented bwd bf16 L=131072, %d segments (2k-32k)" % len(lens), xs, 3, 1, torch, gqa,
@@ -489,6 +694,7 @@ def main():
     for r in [prim] + secondary:
         dts = "bf16" if "bf16" in r["workload"] else "f16" if "fp16" in r["workload"] else "f32"
         r["pct_mfma_peak"] = 100.0 * r["kernel_tflops"] / work.PEAK_TFLOPS[dts]
+        r["traffic"] = stored_traffic(r["workload"])
         if "exec_tflops" in r:
             r["pct_mfma_peak_exec"] = 100.0 * r["exec_tflops"] / work.PEAK_TFLOPS[dts]
 
@@ -524,16 +730,12 @@ def main():
     if shards is not None:
         out["context_parallel_shards"] = shards
     if args.copy_probe:
-        n = 1 << 28  # 2^28 fp32 = 1 GiB read + 1 GiB written per copy
-        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        out["copy_probe_bytes"] = {"read": 4 * n, "written": 4 * n}
-        del src, dst
-    if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(x)
+        out["copy_probe_bytes"] = copy_probe(torch)
+    if cpu:
+        out["cpu_baseline"] = cpu_baseline(x, threads, aff)
+        if cpu_cfg:
+            out["cpu_baseline"]["per_config"] = [{k: (round(v, 5) if isinstance(v, float) else v)
+                                                 for k, v in c.items()} for c in cpu_cfg]
     print(json.dumps(out), flush=True)
 
 

@@ -28,6 +28,25 @@ def visible_pairs(Lq: int, Lk: int, *, causal: bool = True, q_offset: int = 0, s
     return total
 
 
+def visible_pairs_rows(rows, Lk: int, *, causal: bool = True, q_offset: int = 0, seg_q=None, seg_k=None) -> int:
+    """Visible (query, key) pairs of one head over the query rows `rows` only
+    (seg_q: the ids of all query rows; seg_k: of all keys)."""
+    rows = np.asarray(rows, dtype=np.int64)
+    lim = np.minimum(Lk, q_offset + rows + 1) if causal else np.full(len(rows), Lk, dtype=np.int64)
+    if seg_q is None:
+        return int(lim.sum())
+    sq = np.asarray(seg_q).reshape(-1)[rows]
+    sk = np.asarray(seg_k).reshape(-1)
+    order = np.argsort(sk, kind="stable")
+    ks = sk[order]
+    lo = np.searchsorted(ks, sq, "left")
+    hi = np.searchsorted(ks, sq, "right")
+    total = 0
+    for a, b, l in zip(lo, hi, lim):
+        total += int(np.searchsorted(order[a:b], l, "left"))  # positions with the row's id below its limit
+    return total
+
+
 def flops(B, Hq, Lq, Lk, D, **kw) -> int:
     """Algorithmic FLOPs of the forward (same pair count in every batch row unless
     per-batch segment ids are given as [B, L] arrays)."""
