@@ -39,6 +39,7 @@ UNITS = {
     "gqa_attn.hip": [],
     "fwd_f32.hip": VGPR_FORM,
     "fwd_h16.hip": [],
+    "decode_h16.hip": [],
     "bwd_f32.hip": [],
     "bwd_h16.hip": [],
 }

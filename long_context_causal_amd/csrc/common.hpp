@@ -47,6 +47,9 @@ struct FwdParams {
   int64_t part_rows;  // B * Hq * Lq: the rows of one split's part
   float* o_part;
   float* lse_part;
+  // Host plan only: the launch goes to the short-block (decode) kernel, whose
+  // grid is n_split x n_qb row blocks of 64 packed rows x G = B * Hkv.
+  int decode;
 };
 
 // Arguments of one backward launch pair (passed by value to both kernels).

@@ -24,6 +24,13 @@ bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
 
 bool is_pow2_rep(int64_t r) { return r == 1 || r == 2 || r == 4 || r == 8 || r == 16; }
 
+// Launches the short-block (decode) kernel serves: 16-bit inputs, no segment
+// ids, fewer than 32 query positions, and key counts whose 32-key tile ends
+// stay below 2^31 (its tile arithmetic is 32-bit).
+bool decode_shape(int dtype, int64_t Lq, int64_t Lk, bool seg) {
+  return dtype != GQA_F32 && !seg && Lq < gqa::kDecodeMaxLq && Lk < ((int64_t)1 << 31) - 64;
+}
+
 // split-KV: the most splits one launch takes, and the workgroup count the
 // recommended split count aims at: one per compute unit (the forward kernels'
 // LDS use admits one workgroup per CU; measured on 16 decode rows over 60,926
@@ -78,18 +85,30 @@ static int fwd_plan(gqa::FwdParams& p, const void* q, const void* k, const void*
   p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
   p.n_split = 1;
   p.part_rows = B * Hq * Lq;
+  p.decode = 0;
+  if (decode_shape(dtype, Lq, Lk, seg_q != nullptr)) {
+    // row blocks of 64 packed (head, position) rows per KV head
+    p.decode = 1;
+    p.n_qb = (int)((n_rep * Lq + gqa::kDecodeBlockRows - 1) / gqa::kDecodeBlockRows);
+    p.G = (int)(B * Hkv);
+  }
   return GQA_OK;
 }
 
 static hipError_t launch_fwd(const gqa::FwdParams& p, int dtype, hipStream_t s) {
+  if (p.decode) return dtype == GQA_BF16 ? gqa::launch_decode_bf16(p, s) : gqa::launch_decode_f16(p, s);
   return dtype == GQA_F32    ? gqa::launch_fwd_f32(p, s)
          : dtype == GQA_BF16 ? gqa::launch_fwd_bf16(p, s)
                              : gqa::launch_fwd_f16(p, s);
 }
 
+// Keys per tile of the kernel a plan launches (the unit of a split-KV range).
+static int64_t plan_tile_keys(const gqa::FwdParams& p, int dtype) {
+  return p.decode ? gqa::kTileKeysDec : dtype == GQA_F32 ? gqa::kTileKeysF32 : gqa::kTileKeysH16;
+}
+
 // Key tiles per split and the number of (non-empty) splits for a requested count.
-static void split_shape(int64_t Lk, int dtype, int n_split, int* split_tiles, int* n_eff) {
-  const int64_t tile = dtype == GQA_F32 ? gqa::kTileKeysF32 : gqa::kTileKeysH16;
+static void split_shape(int64_t Lk, int64_t tile, int n_split, int* split_tiles, int* n_eff) {
   const int64_t n_tiles = (Lk + tile - 1) / tile;
   const int64_t st = (n_tiles + n_split - 1) / n_split;
   *split_tiles = (int)st;
@@ -113,8 +132,12 @@ GQA_API int gqa_attn_split_count(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq,
   const int W = dtype == GQA_F32 ? gqa::kWavesF32 : gqa::kWavesH16;
   const int64_t hpc = n_rep < W ? n_rep : W;
   const int64_t ppc = (W / hpc) * (dtype == GQA_F32 ? gqa::kRowsF32 : gqa::kRowsH16);
-  const int64_t base = ((Lq + ppc - 1) / ppc) * B * Hkv * (n_rep / hpc);
-  const int64_t tile = dtype == GQA_F32 ? gqa::kTileKeysF32 : gqa::kTileKeysH16;
+  // workgroups of one split (for short blocks, those of the decode kernel: the
+  // count assumes no segment ids)
+  const bool dec = decode_shape(dtype, Lq, Lk, false);
+  const int64_t base = dec ? ((n_rep * Lq + gqa::kDecodeBlockRows - 1) / gqa::kDecodeBlockRows) * B * Hkv
+                           : ((Lq + ppc - 1) / ppc) * B * Hkv * (n_rep / hpc);
+  const int64_t tile = dec ? gqa::kTileKeysDec : dtype == GQA_F32 ? gqa::kTileKeysF32 : gqa::kTileKeysH16;
   const int64_t n_tiles = (Lk + tile - 1) / tile;
   // aim at one workgroup per compute unit, each split at least 4 tiles long
   int64_t n = (kSplitTargetWorkgroups + base - 1) / base;
@@ -176,7 +199,7 @@ GQA_API int gqa_attn_fwd_split(const void* q, const void* k, const void* v, void
   if (rc != GQA_OK) return rc;
   if (n_split < 1 || n_split > kMaxSplits) return GQA_ERR_UNSUPPORTED;
   int split_tiles, n_eff;
-  split_shape(Lk, dtype, n_split, &split_tiles, &n_eff);
+  split_shape(Lk, plan_tile_keys(p, dtype), n_split, &split_tiles, &n_eff);
   hipStream_t s = (hipStream_t)stream;
   if (n_eff <= 1) {
     (void)hipGetLastError();
@@ -236,7 +259,7 @@ GQA_API int gqa_attn_fwd_split_noalloc(const void* q, const void* k, const void*
     if (n_split > fit) n_split = fit < 1 ? 1 : (int)fit;
   }
   int split_tiles, n_eff;
-  split_shape(Lk, dtype, n_split, &split_tiles, &n_eff);
+  split_shape(Lk, plan_tile_keys(p, dtype), n_split, &split_tiles, &n_eff);
   hipStream_t s = (hipStream_t)stream;
   if (n_eff <= 1) {
     (void)hipGetLastError();

@@ -92,63 +92,82 @@ __global__ __launch_bounds__(256) void merge_kernel(const T* o1, const float* ls
 // Merge of the n_split partial results of a split-KV forward (fp32 O parts
 // [n_split][rows][D], lse parts [n_split][rows]) into o (in T) and lse: the
 // same log-sum-exp combination over n_split disjoint key ranges. One
-// workgroup per row (D = 256): wave 0 forms the max and the sum of the
-// weights; then 8 groups of 32 lanes each take every 8th split (lane c of a
-// group holds d 8c .. 8c + 7), with the loads of several splits in flight,
-// and the 8 group sums meet in LDS. With many splits and few rows (decoding)
-// a wave per row walking the splits one after another would wait on every
-// load in turn.
+// workgroup per row (D = 256): 8 groups of 32 lanes take every 8th split
+// (lane c of a group holds d 8c .. 8c + 7) and keep a running state over
+// their splits -- max M, weight sum W = sum exp(lse_s - M), weighted sum
+// Z = sum exp(lse_s - M) o_s -- that moves to a new max by one rescale. The
+// splits come in batches of 8 per group whose loads (lse and O) are all
+// issued before any of them is used, so a batch costs one round trip to
+// memory (indexes past the last split load split sg again and are masked).
+// The 8 group states then meet in LDS, rescaled to the common max.
 constexpr int kMergeGroups = 8;
+constexpr int kMergeBatch = 8;
 template <typename T>
 __global__ __launch_bounds__(256) void merge_splits_kernel(const float* o_part, const float* lse_part, int n_split,
                                                            T* o, float* lse, int64_t rows) {
   __shared__ float part[kMergeGroups][kD];
-  __shared__ float s_max, s_inv, s_lse;
+  __shared__ float gmax[kMergeGroups], gsum[kMergeGroups];
   const int64_t r = blockIdx.x;
-  const int t = threadIdx.x, lane = t & 63;
-  if (t < 64) {
-    float m = -INFINITY;
-    for (int s = lane; s < n_split; s += 64) m = fmaxf(m, lse_part[(int64_t)s * rows + r]);
-    for (int x = 32; x >= 1; x >>= 1) m = fmaxf(m, __shfl_xor(m, x));
-    float sum = 0.f;
-    if (m != -INFINITY)
-      for (int s = lane; s < n_split; s += 64) sum += expf(lse_part[(int64_t)s * rows + r] - m);
-    for (int x = 32; x >= 1; x >>= 1) sum += __shfl_xor(sum, x);
-    if (lane == 0) {
-      s_max = m;
-      s_inv = sum > 0.f ? 1.f / sum : 0.f;
-      s_lse = (m == -INFINITY) ? -INFINITY : m + logf(sum);
+  const int t = threadIdx.x, sg = t >> 5, c = t & 31;
+  float m = -INFINITY, w = 0.f;
+  float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int s0 = sg; s0 < n_split; s0 += kMergeBatch * kMergeGroups) {
+    float a[kMergeBatch];
+    f32x4 x[kMergeBatch][2];
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) {
+      const int s = s0 + j * kMergeGroups;
+      const int sl = s < n_split ? s : sg;
+      a[j] = lse_part[(int64_t)sl * rows + r];
+      const float* src = o_part + ((int64_t)sl * rows + r) * kD + 8 * c;
+      x[j][0] = *(const f32x4*)src;
+      x[j][1] = *(const f32x4*)(src + 4);
+    }
+    // one statement takes every loaded value: all 24 loads are issued before
+    // the first wait (left to itself the compiler interleaves loads and waits)
+    asm volatile("" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]),
+                 "+v"(a[7]), "+v"(x[0][0]), "+v"(x[0][1]), "+v"(x[1][0]), "+v"(x[1][1]), "+v"(x[2][0]),
+                 "+v"(x[2][1]), "+v"(x[3][0]), "+v"(x[3][1]), "+v"(x[4][0]), "+v"(x[4][1]), "+v"(x[5][0]),
+                 "+v"(x[5][1]), "+v"(x[6][0]), "+v"(x[6][1]), "+v"(x[7][0]), "+v"(x[7][1]));
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) {
+      // an empty split (lse -inf, O 0) adds nothing; while every split so far
+      // was empty the state stays (-inf, 0, 0)
+      const float aj = s0 + j * kMergeGroups < n_split ? a[j] : -INFINITY;
+      const float mn = fmaxf(m, aj);
+      const float sc = mn == -INFINITY ? 1.f : expf(m - mn);
+      const float e = mn == -INFINITY ? 0.f : expf(aj - mn);
+      w = fmaf(w, sc, e);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) z[i] = fmaf(z[i], sc, e * x[j][i >> 2][i & 3]);
+      m = mn;
     }
   }
-  __syncthreads();
-  const float M = s_max, inv = s_inv;
-  const int sg = t >> 5, c = t & 31;
-  float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  if (M != -INFINITY) {
-#pragma unroll 4
-    for (int s = sg; s < n_split; s += kMergeGroups) {
-      const float w = expf(lse_part[(int64_t)s * rows + r] - M) * inv;
-      float x[8];
-      load8<float>(o_part + ((int64_t)s * rows + r) * kD + 8 * c, x);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) z[i] = fmaf(w, x[i], z[i]);
-    }
+  if (c == 0) {
+    gmax[sg] = m;
+    gsum[sg] = w;
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) part[sg][8 * c + i] = z[i];
   __syncthreads();
   if (t < 32) {
-    float y[8];
+    float M = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float acc = 0.f;
+    for (int g2 = 0; g2 < kMergeGroups; ++g2) M = fmaxf(M, gmax[g2]);
+    float tot = 0.f, y[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int g2 = 0; g2 < kMergeGroups; ++g2) acc += part[g2][8 * t + i];
-      y[i] = acc;
+    for (int g2 = 0; g2 < kMergeGroups; ++g2) {
+      const float sc = gmax[g2] == -INFINITY ? 0.f : expf(gmax[g2] - M);
+      tot = fmaf(sc, gsum[g2], tot);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) y[i] = fmaf(sc, part[g2][8 * t + i], y[i]);
     }
+    const float inv = tot > 0.f ? 1.f / tot : 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] *= inv;
     store8<T>(o + r * kD + 8 * t, y);
+    if (t == 0) lse[r] = tot > 0.f ? M + logf(tot) : -INFINITY;
   }
-  if (t == 0) lse[r] = s_lse;
 }
 
 }  // namespace gqa

@@ -1,0 +1,120 @@
+"""Short query blocks (decoding: fewer than 32 positions) with 16-bit inputs
+and no segment ids: the launches the packed-row decode kernel serves, through
+gqa_attn_fwd and gqa_attn_fwd_split, against the fp64 oracle, every output
+row.
+
+The kernel packs the query rows of one KV head (n_rep heads x Lq positions)
+into blocks of 64, 16 per wave, so the cases vary what that packing meets:
+group sizes 1..16 and Lq 1..31 (a wave's 16 rows spanning several heads, a
+last block cut short, several blocks per head), causal rows whose visible
+keys end before, at and past the key sequence's end, ragged key counts (32-key
+tiles), B = 2, and split counts from 1 to more splits than tiles.
+
+Bars as for the forward: max|do| <= 2e-2 (bf16) / 2.5e-3 (fp16), max|dlse| <= 1e-4.
+"""
+import numpy as np
+import pytest
+import torch
+
+import long_context_causal_amd as gqa
+import oracle
+import synth
+from gpu_util import TOL_O, compare, to_dev
+
+pytestmark = pytest.mark.gpu
+
+DT = ["bf16", "f16"]
+
+
+def check(x, label, n_split=None, unsplit=True):
+    """Oracle check of gqa_attn_fwd_split (at n_split; None = the library's
+    count) and, if asked, of gqa_attn_fwd on the same inputs."""
+    print("case:", label, "n_split", n_split, flush=True)
+    q, k, v = to_dev(x)
+    kw = dict(causal=x.causal, q_offset=x.q_offset)
+    o_ref, l_ref = oracle.attn(x.q, x.k, x.v, causal=x.causal, q_offset=x.q_offset)
+    o, lse = gqa.fwd_split(q, k, v, n_split=n_split, **kw)
+    torch.cuda.synchronize()
+    compare(o, lse, o_ref, l_ref, x.dtype, label="%s split %s" % (label, n_split))
+    if unsplit:
+        o1, l1 = gqa.fwd(q, k, v, **kw)
+        torch.cuda.synchronize()
+        compare(o1, l1, o_ref, l_ref, x.dtype, label="%s unsplit" % label)
+
+
+@pytest.mark.parametrize("dtype", DT)
+@pytest.mark.parametrize("rep,Lq", [(4, 16), (4, 1), (4, 5), (4, 31), (1, 3), (1, 31), (2, 7), (8, 16), (16, 2),
+                                    (16, 31)])
+def test_group_sizes_and_lengths(dtype, rep, Lq):
+    """Decode rows at the end of a ragged key sequence (2,017 keys: 63 full
+    tiles and one of a single key)."""
+    Hkv, Lk = 2, 2017
+    x = synth.gqa(1, Hkv * rep, Hkv, Lq, Lk, seed=300 + 37 * rep + Lq, dtype=dtype, q_offset=Lk - Lq)
+    check(x, "rep%d Lq=%d Lk=%d %s" % (rep, Lq, Lk, dtype), n_split=11)
+
+
+@pytest.mark.parametrize("dtype", DT)
+@pytest.mark.parametrize("q_offset", [0, 1000, 2000, 2017, 2040, 1 << 40])
+def test_causal_ends(dtype, q_offset):
+    """Rows at q_offset + 0..15 over 2,017 keys: visible keys end inside the
+    sequence (the tail is never read), at its end, or past it (every key
+    visible; q_offset far beyond 2^31 included)."""
+    Lq, Lk = 16, 2017
+    x = synth.gqa(1, 16, 4, Lq, Lk, seed=320, dtype=dtype, q_offset=q_offset)
+    check(x, "q_offset=%d %s" % (q_offset, dtype), n_split=5)
+
+
+@pytest.mark.parametrize("dtype", DT)
+@pytest.mark.parametrize("Lk", [1, 2, 31, 32, 33, 95])
+def test_short_key_sequences(dtype, Lk):
+    """Fewer keys than one ring of tiles (4 x 32), including a single key;
+    splits past the last tile are empty and merge as nothing."""
+    Lq = 3
+    x = synth.gqa(1, 8, 2, Lq, Lk, seed=330 + Lk, dtype=dtype, q_offset=max(Lk - Lq, 0))
+    check(x, "Lk=%d %s" % (Lk, dtype), n_split=4)
+
+
+@pytest.mark.parametrize("dtype", DT)
+def test_noncausal_batch_two(dtype):
+    x = synth.gqa(2, 16, 4, 9, 3001, seed=340, dtype=dtype, causal=False)
+    check(x, "B2 noncausal Lq=9 Lk=3001 " + dtype, n_split=13)
+
+
+@pytest.mark.parametrize("dtype", DT)
+@pytest.mark.parametrize("n_split", [1, 2, 64, 1000])
+def test_split_counts(dtype, n_split):
+    """The same 16 rows over 4,500 keys at 1, 2, 64 and 1,000 requested splits
+    (141 tiles: 1,000 requests give 141 one-tile ranges)."""
+    x = synth.gqa(1, 16, 4, 16, 4500, seed=350, dtype=dtype, q_offset=4500 - 16)
+    check(x, "splits %d %s" % (n_split, dtype), n_split=n_split, unsplit=n_split == 1)
+
+
+def test_peaky_scores_rescale():
+    """Query rows scaled by 6 (logit standard deviation about 6): the running
+    max moves often, and the lazy rescale of O, l and lr is exercised."""
+    x0 = synth.gqa(1, 16, 4, 16, 3000, seed=360, q_offset=3000 - 16)
+    x = synth.Inputs(x0.q * np.float32(6.0), x0.k, x0.v, "bf16", q_offset=3000 - 16)
+    check(x, "peaky bf16", n_split=6)
+
+
+def test_full_size_decode_every_row():
+    """16 decode rows after 60,926 bf16 keys, at the library's split count
+    (the measured decode workload): every row of every head."""
+    Lk = 60926
+    x = synth.gqa(1, 16, 4, 16, Lk, seed=370, dtype="bf16", q_offset=Lk - 16)
+    check(x, "full size decode bf16", n_split=None, unsplit=False)
+
+
+def test_repeat_calls_identical():
+    """The kernel's result does not depend on what an earlier call left in LDS
+    or in the workspace: two calls on different inputs, then the first again,
+    give the first result bit for bit."""
+    xa = synth.gqa(1, 16, 4, 16, 2500, seed=380, dtype="bf16", q_offset=2484)
+    xb = synth.gqa(1, 16, 4, 16, 2500, seed=381, dtype="bf16", q_offset=2484)
+    qa, ka, va = to_dev(xa)
+    qb, kb, vb = to_dev(xb)
+    oa, la = gqa.fwd_split(qa, ka, va, q_offset=2484, n_split=9)
+    gqa.fwd_split(qb, kb, vb, q_offset=2484, n_split=9)
+    oa2, la2 = gqa.fwd_split(qa, ka, va, q_offset=2484, n_split=9)
+    torch.cuda.synchronize()
+    assert torch.equal(oa, oa2) and torch.equal(la, la2)
