@@ -250,15 +250,15 @@ __device__ __forceinline__ V8 k_frag(int q, lds_cchar* const* kb) {
 
 // Phase A: S^T(next) = K Q^T for the tile in K stage kst (32 MFMAs over
 // D = 256, two key halves) with slots 0..31 of the current tile's exps, the
-// tile copies (K and ids of the tile two ahead, V of the tile one ahead: early
+// tile copies (K of the tile two ahead, V of the tile one ahead: early
 // enough that they land before the next barrier), and the first V fragments
 // of phase B (already resident). Q stays in AGPRs, where the products read it
 // (the empty asm pins it there; the VGPRs go to the scores, P and fragments).
 template <typename E>
 __device__ __forceinline__ void phase_a(int kst, typename Elem<E>::v8* qf, const LanesB& ln, f32x16* s_nxt,
                                         const float* s_cur, float sl2, float m_use, unsigned* pk, ExpPipe<E>& ep,
-                                        const PartCopy& kc, const PartCopy& vc, bool seg, int wave, int lane,
-                                        lds_cchar* const* vb, typename Elem<E>::v8* vf) {
+                                        const PartCopy& kc, const PartCopy& vc, int wave, lds_cchar* const* vb,
+                                        typename Elem<E>::v8* vf) {
   typedef typename Elem<E>::v8 V8;
   lds_cchar* kb[8];
 #pragma unroll
@@ -275,7 +275,6 @@ __device__ __forceinline__ void phase_a(int kst, typename Elem<E>::v8* qf, const
     ep.slot(q, s_cur, sl2, m_use, pk);
     if ((q & 3) == 1) kc.rows(ln.ldk, q >> 2, wave);
     if ((q & 3) == 3) vc.rows(ln.ldv, q >> 2, wave);
-    if (q == 2 && seg) kc.ids(wave, lane);  // seg: the tile needs its key ids (not full)
     if (q >= 32 - kVPre) vf[q - (32 - kVPre)] = v_frag<V8>(q - (32 - kVPre), 0, vb);
     GQA_SEGMENT_END();
   }
@@ -309,7 +308,7 @@ __device__ __forceinline__ void qk_only(int kst, const typename Elem<E>::v8* qf,
 // compiler keeps O in VGPRs around the loop and copies it into AGPRs before
 // every PV product).
 __device__ __forceinline__ void rescale(f32x16* acc, RowState& rs, float alpha) {
-  if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+  if (__builtin_expect(__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0, 0)) {
 #pragma unroll
     for (int n = 0; n < 8; ++n) {
       acc[n] *= alpha;
@@ -378,7 +377,7 @@ struct H16Wave {
   __device__ __forceinline__ bool mask_if_needed(float* s, int t, bool full, int st) {
     const int64_t k0 = (int64_t)t * kBkB;
     const bool seg_elem = SEG && !full;
-    if (seg_elem || k0 + kBkB > p.Lk || (p.causal && k0 + kBkB - 1 > p.q_offset + pw)) {
+    if (__builtin_expect(seg_elem || k0 + kBkB > p.Lk || (p.causal && k0 + kBkB - 1 > p.q_offset + pw), 0)) {
 #pragma unroll
       for (int j = 0; j < 2; ++j)
         mask_half(s + 16 * j, k0 + 32 * j, g, p.Lk, p.causal, lim, seg_elem,
@@ -449,6 +448,10 @@ struct H16Wave {
     const bool f3 = is_full(n3);
     const PartCopy kc = k_copy(st, nn);   // K(#i+2) into K(#i)'s stage
     const PartCopy vc = v_copy(st1, nxt);  // V(#i+1) into V(#i-1)'s stage
+    // the key ids of K(#i+2), where that tile needs them (not full), go out
+    // here rather than among the products: phase A is then the same code with
+    // and without segment ids
+    if (__builtin_expect(SEG && !f_nn, 0)) kc.ids(wave, lane);
     unsigned pk[16];
     ExpPipe<E> ep;
     f32x16 s_nxt[2];
@@ -456,8 +459,7 @@ struct H16Wave {
 #pragma unroll
     for (int j = 0; j < 4; ++j) vbs[j] = ln.v[j] + st * kTileBytesB;
     V8 vf[kVPre];
-    phase_a<E>(st1, qf, ln, s_nxt, s_cur, p.scale_log2, rs.m_use, pk, ep, kc, vc, SEG && !f_nn, wave, lane, vbs,
-               vf);
+    phase_a<E>(st1, qf, ln, s_nxt, s_cur, p.scale_log2, rs.m_use, pk, ep, kc, vc, wave, vbs, vf);
     float sn[32];
     const float alpha = phase_b(st1, s_nxt, pk, ep, vbs, vf, sn);
     rescale(acc, rs, alpha);
