@@ -143,16 +143,67 @@ def run_split_workload(name, x, steps, warmup, torch, gqa, work):
     torch.cuda.synchronize()
     _, ms_plain, _, _ = time_calls(plain, steps, warmup, torch)
     wall_ms, ms_split, ev_min, ev_max = time_calls(split, steps, warmup, torch)
+    med_split = time_calls.last_median
+    graph_ms = split_graph_ms(split, o, lse, steps, torch)
     fl = work.flops(B, Hq, Lq, Lk, Dh, causal=x.causal, q_offset=x.q_offset)
     es = 4 if x.dtype == "f32" else 2
     kv_bytes = 2 * B * Hkv_ * Lk * Dh * es
     del q, k, v, o, lse, ws
     torch.cuda.empty_cache()
     return dict(workload=name, n_split=n_split, flops=fl, wall_ms=wall_ms, kernel_ms=ms_split,
-                kernel_ms_min=ev_min, kernel_ms_max=ev_max, kernel_ms_median=time_calls.last_median,
+                kernel_ms_min=ev_min, kernel_ms_max=ev_max, kernel_ms_median=med_split,
                 unsplit_ms=ms_plain, speedup=ms_plain / ms_split,
                 tflops=fl / (wall_ms * 1e-3) / 1e12, kernel_tflops=fl / (ms_split * 1e-3) / 1e12,
-                kv_bytes=kv_bytes, kv_gbs=kv_bytes / (ms_split * 1e-3) / 1e9)
+                kv_bytes=kv_bytes, kv_gbs=kv_bytes / (ms_split * 1e-3) / 1e9,
+                graph_ms=graph_ms, graph_kv_gbs=kv_bytes / (graph_ms * 1e-3) / 1e9 if graph_ms else None)
+
+
+def split_graph_ms(split, o, lse, steps, torch):
+    """GPU time per call of the split-KV pair (partials + merge) replayed from a
+    HIP graph: per-call events on a short call also hold the host's launch
+    time, which a graph replay leaves out. Every replay's o and lse are checked
+    bit for bit against the eager call's; on a mismatch (or a capture error)
+    the figure is None."""
+    split()
+    torch.cuda.synchronize()
+    o_ref, l_ref = o.clone(), lse.clone()
+    try:
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            split()  # warm-up on the capture stream
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            split()
+        torch.cuda.synchronize()
+    except RuntimeError as e:
+        print("graph capture failed: %s" % e, file=sys.stderr)
+        return None
+    for _ in range(3):
+        o.zero_()
+        lse.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        if not (torch.equal(o, o_ref) and torch.equal(lse, l_ref)):
+            print("graph replay differs from the eager call", file=sys.stderr)
+            return None
+    # back-to-back replays keep the queue ahead of the GPU, so the time between
+    # the events is the GPU's; the best of 3 batches
+    reps = max(steps, 20)
+    best = None
+    for _ in range(3):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        t = a.elapsed_time(b) / reps
+        best = t if best is None else min(best, t)
+    return best
 
 
 def run_branch(steps, warmup, torch, gqa, work, synth):
