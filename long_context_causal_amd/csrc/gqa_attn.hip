@@ -383,4 +383,4 @@ GQA_API const char* gqa_attn_strerror(int code) {
   }
 }
 
-GQA_API int gqa_attn_version(void) { return (1 << 16) | 4; }
+GQA_API int gqa_attn_version(void) { return (1 << 16) | 5; }

@@ -45,7 +45,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_strerror():
-    assert gqa.version() == (1, 4)
+    assert gqa.version() == (1, 5)
     msgs = [gqa.strerror(c) for c in range(8)]
     assert len(set(msgs)) == 8 and msgs[0] == "success"
     assert "unknown" in gqa.strerror(99)
@@ -159,6 +159,15 @@ def test_split_workspace_and_count():
     assert gqa.split_count(1, 16, 4, 30468, 30468, gqa.GQA_F32) == 1
     # short keys: at most a quarter of the tile count (1000 keys = 32 tiles of 32)
     assert gqa.split_count(1, 16, 4, 1, 1000, gqa.GQA_F32) == 8
+    # 16-bit decode shapes (Lq < 32) count the decode kernel's workgroups: row
+    # blocks of 64 packed (head, position) rows per KV head. 16 heads per KV
+    # head x 31 positions = 496 rows = 8 blocks: 32 workgroups per split, so 8
+    # splits fill 256; 16 decode rows (64 rows, one block): 64 splits
+    assert gqa.split_count(1, 64, 4, 31, 60926, gqa.GQA_BF16) == 8
+    assert gqa.split_count(1, 16, 4, 16, 60926, gqa.GQA_F16) == 64
+    # 32-key tiles: 200 keys = 7 tiles, at most a quarter of them (1)
+    assert gqa.split_count(1, 16, 4, 16, 200, gqa.GQA_BF16) == 1
+    assert gqa.split_count(1, 16, 4, 16, 260, gqa.GQA_BF16) == 2
 
 
 def test_python_binding_rejects_host_tensors():
