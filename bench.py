@@ -155,7 +155,9 @@ def run_split_workload(name, x, steps, warmup, torch, gqa, work):
                 unsplit_ms=ms_plain, speedup=ms_plain / ms_split,
                 tflops=fl / (wall_ms * 1e-3) / 1e12, kernel_tflops=fl / (ms_split * 1e-3) / 1e12,
                 kv_bytes=kv_bytes, kv_gbs=kv_bytes / (ms_split * 1e-3) / 1e9,
-                graph_ms=graph_ms, graph_kv_gbs=kv_bytes / (graph_ms * 1e-3) / 1e9 if graph_ms else None)
+                kv_frac_hbm_peak=kv_bytes / (ms_split * 1e-3) / (work.PEAK_HBM_GBS * 1e9),
+                graph_ms=graph_ms, graph_kv_gbs=kv_bytes / (graph_ms * 1e-3) / 1e9 if graph_ms else None,
+                graph_kv_frac_hbm_peak=kv_bytes / (graph_ms * 1e-3) / (work.PEAK_HBM_GBS * 1e9) if graph_ms else None)
 
 
 def split_graph_ms(split, o, lse, steps, torch):
