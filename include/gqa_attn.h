@@ -139,11 +139,11 @@ int gqa_attn_bwd(const void* q, const void* k, const void* v, const void* o, con
  * shared prefix, system1-omni issue 27, "Three differences from Cua-S1 that
  * matter", item 3), where gqa_attn_fwd would launch too few workgroups to fill
  * the GPU. The key range is cut into n_split consecutive ranges of whole key
- * tiles: 32 keys for fp32 inputs, and for 16-bit inputs with fewer than 32
- * query positions and no segment ids (decoding, which runs on a kernel of its
- * own that packs the group's heads x positions into 16-row products); 64 keys
- * for the other 16-bit calls. One launch computes every (query block, head
- * group, range) and
+ * tiles. Calls with fewer than 32 query positions and no segment ids
+ * (decoding) run on kernels of their own that pack the group's heads x
+ * positions into 16-row products: 16-key tiles for fp32 inputs, 32 keys for
+ * 16-bit inputs. Other calls: 32 keys for fp32 inputs, 64 keys for 16-bit
+ * inputs. One launch computes every (query block, head group, range) and
  * writes a normalised partial o (fp32) and its lse into `workspace`, and a
  * second kernel combines the parts with the log-sum-exp merge of
  * gqa_attn_merge, over n_split parts, then rounds o once to `dtype`.

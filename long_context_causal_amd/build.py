@@ -27,7 +27,7 @@ COMMON_FLAGS = [
     "-fvisibility=hidden",
 ]
 
-# MFMA accumulators in the VGPR file: in the fp32 kernel the O accumulator is
+# MFMA accumulators in the VGPR file: in the fp32 kernels the O accumulator is
 # also touched by VALU inside the loop (rescale) and fits the VGPR file; the
 # AGPR form made the compiler copy it between the two register files on every
 # iteration.
@@ -40,6 +40,7 @@ UNITS = {
     "fwd_f32.hip": VGPR_FORM,
     "fwd_h16.hip": [],
     "decode_h16.hip": [],
+    "decode_f32.hip": VGPR_FORM,
     "bwd_f32.hip": [],
     "bwd_h16.hip": [],
 }

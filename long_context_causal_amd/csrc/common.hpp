@@ -105,6 +105,19 @@ __device__ __forceinline__ float xor32_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// max / sum of a value over the 4 lanes l % 16 + 16 j (j = 0..3): the lanes
+// of one query row in the 16x16 product layouts (the decode kernels).
+__device__ __forceinline__ float xor16_max(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_sum(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float row4_max(float x) { return xor32_max(xor16_max(x)); }
+__device__ __forceinline__ float row4_sum(float x) { return xor32_sum(xor16_sum(x)); }
+
 __device__ __forceinline__ int wave_min_i(int x) {
   for (int s = 32; s >= 1; s >>= 1) x = min(x, __shfl_xor(x, s));
   return x;

@@ -1,0 +1,283 @@
+// decode_f32.hpp -- causal grouped-query attention forward for short query
+// blocks (decoding: fewer than 32 positions) over long key sequences, fp32
+// inputs and fp32 arithmetic throughout, on the 16x16x4 fp32 MFMA of gfx950.
+// This is the serving step of an fp32 model over a long state, which meets
+// the same grouped-query fallback (kev PR 202, "Not in this PR"). The
+// arithmetic is that of the fp32 long-block kernel (fwd_f32.hpp): scores in
+// the base-2 domain, online softmax with the lazy rescale, P kept in fp32 for
+// the PV product.
+//
+// Rows are packed as in the 16-bit decode kernel: the n_rep heads x Lq
+// positions of one KV head form blocks of 64 rows (row rr of a block is head
+// rr / Lq of the group at position rr % Lq; a block is one contiguous run of
+// rows of Q and of O). One workgroup = 4 waves x 16 rows = one block over one
+// key range (a split). Per key tile of 16 keys a wave forms S^T = K Q^T (64
+// products of 16 keys x 16 rows x 4 d), the softmax of its 16 rows and
+// O^T += V^T P^T (4 key steps x 16 d blocks). The long-block kernel's 32-row
+// tiles over 32 positions of 4 heads would leave most rows empty at these
+// lengths: it streams K and V at about 2 TB/s here.
+//
+// Operand layouts (16x16x4 fp32 product: A lane l = row l % 16, k l / 16; B
+// lane l = column l % 16, k l / 16; D lane l = rows 4 (l / 16) + e, column
+// l % 16). A lane (r16 = l % 16, g = l / 16) owns query row r16 of its wave.
+//   QK: product kk = 4 b + c contracts d = 16 b + 4 g + c over the lanes'
+//       k index g, so one 16-byte LDS read of key r16 at d 16 b + 4 g gives
+//       the A operands of 4 products, and Q (64 registers) is held as
+//       Q[r16][16 b + 4 g .. + 3] for b = 0..15.
+//   S^T: the lane holds keys 4 g + e (e = 0..3) of row r16.
+//   PV: key step e contracts keys 4 g + e, whose P the lane holds already
+//       (its own S^T value). D block nb = 4 a + c has row m at d
+//       64 a + 4 m + c, so one 16-byte read of key 4 g + e at d 64 a + 4 m
+//       gives the A operands of 4 blocks; the lane's O^T values then sit at
+//       d = 64 a + 16 g + 4 e + c (block 4 a + c, element e).
+//
+// LDS: a ring of 5 stages of one tile each (K then V, 16 keys x 1 KB each:
+// 32 KB; all 160 KB), 4 tiles' copies in flight while the 5th is computed, one
+// workgroup barrier per tile. Q (64 rows x 1 KB) arrives by the same kind of
+// copy into the last two stages, issued before the first three tiles' copies
+// so that one wait covers Q and tile 0; once every wave holds its Q in
+// registers (a second barrier) those two stages take tiles 3 and 4.
+#pragma once
+#include "common.hpp"
+
+namespace gqa {
+
+constexpr int kDecFWaves = 4;                          // waves per workgroup
+constexpr int kDecFRows = 16;                          // query rows per wave
+constexpr int kDecFBlockRows = kDecFWaves * kDecFRows;  // 64 packed rows per workgroup
+constexpr int kDecFBk = 16;                            // keys per tile
+constexpr int kDecFStages = 5;                         // LDS ring depth (tiles)
+constexpr int kDecFRow = kD * 4;                       // 1 KB: one key row
+constexpr int kDecFPart = kDecFBk * kDecFRow;          // 16 KB: the K (or V) part of a tile
+constexpr int kDecFStage = 2 * kDecFPart;              // 32 KB: K then V
+constexpr int kDecFCopies = kDecFBk / kDecFWaves;      // 1 KB copies (one key row each) per wave per part
+constexpr int kDecFQCopies = kDecFBlockRows / kDecFWaves;  // 1 KB Q row copies per wave (16)
+// copies a wave issues per tile; the wait at the top of a step leaves the
+// last three tiles' copies in flight
+constexpr int kDecFTileCopies = 2 * kDecFCopies;
+static_assert(kDecFTileCopies * (kDecFStages - 2) == 24, "the s_waitcnt immediates below assume 24");
+// before the loop: Q, then tiles 0..2; the first wait leaves tiles 1 and 2 in flight
+static_assert(2 * kDecFTileCopies == 16, "the first s_waitcnt immediate below assumes 16");
+static_assert(kDecFBlockRows * kDecFRow == 2 * kDecFStage, "Q of a row block fills the last two stages");
+constexpr float kDecFLazy = 8.0f;  // lazy-rescale threshold (log2 units), as in the long-block kernel
+
+// LDS image: 1 KB key rows of 64 chunks of 16 bytes; chunk c of key r is
+// stored at (c & ~15) | ((c & 15) ^ (r % 16)). A 16-byte-per-lane read of 16
+// keys at one chunk (the K read) and one of 16 chunks of one key (the V read)
+// then each meet all 64 banks once per 16 lanes.
+__device__ __forceinline__ uint32_t decf_chunk(int c, int key) {
+  return (uint32_t)((c & ~15) | ((c & 15) ^ (key & 15)));
+}
+
+struct DecFSmem {
+  __attribute__((aligned(16))) char stage[kDecFStages][kDecFStage];
+};
+
+typedef __attribute__((address_space(3))) const char decf_lds_cchar;
+typedef __attribute__((address_space(3))) const f32x4 decf_lds_f32x4;
+
+__global__ __launch_bounds__(kDecFWaves * 64) void decode_f32_kernel(FwdParams p) {
+  __shared__ DecFSmem sm;
+  const int wave = wave_id(), lane = lane_id();
+  const int r16 = lane & 15, g = lane >> 4;
+
+  // which (batch, KV head), row block and key split this workgroup owns
+  const int n_split = p.n_split > 1 ? p.n_split : 1;
+  const int split = (int)blockIdx.x % n_split;
+  const int rest = (int)blockIdx.x / n_split;
+  const int rb = rest % p.n_qb;
+  const int bh = rest / p.n_qb;
+  const int b = bh / p.Hkv, kvh = bh % p.Hkv;
+  // packed rows of the group (n_rep <= 16 heads x Lq < 32 positions: 32-bit)
+  const int R = p.n_rep * (int)p.Lq;
+  const int row0 = rb * kDecFBlockRows;
+  const int64_t grow0 = ((int64_t)b * p.Hq + (int64_t)kvh * p.n_rep) * p.Lq;  // global row of packed row 0
+
+  // this lane's row (wave rows 16 wave .. + 15) and its last visible key; a
+  // row past the group's end (its Q reads as zeros) writes nothing
+  const int rr = row0 + wave * kDecFRows + r16;
+  const bool row_ok = rr < R;
+  const int64_t pos = row_ok ? (int64_t)(rr % (int)p.Lq) : 0;
+  const int64_t kv_end = p.causal ? min(p.Lk, p.q_offset + p.Lq) : p.Lk;
+  const int lim = (int)(p.causal ? min(p.q_offset + pos, p.Lk - 1) : p.Lk - 1);
+  // tiles from this key on hold a key hidden from some row (causal or past Lk)
+  const int mask_from = (int)(p.causal ? min(p.q_offset, p.Lk - 1) : p.Lk - 1);
+  const int n_tiles = (int)((kv_end + kDecFBk - 1) / kDecFBk);
+  const int t_lo = p.n_split > 1 ? split * p.split_tiles : 0;
+  const int t_hi = p.n_split > 1 ? min(n_tiles, t_lo + p.split_tiles) : n_tiles;
+  const int n = max(0, t_hi - t_lo);
+
+  const int64_t kv_head = (int64_t)b * p.Hkv + kvh;
+  const char* kbase = (const char*)p.k + kv_head * p.Lk * kDecFRow;
+  const char* vbase = (const char*)p.v + kv_head * p.Lk * kDecFRow;
+
+  // per-lane copy offsets: copy it of this wave, in either part, is key row
+  // kDecFCopies wave + it (of Q: row kDecFQCopies wave + it); lane l writes
+  // its LDS chunk l, fetched from the global chunk stored there
+  uint32_t ldo[kDecFCopies], ldq[kDecFQCopies];
+#pragma unroll
+  for (int it = 0; it < kDecFCopies; ++it) {
+    const int key = kDecFCopies * wave + it;
+    ldo[it] = (uint32_t)key * kDecFRow + (decf_chunk(lane, key) << 4);
+  }
+#pragma unroll
+  for (int it = 0; it < kDecFQCopies; ++it) {
+    const int row = kDecFQCopies * wave + it;
+    ldq[it] = (uint32_t)row * kDecFRow + (decf_chunk(lane, row) << 4);
+  }
+  const uint32_t lds_stage0 = lds_addr(sm.stage[0]);
+  const uint32_t lds_q = lds_addr(sm.stage[kDecFStages - 2]);
+
+  // Copies of tile t (absolute) into stage st; a tile past this split's range
+  // (or Lk) copies from a resource of size 0, which writes zeros, so every
+  // step issues the same number of copies and the wait count stays fixed.
+  auto copy_tile = [&](int st, int t) {
+    const bool valid = t < t_hi;
+    const uint32_t keys = valid ? min((uint32_t)p.Lk - (uint32_t)t * kDecFBk, (uint32_t)kDecFBk) : 0u;
+    const uint64_t off = valid ? (uint64_t)(uint32_t)t * kDecFPart : 0u;
+    const rsrc_t rk = make_rsrc(kbase + off, keys * kDecFRow);
+    const rsrc_t rv = make_rsrc(vbase + off, keys * kDecFRow);
+    const uint32_t dst = lds_stage0 + (uint32_t)st * kDecFStage + (uint32_t)(kDecFCopies * wave) * kDecFRow;
+#pragma unroll
+    for (int it = 0; it < kDecFCopies; ++it) {
+      buf2lds16_imm(rk, ldo[it], dst, (uint32_t)it * kDecFRow);
+      buf2lds16_imm(rv, ldo[it], dst + kDecFPart, (uint32_t)it * kDecFRow);
+    }
+  };
+  // Q of the block (rows past the group's end read as zeros) into the last
+  // two stages, then tiles 0..2 into stages 0..2
+  {
+    const int rows = min(kDecFBlockRows, R - row0);
+    const rsrc_t rq = make_rsrc((const float*)p.q + (grow0 + row0) * kD, (uint32_t)rows * kDecFRow);
+    const uint32_t dst = lds_q + (uint32_t)(kDecFQCopies * wave) * kDecFRow;
+#pragma unroll
+    for (int it = 0; it < kDecFQCopies; ++it) buf2lds16_imm(rq, ldq[it], dst, (uint32_t)it * kDecFRow);
+  }
+#pragma unroll
+  for (int j = 0; j < kDecFStages - 2; ++j) copy_tile(j, t_lo + j);
+
+  // LDS read addresses (stage 0; a stage adds st * 32 KB). K: key r16, chunk
+  // 4 bb + g (bb = 0..15) at 256 (bb / 4) + 16 ((4 (bb % 4) + g) ^ r16). V, key
+  // step e: key 4 g + e, chunk 16 a + r16 at 256 a + 16 (r16 ^ (4 g + e)).
+  decf_lds_cchar* const st0 = (decf_lds_cchar*)sm.stage[0];
+  decf_lds_cchar* kr[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) kr[j] = st0 + r16 * kDecFRow + (((4 * j + g) ^ r16) << 4);
+  decf_lds_cchar* vr[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int key = 4 * g + e;
+    vr[e] = st0 + kDecFPart + key * kDecFRow + ((r16 ^ key) << 4);
+  }
+
+  asm volatile("s_waitcnt vmcnt(16)" ::: "memory");  // this wave's Q and tile-0 copies have landed
+  __syncthreads();                                    // ... and every wave's
+
+  // Q as the B operand: qf[b] = Q[row 16 wave + r16][16 b + 4 g .. + 3]
+  f32x4 qf[16];
+  {
+    decf_lds_cchar* qb = (decf_lds_cchar*)sm.stage[kDecFStages - 2] + (wave * kDecFRows + r16) * kDecFRow;
+#pragma unroll
+    for (int bb = 0; bb < 16; ++bb)
+      qf[bb] = *(decf_lds_f32x4*)(qb + ((bb >> 2) << 8) + (((4 * (bb & 3) + g) ^ r16) << 4));
+    // every wave's Q is in registers before the first copy into those stages
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+
+  const float sl2 = p.scale_log2;
+  float m = -INFINITY, m_use = 0.f, l = 0.f;
+  f32x4 acc[16];
+#pragma unroll
+  for (int nb = 0; nb < 16; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int i = 0, st = 0; i < n; ++i, st = st == kDecFStages - 1 ? 0 : st + 1) {
+    if (i > 0) {
+      asm volatile("s_waitcnt vmcnt(24)" ::: "memory");  // tile i's copies have landed
+      __syncthreads();  // ... for every wave; the stage of tile i - 1 is free
+    }
+    if (i == 0) copy_tile(kDecFStages - 2, t_lo + kDecFStages - 2);  // tile 3 into the other Q stage
+    copy_tile(st == 0 ? kDecFStages - 1 : st - 1, t_lo + i + kDecFStages - 1);
+    const int t = t_lo + i;
+    const int so = st * kDecFStage;
+
+    // All 16 K reads of the tile go out before the first product and are
+    // waited for once.
+    f32x4 kf[16];
+#pragma unroll
+    for (int bb = 0; bb < 16; ++bb) kf[bb] = *(decf_lds_f32x4*)(kr[bb & 3] + so + ((bb >> 2) << 8));
+    asm volatile("" : "+v"(kf[0]), "+v"(kf[1]), "+v"(kf[2]), "+v"(kf[3]), "+v"(kf[4]), "+v"(kf[5]), "+v"(kf[6]),
+                 "+v"(kf[7]), "+v"(kf[8]), "+v"(kf[9]), "+v"(kf[10]), "+v"(kf[11]), "+v"(kf[12]), "+v"(kf[13]),
+                 "+v"(kf[14]), "+v"(kf[15]));
+    // S^T = K Q^T: s[e] is key 4 g + e of row r16
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int bb = 0; bb < 16; ++bb)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) s = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[bb][c], qf[bb][c], s, 0, 0, 0);
+    // the V reads do not depend on P: they go out now and land during the softmax
+    f32x4 vf[4][4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) vf[e][a] = *(decf_lds_f32x4*)(vr[e] + so + (a << 8));
+    if (t * kDecFBk + kDecFBk - 1 > mask_from) {
+      const int k0 = t * kDecFBk + 4 * g;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s[e] = k0 + e <= lim ? s[e] : -INFINITY;
+    }
+    // row max over the 4 lanes of the row, then the lazy update (the running
+    // max moves only when a row's max grows by more than 8 in log2 units)
+    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    mx = row4_max(mx) * sl2;
+    if (mx > m + kDecFLazy) {
+      const float alpha = fast_exp2(m - mx);  // 0 while m is -inf
+      m = mx;
+      m_use = mx;
+#pragma unroll
+      for (int nb = 0; nb < 16; ++nb) acc[nb] *= alpha;
+      l *= alpha;
+    }
+    float pe[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pe[e] = fast_exp2(fmaf(s[e], sl2, -m_use));
+    l += (pe[0] + pe[1]) + (pe[2] + pe[3]);
+
+    // O^T += V^T P^T: key step e, d block nb = 4 a + c
+    asm volatile("" : "+v"(vf[0][0]), "+v"(vf[0][1]), "+v"(vf[0][2]), "+v"(vf[0][3]), "+v"(vf[1][0]),
+                 "+v"(vf[1][1]), "+v"(vf[1][2]), "+v"(vf[1][3]), "+v"(vf[2][0]), "+v"(vf[2][1]), "+v"(vf[2][2]),
+                 "+v"(vf[2][3]), "+v"(vf[3][0]), "+v"(vf[3][1]), "+v"(vf[3][2]), "+v"(vf[3][3]));
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          acc[4 * a + c] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf[e][a][c], pe[e], acc[4 * a + c], 0, 0, 0);
+  }
+  // the zero copies of the tiles past the range are still in flight
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  // epilogue: lane holds O[row r16][64 a + 16 g + 4 e + c] in acc[4 a + c][e]
+  const float l_tot = row4_sum(l);
+  if (row_ok) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float lse = l_tot > 0.f ? (m_use + log2f(l_tot)) * 0.69314718055994530942f : -INFINITY;
+    const int64_t grow = grow0 + rr;
+    float* op = p.n_split > 1 ? p.o_part + ((int64_t)split * p.part_rows + grow) * kD : (float*)p.o + grow * kD;
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        *(f32x4*)(op + 64 * a + 16 * g + 4 * e) = f32x4{acc[4 * a][e] * inv, acc[4 * a + 1][e] * inv,
+                                                        acc[4 * a + 2][e] * inv, acc[4 * a + 3][e] * inv};
+    if (g == 0) {
+      if (p.n_split > 1)
+        p.lse_part[(int64_t)split * p.part_rows + grow] = lse;
+      else
+        p.lse[grow] = lse;
+    }
+  }
+}
+
+}  // namespace gqa

@@ -75,19 +75,6 @@ struct Dec16<_Float16> {
   }
 };
 
-// max / sum of a value over the 4 lanes l % 16 + 16 j (j = 0..3): the lanes
-// of one query row in the 16x16 product layouts.
-__device__ __forceinline__ float xor16_max(float x) {
-  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float xor16_sum(float x) {
-  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float row4_max(float x) { return xor32_max(xor16_max(x)); }
-__device__ __forceinline__ float row4_sum(float x) { return xor32_sum(xor16_sum(x)); }
-
 typedef __attribute__((address_space(3))) const char dec_lds_cchar;
 typedef __attribute__((address_space(3))) s16x4 dec_lds_s16x4;
 

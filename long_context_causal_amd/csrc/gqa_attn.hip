@@ -28,8 +28,12 @@ bool is_pow2_rep(int64_t r) { return r == 1 || r == 2 || r == 4 || r == 8 || r =
 // ids, fewer than 32 query positions, and key counts whose 32-key tile ends
 // stay below 2^31 (its tile arithmetic is 32-bit).
 bool decode_shape(int dtype, int64_t Lq, int64_t Lk, bool seg) {
-  return dtype != GQA_F32 && !seg && Lq < gqa::kDecodeMaxLq && Lk < ((int64_t)1 << 31) - 64;
+  (void)dtype;  // every input type has a decode kernel
+  return !seg && Lq < gqa::kDecodeMaxLq && Lk < ((int64_t)1 << 31) - 64;
 }
+
+// Keys per tile of the decode kernel of an input type.
+int64_t decode_tile_keys(int dtype) { return dtype == GQA_F32 ? gqa::kTileKeysDecF32 : gqa::kTileKeysDec; }
 
 // split-KV: the most splits one launch takes, and the workgroup count the
 // recommended split count aims at: one per compute unit (the forward kernels'
@@ -96,7 +100,10 @@ static int fwd_plan(gqa::FwdParams& p, const void* q, const void* k, const void*
 }
 
 static hipError_t launch_fwd(const gqa::FwdParams& p, int dtype, hipStream_t s) {
-  if (p.decode) return dtype == GQA_BF16 ? gqa::launch_decode_bf16(p, s) : gqa::launch_decode_f16(p, s);
+  if (p.decode)
+    return dtype == GQA_F32    ? gqa::launch_decode_f32(p, s)
+           : dtype == GQA_BF16 ? gqa::launch_decode_bf16(p, s)
+                               : gqa::launch_decode_f16(p, s);
   return dtype == GQA_F32    ? gqa::launch_fwd_f32(p, s)
          : dtype == GQA_BF16 ? gqa::launch_fwd_bf16(p, s)
                              : gqa::launch_fwd_f16(p, s);
@@ -104,7 +111,7 @@ static hipError_t launch_fwd(const gqa::FwdParams& p, int dtype, hipStream_t s) 
 
 // Keys per tile of the kernel a plan launches (the unit of a split-KV range).
 static int64_t plan_tile_keys(const gqa::FwdParams& p, int dtype) {
-  return p.decode ? gqa::kTileKeysDec : dtype == GQA_F32 ? gqa::kTileKeysF32 : gqa::kTileKeysH16;
+  return p.decode ? decode_tile_keys(dtype) : dtype == GQA_F32 ? gqa::kTileKeysF32 : gqa::kTileKeysH16;
 }
 
 // Key tiles per split and the number of (non-empty) splits for a requested count.
@@ -137,7 +144,7 @@ GQA_API int gqa_attn_split_count(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq,
   const bool dec = decode_shape(dtype, Lq, Lk, false);
   const int64_t base = dec ? ((n_rep * Lq + gqa::kDecodeBlockRows - 1) / gqa::kDecodeBlockRows) * B * Hkv
                            : ((Lq + ppc - 1) / ppc) * B * Hkv * (n_rep / hpc);
-  const int64_t tile = dec ? gqa::kTileKeysDec : dtype == GQA_F32 ? gqa::kTileKeysF32 : gqa::kTileKeysH16;
+  const int64_t tile = dec ? decode_tile_keys(dtype) : dtype == GQA_F32 ? gqa::kTileKeysF32 : gqa::kTileKeysH16;
   const int64_t n_tiles = (Lk + tile - 1) / tile;
   // aim at one workgroup per compute unit, each split at least 4 tiles long
   int64_t n = (kSplitTargetWorkgroups + base - 1) / base;
@@ -383,4 +390,4 @@ GQA_API const char* gqa_attn_strerror(int code) {
   }
 }
 
-GQA_API int gqa_attn_version(void) { return (1 << 16) | 5; }
+GQA_API int gqa_attn_version(void) { return (1 << 16) | 6; }

@@ -21,13 +21,15 @@ hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream);
 hipError_t launch_fwd_f16(const FwdParams& p, hipStream_t stream);
 
-// Short query blocks (decoding) with 16-bit inputs and no segment ids: query
-// positions below which the decode kernel serves a launch, its packed rows per
-// workgroup and keys per tile (the unit of its split-KV ranges). Grid:
-// n_split x p.n_qb row blocks x p.G (= B * Hkv); p.n_qb = ceil(n_rep Lq / 64).
-constexpr int kDecodeMaxLq = 32, kDecodeBlockRows = 64, kTileKeysDec = 32;
+// Short query blocks (decoding) with no segment ids: query positions below
+// which a decode kernel serves a launch, its packed rows per workgroup and keys
+// per tile (the unit of its split-KV ranges: 32 for 16-bit inputs, 16 for
+// fp32). Grid: n_split x p.n_qb row blocks x p.G (= B * Hkv); p.n_qb =
+// ceil(n_rep Lq / 64).
+constexpr int kDecodeMaxLq = 32, kDecodeBlockRows = 64, kTileKeysDec = 32, kTileKeysDecF32 = 16;
 hipError_t launch_decode_bf16(const FwdParams& p, hipStream_t stream);
 hipError_t launch_decode_f16(const FwdParams& p, hipStream_t stream);
+hipError_t launch_decode_f32(const FwdParams& p, hipStream_t stream);
 
 // Backward: waves per workgroup and query rows per wave of the dQ kernel, keys
 // per workgroup of the dK/dV kernel (host plan).

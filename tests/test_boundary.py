@@ -45,7 +45,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_strerror():
-    assert gqa.version() == (1, 5)
+    assert gqa.version() == (1, 6)
     msgs = [gqa.strerror(c) for c in range(8)]
     assert len(set(msgs)) == 8 and msgs[0] == "success"
     assert "unknown" in gqa.strerror(99)
@@ -152,22 +152,31 @@ def test_split_workspace_and_count():
     # workspace: n_split * B * Hq * Lq * (D + 1) fp32 values
     assert gqa.split_workspace(2, 16, 100, 256, 8) == 8 * 2 * 16 * 100 * 257 * 4
     assert gqa.split_workspace(1, 16, 100, 256, 0) == 0
-    # one decode row over 60,926 keys (bf16, 64-key tiles): 4 workgroups without
-    # splits, so the count aims at 256 workgroups: 64 ranges of >= 4 tiles
+    # one decode row over 60,926 keys (bf16 decode kernel, 32-key tiles): 4
+    # workgroups without splits, so the count aims at 256 workgroups: 64
+    # ranges of >= 4 tiles
     assert gqa.split_count(1, 16, 4, 1, 60926, gqa.GQA_BF16) == 64
     # the 30k fp32 forward already launches 3,808 workgroups
     assert gqa.split_count(1, 16, 4, 30468, 30468, gqa.GQA_F32) == 1
-    # short keys: at most a quarter of the tile count (1000 keys = 32 tiles of 32)
-    assert gqa.split_count(1, 16, 4, 1, 1000, gqa.GQA_F32) == 8
+    # short keys: at most a quarter of the tile count (fp32 decode kernel:
+    # 1000 keys = 63 tiles of 16)
+    assert gqa.split_count(1, 16, 4, 1, 1000, gqa.GQA_F32) == 15
+    # fp32 rows past the decode bound (32 positions) take the long-block
+    # kernel's 32-key tiles: 32 rows = one block of 4 workgroups, 1000 keys =
+    # 32 tiles, at most 8 ranges
+    assert gqa.split_count(1, 16, 4, 32, 1000, gqa.GQA_F32) == 8
     # 16-bit decode shapes (Lq < 32) count the decode kernel's workgroups: row
     # blocks of 64 packed (head, position) rows per KV head. 16 heads per KV
     # head x 31 positions = 496 rows = 8 blocks: 32 workgroups per split, so 8
     # splits fill 256; 16 decode rows (64 rows, one block): 64 splits
     assert gqa.split_count(1, 64, 4, 31, 60926, gqa.GQA_BF16) == 8
     assert gqa.split_count(1, 16, 4, 16, 60926, gqa.GQA_F16) == 64
+    assert gqa.split_count(1, 16, 4, 16, 60926, gqa.GQA_F32) == 64
     # 32-key tiles: 200 keys = 7 tiles, at most a quarter of them (1)
     assert gqa.split_count(1, 16, 4, 16, 200, gqa.GQA_BF16) == 1
     assert gqa.split_count(1, 16, 4, 16, 260, gqa.GQA_BF16) == 2
+    # 16-key tiles (fp32): 200 keys = 13 tiles, a quarter of them (3)
+    assert gqa.split_count(1, 16, 4, 16, 200, gqa.GQA_F32) == 3
 
 
 def test_python_binding_rejects_host_tensors():

@@ -1,16 +1,18 @@
-"""Short query blocks (decoding: fewer than 32 positions) with 16-bit inputs
-and no segment ids: the launches the packed-row decode kernel serves, through
-gqa_attn_fwd and gqa_attn_fwd_split, against the fp64 oracle, every output
-row.
+"""Short query blocks (decoding: fewer than 32 positions) with no segment
+ids: the launches the packed-row decode kernels serve (fp32, and 16-bit
+inputs), through gqa_attn_fwd and gqa_attn_fwd_split, against the fp64
+oracle, every output row.
 
-The kernel packs the query rows of one KV head (n_rep heads x Lq positions)
+The kernels pack the query rows of one KV head (n_rep heads x Lq positions)
 into blocks of 64, 16 per wave, so the cases vary what that packing meets:
 group sizes 1..16 and Lq 1..31 (a wave's 16 rows spanning several heads, a
 last block cut short, several blocks per head), causal rows whose visible
-keys end before, at and past the key sequence's end, ragged key counts (32-key
-tiles), B = 2, and split counts from 1 to more splits than tiles.
+keys end before, at and past the key sequence's end, ragged key counts (16-key
+tiles in fp32, 32-key tiles in 16-bit; a ring of 4 tiles in flight), B = 2,
+and split counts from 1 to more splits than tiles.
 
-Bars as for the forward: max|do| <= 2e-2 (bf16) / 2.5e-3 (fp16), max|dlse| <= 1e-4.
+Bars as for the forward: max|do| <= 2e-5 (fp32) / 2e-2 (bf16) / 2.5e-3 (fp16),
+max|dlse| <= 1e-4.
 """
 import numpy as np
 import pytest
@@ -23,23 +25,24 @@ from gpu_util import TOL_O, compare, to_dev
 
 pytestmark = pytest.mark.gpu
 
-DT = ["bf16", "f16"]
+DT = ["f32", "bf16", "f16"]
 
 
-def check(x, label, n_split=None, unsplit=True):
+def check(x, label, n_split=None, unsplit=True, tol_scale=1.0):
     """Oracle check of gqa_attn_fwd_split (at n_split; None = the library's
-    count) and, if asked, of gqa_attn_fwd on the same inputs."""
+    count) and, if asked, of gqa_attn_fwd on the same inputs (tol_scale as in
+    gpu_util.compare)."""
     print("case:", label, "n_split", n_split, flush=True)
     q, k, v = to_dev(x)
     kw = dict(causal=x.causal, q_offset=x.q_offset)
     o_ref, l_ref = oracle.attn(x.q, x.k, x.v, causal=x.causal, q_offset=x.q_offset)
     o, lse = gqa.fwd_split(q, k, v, n_split=n_split, **kw)
     torch.cuda.synchronize()
-    compare(o, lse, o_ref, l_ref, x.dtype, label="%s split %s" % (label, n_split))
+    compare(o, lse, o_ref, l_ref, x.dtype, label="%s split %s" % (label, n_split), tol_scale=tol_scale)
     if unsplit:
         o1, l1 = gqa.fwd(q, k, v, **kw)
         torch.cuda.synchronize()
-        compare(o1, l1, o_ref, l_ref, x.dtype, label="%s unsplit" % label)
+        compare(o1, l1, o_ref, l_ref, x.dtype, label="%s unsplit" % label, tol_scale=tol_scale)
 
 
 @pytest.mark.parametrize("dtype", DT)
@@ -65,10 +68,11 @@ def test_causal_ends(dtype, q_offset):
 
 
 @pytest.mark.parametrize("dtype", DT)
-@pytest.mark.parametrize("Lk", [1, 2, 31, 32, 33, 95])
+@pytest.mark.parametrize("Lk", [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 95, 129])
 def test_short_key_sequences(dtype, Lk):
-    """Fewer keys than one ring of tiles (4 x 32), including a single key;
-    splits past the last tile are empty and merge as nothing."""
+    """About one ring of tiles (4 x 16 keys in fp32, 4 x 32 in 16-bit) and
+    less, including a single key; splits past the last tile are empty and
+    merge as nothing."""
     Lq = 3
     x = synth.gqa(1, 8, 2, Lq, Lk, seed=330 + Lk, dtype=dtype, q_offset=max(Lk - Lq, 0))
     check(x, "Lk=%d %s" % (Lk, dtype), n_split=4)
@@ -84,33 +88,37 @@ def test_noncausal_batch_two(dtype):
 @pytest.mark.parametrize("n_split", [1, 2, 64, 1000])
 def test_split_counts(dtype, n_split):
     """The same 16 rows over 4,500 keys at 1, 2, 64 and 1,000 requested splits
-    (141 tiles: 1,000 requests give 141 one-tile ranges)."""
+    (141 tiles of 32 keys, 282 of 16: 1,000 requests give one-tile ranges)."""
     x = synth.gqa(1, 16, 4, 16, 4500, seed=350, dtype=dtype, q_offset=4500 - 16)
     check(x, "splits %d %s" % (n_split, dtype), n_split=n_split, unsplit=n_split == 1)
 
 
-def test_peaky_scores_rescale():
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_peaky_scores_rescale(dtype):
     """Query rows scaled by 6 (logit standard deviation about 6): the running
-    max moves often, and the lazy rescale of O, l and lr is exercised."""
-    x0 = synth.gqa(1, 16, 4, 16, 3000, seed=360, q_offset=3000 - 16)
-    x = synth.Inputs(x0.q * np.float32(6.0), x0.k, x0.v, "bf16", q_offset=3000 - 16)
-    check(x, "peaky bf16", n_split=6)
+    max moves often, and the lazy rescale of O, l (and lr) is exercised. The
+    fp32 bars scale with the logits (gpu_util.compare)."""
+    x0 = synth.gqa(1, 16, 4, 16, 3000, seed=360, dtype=dtype, q_offset=3000 - 16)
+    x = synth.Inputs(x0.q * np.float32(6.0), x0.k, x0.v, dtype, q_offset=3000 - 16)
+    check(x, "peaky " + dtype, n_split=6, tol_scale=6.0 if dtype == "f32" else 1.0)
 
 
-def test_full_size_decode_every_row():
-    """16 decode rows after 60,926 bf16 keys, at the library's split count
-    (the measured decode workload): every row of every head."""
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_full_size_decode_every_row(dtype):
+    """16 decode rows after 60,926 keys, at the library's split count (the
+    measured decode workloads): every row of every head."""
     Lk = 60926
-    x = synth.gqa(1, 16, 4, 16, Lk, seed=370, dtype="bf16", q_offset=Lk - 16)
-    check(x, "full size decode bf16", n_split=None, unsplit=False)
+    x = synth.gqa(1, 16, 4, 16, Lk, seed=370, dtype=dtype, q_offset=Lk - 16)
+    check(x, "full size decode " + dtype, n_split=None, unsplit=False)
 
 
-def test_repeat_calls_identical():
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_repeat_calls_identical(dtype):
     """The kernel's result does not depend on what an earlier call left in LDS
     or in the workspace: two calls on different inputs, then the first again,
     give the first result bit for bit."""
-    xa = synth.gqa(1, 16, 4, 16, 2500, seed=380, dtype="bf16", q_offset=2484)
-    xb = synth.gqa(1, 16, 4, 16, 2500, seed=381, dtype="bf16", q_offset=2484)
+    xa = synth.gqa(1, 16, 4, 16, 2500, seed=380, dtype=dtype, q_offset=2484)
+    xb = synth.gqa(1, 16, 4, 16, 2500, seed=381, dtype=dtype, q_offset=2484)
     qa, ka, va = to_dev(xa)
     qb, kb, vb = to_dev(xb)
     oa, la = gqa.fwd_split(qa, ka, va, q_offset=2484, n_split=9)
