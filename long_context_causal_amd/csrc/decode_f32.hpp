@@ -32,10 +32,12 @@
 //       d = 64 a + 16 g + 4 e + c (block 4 a + c, element e).
 //
 // LDS: a ring of 5 stages of one tile each (K then V, 16 keys x 1 KB each:
-// 32 KB; all 160 KB), 4 tiles' copies in flight while the 5th is computed, one
-// workgroup barrier per tile. Q (64 rows x 1 KB) arrives by the same kind of
-// copy into the last two stages, issued before the first three tiles' copies
-// so that one wait covers Q and tile 0; once every wave holds its Q in
+// 32 KB; all 160 KB) and one workgroup barrier per tile. In step i the V reads
+// of tile i go out between the score products and the K reads of tile i + 1
+// between the PV products (so neither waits for the LDS), while tiles i + 2 ..
+// i + 4 are in flight. Q (64 rows x 1 KB) arrives by the same kind of copy
+// into the last two stages, issued before the first three tiles' copies so
+// that one wait covers Q and tiles 0 and 1; once every wave holds its Q in
 // registers (a second barrier) those two stages take tiles 3 and 4.
 #pragma once
 #include "common.hpp"
@@ -51,13 +53,12 @@ constexpr int kDecFRow = kD * 4;                       // 1 KB: one key row
 constexpr int kDecFPart = kDecFBk * kDecFRow;          // 16 KB: the K (or V) part of a tile
 constexpr int kDecFStage = 2 * kDecFPart;              // 32 KB: K then V
 constexpr int kDecFCopies = kDecFBk / kDecFWaves;      // 1 KB copies (one key row each) per wave per part
-constexpr int kDecFQCopies = kDecFBlockRows / kDecFWaves;  // 1 KB Q row copies per wave (16)
-// copies a wave issues per tile; the wait at the top of a step leaves the
-// last three tiles' copies in flight
+// copies a wave issues per tile; the wait at the top of step i leaves the
+// copies of tiles i + 2 and i + 3 in flight
 constexpr int kDecFTileCopies = 2 * kDecFCopies;
-static_assert(kDecFTileCopies * (kDecFStages - 2) == 24, "the s_waitcnt immediates below assume 24");
-// before the loop: Q, then tiles 0..2; the first wait leaves tiles 1 and 2 in flight
-static_assert(2 * kDecFTileCopies == 16, "the first s_waitcnt immediate below assumes 16");
+static_assert(kDecFTileCopies * (kDecFStages - 3) == 16, "the s_waitcnt immediates below assume 16");
+// before the loop: Q, then tiles 0..2; the first wait leaves tile 2 in flight
+static_assert(kDecFTileCopies == 8, "the first s_waitcnt immediate below assumes 8");
 static_assert(kDecFBlockRows * kDecFRow == 2 * kDecFStage, "Q of a row block fills the last two stages");
 constexpr float kDecFLazy = 8.0f;  // lazy-rescale threshold (log2 units), as in the long-block kernel
 
@@ -76,10 +77,25 @@ struct DecFSmem {
 typedef __attribute__((address_space(3))) const char decf_lds_cchar;
 typedef __attribute__((address_space(3))) const f32x4 decf_lds_f32x4;
 
+// DS (split d), for groups of at most 16 packed rows (one decode position of
+// a 4-head group, say): the 4 waves share the block's 16 rows and each owns a
+// quarter of d, 64 values. Per tile a wave forms its quarter's partial S^T (16
+// products), the partials meet through the LDS (each wave adds all four in the
+// same order, so every wave holds the same S^T and the same softmax state),
+// and the wave forms O^T for its quarter of d (16 products). Without DS, a
+// group of 16 rows would leave three waves idle and the fourth would carry all
+// 128 products of every tile. The exchange uses the current stage's K part,
+// whose K every wave read into registers in the step before.
+template <bool DS>
 __global__ __launch_bounds__(kDecFWaves * 64) void decode_f32_kernel(FwdParams p) {
   __shared__ DecFSmem sm;
+  constexpr int kBlockRows = DS ? kDecFRows : kDecFBlockRows;  // packed rows per workgroup
+  constexpr int kQCopies = kBlockRows / kDecFWaves;           // 1 KB Q row copies per wave
+  constexpr int kQ = DS ? 4 : 16;                             // 16-byte Q (and K) reads per lane
+  constexpr int kNB = DS ? 4 : 16;                            // O^T blocks of 16 d per wave
   const int wave = wave_id(), lane = lane_id();
   const int r16 = lane & 15, g = lane >> 4;
+  const int dq = DS ? wave : 0;  // this wave's quarter of d (DS)
 
   // which (batch, KV head), row block and key split this workgroup owns
   const int n_split = p.n_split > 1 ? p.n_split : 1;
@@ -90,12 +106,14 @@ __global__ __launch_bounds__(kDecFWaves * 64) void decode_f32_kernel(FwdParams p
   const int b = bh / p.Hkv, kvh = bh % p.Hkv;
   // packed rows of the group (n_rep <= 16 heads x Lq < 32 positions: 32-bit)
   const int R = p.n_rep * (int)p.Lq;
-  const int row0 = rb * kDecFBlockRows;
+  const int row0 = rb * kBlockRows;
   const int64_t grow0 = ((int64_t)b * p.Hq + (int64_t)kvh * p.n_rep) * p.Lq;  // global row of packed row 0
 
-  // this lane's row (wave rows 16 wave .. + 15) and its last visible key; a
-  // row past the group's end (its Q reads as zeros) writes nothing
-  const int rr = row0 + wave * kDecFRows + r16;
+  // this lane's row (DS: row r16 of the block in every wave; else rows
+  // 16 wave .. + 15) and its last visible key; a row past the group's end (its
+  // Q reads as zeros) writes nothing
+  const int rw = DS ? r16 : wave * kDecFRows + r16;  // row within the block
+  const int rr = row0 + rw;
   const bool row_ok = rr < R;
   const int64_t pos = row_ok ? (int64_t)(rr % (int)p.Lq) : 0;
   const int64_t kv_end = p.causal ? min(p.Lk, p.q_offset + p.Lq) : p.Lk;
@@ -112,17 +130,17 @@ __global__ __launch_bounds__(kDecFWaves * 64) void decode_f32_kernel(FwdParams p
   const char* vbase = (const char*)p.v + kv_head * p.Lk * kDecFRow;
 
   // per-lane copy offsets: copy it of this wave, in either part, is key row
-  // kDecFCopies wave + it (of Q: row kDecFQCopies wave + it); lane l writes
-  // its LDS chunk l, fetched from the global chunk stored there
-  uint32_t ldo[kDecFCopies], ldq[kDecFQCopies];
+  // kDecFCopies wave + it (of Q: row kQCopies wave + it); lane l writes its
+  // LDS chunk l, fetched from the global chunk stored there
+  uint32_t ldo[kDecFCopies], ldq[kQCopies];
 #pragma unroll
   for (int it = 0; it < kDecFCopies; ++it) {
     const int key = kDecFCopies * wave + it;
     ldo[it] = (uint32_t)key * kDecFRow + (decf_chunk(lane, key) << 4);
   }
 #pragma unroll
-  for (int it = 0; it < kDecFQCopies; ++it) {
-    const int row = kDecFQCopies * wave + it;
+  for (int it = 0; it < kQCopies; ++it) {
+    const int row = kQCopies * wave + it;
     ldq[it] = (uint32_t)row * kDecFRow + (decf_chunk(lane, row) << 4);
   }
   const uint32_t lds_stage0 = lds_addr(sm.stage[0]);
@@ -145,82 +163,104 @@ __global__ __launch_bounds__(kDecFWaves * 64) void decode_f32_kernel(FwdParams p
     }
   };
   // Q of the block (rows past the group's end read as zeros) into the last
-  // two stages, then tiles 0..2 into stages 0..2
+  // two stages (DS: the first 16 KB of them), then tiles 0..2 into stages 0..2
   {
-    const int rows = min(kDecFBlockRows, R - row0);
+    const int rows = min(kBlockRows, R - row0);
     const rsrc_t rq = make_rsrc((const float*)p.q + (grow0 + row0) * kD, (uint32_t)rows * kDecFRow);
-    const uint32_t dst = lds_q + (uint32_t)(kDecFQCopies * wave) * kDecFRow;
+    const uint32_t dst = lds_q + (uint32_t)(kQCopies * wave) * kDecFRow;
 #pragma unroll
-    for (int it = 0; it < kDecFQCopies; ++it) buf2lds16_imm(rq, ldq[it], dst, (uint32_t)it * kDecFRow);
+    for (int it = 0; it < kQCopies; ++it) buf2lds16_imm(rq, ldq[it], dst, (uint32_t)it * kDecFRow);
   }
 #pragma unroll
   for (int j = 0; j < kDecFStages - 2; ++j) copy_tile(j, t_lo + j);
 
   // LDS read addresses (stage 0; a stage adds st * 32 KB). K: key r16, chunk
   // 4 bb + g (bb = 0..15) at 256 (bb / 4) + 16 ((4 (bb % 4) + g) ^ r16). V, key
-  // step e: key 4 g + e, chunk 16 a + r16 at 256 a + 16 (r16 ^ (4 g + e)).
+  // step e: key 4 g + e, chunk 16 a + r16 at 256 a + 16 (r16 ^ (4 g + e)). DS
+  // reads quarter dq of d only: bb = 4 dq + j, a = dq.
   decf_lds_cchar* const st0 = (decf_lds_cchar*)sm.stage[0];
   decf_lds_cchar* kr[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) kr[j] = st0 + r16 * kDecFRow + (((4 * j + g) ^ r16) << 4);
+  for (int j = 0; j < 4; ++j) kr[j] = st0 + r16 * kDecFRow + (((4 * j + g) ^ r16) << 4) + (dq << 8);
   decf_lds_cchar* vr[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int key = 4 * g + e;
-    vr[e] = st0 + kDecFPart + key * kDecFRow + ((r16 ^ key) << 4);
+    vr[e] = st0 + kDecFPart + key * kDecFRow + ((r16 ^ key) << 4) + (dq << 8);
   }
 
-  asm volatile("s_waitcnt vmcnt(16)" ::: "memory");  // this wave's Q and tile-0 copies have landed
-  __syncthreads();                                    // ... and every wave's
+  asm volatile("s_waitcnt vmcnt(8)" ::: "memory");  // this wave's Q, tile-0 and tile-1 copies have landed
+  __syncthreads();                                   // ... and every wave's
 
-  // Q as the B operand: qf[b] = Q[row 16 wave + r16][16 b + 4 g .. + 3]
-  f32x4 qf[16];
+  // a wave whose 16 rows all lie past the group's end takes part in the
+  // copies and barriers only
+  const bool live = DS || row0 + wave * kDecFRows < R;
+  // Q as the B operand: qf[j] = Q[row rw][16 bb + 4 g .. + 3] (bb = j, or
+  // 4 dq + j with DS), held in AGPRs (read there by the score products); K of
+  // tile 0 into kf
+  f32x4 qf[kQ], kf[kQ];
   {
-    decf_lds_cchar* qb = (decf_lds_cchar*)sm.stage[kDecFStages - 2] + (wave * kDecFRows + r16) * kDecFRow;
+    decf_lds_cchar* qb = (decf_lds_cchar*)sm.stage[kDecFStages - 2] + rw * kDecFRow + (dq << 8);
 #pragma unroll
-    for (int bb = 0; bb < 16; ++bb)
-      qf[bb] = *(decf_lds_f32x4*)(qb + ((bb >> 2) << 8) + (((4 * (bb & 3) + g) ^ r16) << 4));
+    for (int j = 0; j < kQ; ++j) {
+      qf[j] = *(decf_lds_f32x4*)(qb + ((j >> 2) << 8) + (((4 * (j & 3) + g) ^ r16) << 4));
+      kf[j] = *(decf_lds_f32x4*)(kr[j & 3] + ((j >> 2) << 8));
+    }
     // every wave's Q is in registers before the first copy into those stages
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kQ; ++j) asm volatile("" : "+a"(qf[j]));
   }
 
   const float sl2 = p.scale_log2;
   float m = -INFINITY, m_use = 0.f, l = 0.f;
-  f32x4 acc[16];
+  f32x4 acc[kNB];
 #pragma unroll
-  for (int nb = 0; nb < 16; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int nb = 0; nb < kNB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // Step i: K of tile i is in kf (read during step i - 1); the V reads of tile
+  // i go out between the score products, the K reads of tile i + 1 between
+  // the PV products. Tiles i and i + 1 have landed at the top of the step;
+  // i + 2 .. i + 4 are in flight.
   for (int i = 0, st = 0; i < n; ++i, st = st == kDecFStages - 1 ? 0 : st + 1) {
     if (i > 0) {
-      asm volatile("s_waitcnt vmcnt(24)" ::: "memory");  // tile i's copies have landed
+      asm volatile("s_waitcnt vmcnt(16)" ::: "memory");  // tile i + 1's copies have landed
       __syncthreads();  // ... for every wave; the stage of tile i - 1 is free
     }
     if (i == 0) copy_tile(kDecFStages - 2, t_lo + kDecFStages - 2);  // tile 3 into the other Q stage
     copy_tile(st == 0 ? kDecFStages - 1 : st - 1, t_lo + i + kDecFStages - 1);
     const int t = t_lo + i;
     const int so = st * kDecFStage;
+    const int so1 = (st == kDecFStages - 1 ? 0 : st + 1) * kDecFStage;
+    if (!live) continue;
 
-    // All 16 K reads of the tile go out before the first product and are
-    // waited for once.
-    f32x4 kf[16];
+    // S^T = K Q^T: s[e] is key 4 g + e of row r16, summed as four chains (one
+    // per d offset c) added at the end; V read j (key step j / 4 and d blocks
+    // 4 (j % 4) .. + 3; DS: key step j, d blocks of quarter dq) goes out
+    // before score block j
+    f32x4 s4[4] = {};
+    f32x4 vf[kQ];
 #pragma unroll
-    for (int bb = 0; bb < 16; ++bb) kf[bb] = *(decf_lds_f32x4*)(kr[bb & 3] + so + ((bb >> 2) << 8));
-    asm volatile("" : "+v"(kf[0]), "+v"(kf[1]), "+v"(kf[2]), "+v"(kf[3]), "+v"(kf[4]), "+v"(kf[5]), "+v"(kf[6]),
-                 "+v"(kf[7]), "+v"(kf[8]), "+v"(kf[9]), "+v"(kf[10]), "+v"(kf[11]), "+v"(kf[12]), "+v"(kf[13]),
-                 "+v"(kf[14]), "+v"(kf[15]));
-    // S^T = K Q^T: s[e] is key 4 g + e of row r16
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < kQ; ++j) {
+      vf[j] = DS ? *(decf_lds_f32x4*)(vr[j] + so) : *(decf_lds_f32x4*)(vr[j >> 2] + so + ((j & 3) << 8));
 #pragma unroll
-    for (int bb = 0; bb < 16; ++bb)
+      for (int c = 0; c < 4; ++c) s4[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[j][c], qf[j][c], s4[c], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    f32x4 s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+    if (DS) {
+      // the four quarters' partial sums meet in the K part of this tile's
+      // stage (every wave read that K in the step before); each wave adds
+      // them in quarter order
+      float* const xw = (float*)sm.stage[st];
+      *(f32x4*)(xw + (wave * 64 + lane) * 4) = s;
+      __syncthreads();
+      f32x4 part[4];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) s = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[bb][c], qf[bb][c], s, 0, 0, 0);
-    // the V reads do not depend on P: they go out now and land during the softmax
-    f32x4 vf[4][4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-#pragma unroll
-      for (int a = 0; a < 4; ++a) vf[e][a] = *(decf_lds_f32x4*)(vr[e] + so + (a << 8));
+      for (int w = 0; w < 4; ++w) part[w] = w == wave ? s : *(const f32x4*)(xw + (w * 64 + lane) * 4);
+      s = ((part[0] + part[1]) + part[2]) + part[3];
+    }
     if (t * kDecFBk + kDecFBk - 1 > mask_from) {
       const int k0 = t * kDecFBk + 4 * g;
 #pragma unroll
@@ -235,43 +275,45 @@ __global__ __launch_bounds__(kDecFWaves * 64) void decode_f32_kernel(FwdParams p
       m = mx;
       m_use = mx;
 #pragma unroll
-      for (int nb = 0; nb < 16; ++nb) acc[nb] *= alpha;
+      for (int nb = 0; nb < kNB; ++nb) acc[nb] *= alpha;
       l *= alpha;
     }
     float pe[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) pe[e] = fast_exp2(fmaf(s[e], sl2, -m_use));
     l += (pe[0] + pe[1]) + (pe[2] + pe[3]);
+    __builtin_amdgcn_sched_barrier(0);
 
-    // O^T += V^T P^T: key step e, d block nb = 4 a + c
-    asm volatile("" : "+v"(vf[0][0]), "+v"(vf[0][1]), "+v"(vf[0][2]), "+v"(vf[0][3]), "+v"(vf[1][0]),
-                 "+v"(vf[1][1]), "+v"(vf[1][2]), "+v"(vf[1][3]), "+v"(vf[2][0]), "+v"(vf[2][1]), "+v"(vf[2][2]),
-                 "+v"(vf[2][3]), "+v"(vf[3][0]), "+v"(vf[3][1]), "+v"(vf[3][2]), "+v"(vf[3][3]));
+    // O^T += V^T P^T: key step e, d block 4 a + c (DS: a = dq, block c of the
+    // wave); K read j of tile i + 1 goes out before PV group j
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
+    for (int j = 0; j < kQ; ++j) {
+      kf[j] = *(decf_lds_f32x4*)(kr[j & 3] + so1 + ((j >> 2) << 8));
+      const int e = DS ? j : j >> 2, a = DS ? 0 : j & 3;
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          acc[4 * a + c] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf[e][a][c], pe[e], acc[4 * a + c], 0, 0, 0);
+      for (int c = 0; c < 4; ++c)
+        acc[4 * a + c] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf[j][c], pe[e], acc[4 * a + c], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
   // the zero copies of the tiles past the range are still in flight
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  // epilogue: lane holds O[row r16][64 a + 16 g + 4 e + c] in acc[4 a + c][e]
+  // epilogue: lane holds O[row][64 a + 16 g + 4 e + c] in acc[4 a + c][e] (DS:
+  // a = dq, in acc[c][e])
   const float l_tot = row4_sum(l);
-  if (row_ok) {
+  if (row_ok && live) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     const float lse = l_tot > 0.f ? (m_use + log2f(l_tot)) * 0.69314718055994530942f : -INFINITY;
     const int64_t grow = grow0 + rr;
     float* op = p.n_split > 1 ? p.o_part + ((int64_t)split * p.part_rows + grow) * kD : (float*)p.o + grow * kD;
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < kNB / 4; ++a)
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        *(f32x4*)(op + 64 * a + 16 * g + 4 * e) = f32x4{acc[4 * a][e] * inv, acc[4 * a + 1][e] * inv,
-                                                        acc[4 * a + 2][e] * inv, acc[4 * a + 3][e] * inv};
-    if (g == 0) {
+        *(f32x4*)(op + 64 * (a + dq) + 16 * g + 4 * e) = f32x4{acc[4 * a][e] * inv, acc[4 * a + 1][e] * inv,
+                                                               acc[4 * a + 2][e] * inv, acc[4 * a + 3][e] * inv};
+    if (g == 0 && (!DS || wave == 0)) {
       if (p.n_split > 1)
         p.lse_part[(int64_t)split * p.part_rows + grow] = lse;
       else
