@@ -589,7 +589,8 @@ def main():
     ap.add_argument("--only", default=None,
                     help="run one workload: f32-15231, f32-30468, f32-60926, bf16-60926, f16-60926, "
                          "seg-bf16-131072, noids-bf16-131072, branch-f32, bwd-f32-30468, bwd-bf16-60926, "
-                         "split-decode-bf16, split-branch-f32, cp-f32-30468")
+                         "split-decode-bf16, split-decode1-bf16, split-decode-f32, split-decode1-f32, "
+                         "split-branch-f32, cp-f32-30468")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (3 times) to calibrate HBM byte counters")
     ap.add_argument("--pmc-summary", nargs="+", metavar="DB",
@@ -639,6 +640,9 @@ def main():
     }
     split_workloads = {
         "split-decode-bf16": ("split-KV decode bf16 Lq=16 over Lk=60926", 16, 60926, "bf16"),
+        "split-decode1-bf16": ("split-KV decode bf16 Lq=1 over Lk=60926", 1, 60926, "bf16"),
+        "split-decode-f32": ("split-KV decode fp32 Lq=16 over Lk=60926", 16, 60926, "f32"),
+        "split-decode1-f32": ("split-KV decode fp32 Lq=1 over Lk=60926", 1, 60926, "f32"),
         "split-branch-f32": ("split-KV branch fp32 m=256 over S=30468 (Lk=30724)", 256, 30724, "f32"),
     }
     if args.only in split_workloads:
@@ -719,8 +723,9 @@ def main():
             xs = synth.gqa(1, HQ, HKV, Ls, seed=0, dtype=dts)
             secondary.append(run_bwd_workload(nm, xs, max(3, args.steps // 2), 2, torch, gqa, work, synth))
             del xs
-        # split-KV: 16 decode rows over the 64k state (bf16) and one 256-row
-        # branch over the 30k prefix (fp32)
+        # split-KV: 16 and 1 decode positions over the 64k state (bf16 and
+        # fp32, the fp32 server's step) and one 256-row branch over the 30k
+        # prefix (fp32)
         for nm, Lq_, Lk_, dts in split_workloads.values():
             xs = synth.gqa(1, HQ, HKV, Lq_, Lk_, seed=0, dtype=dts, q_offset=Lk_ - Lq_)
             secondary.append(run_split_workload(nm, xs, max(5, args.steps), 3, torch, gqa, work))
