@@ -77,25 +77,29 @@ struct DecFSmem {
 typedef __attribute__((address_space(3))) const char decf_lds_cchar;
 typedef __attribute__((address_space(3))) const f32x4 decf_lds_f32x4;
 
-// DS (split d), for groups of at most 16 packed rows (one decode position of
-// a 4-head group, say): the 4 waves share the block's 16 rows and each owns a
-// quarter of d, 64 values. Per tile a wave forms its quarter's partial S^T (16
-// products), the partials meet through the LDS (each wave adds all four in the
-// same order, so every wave holds the same S^T and the same softmax state),
-// and the wave forms O^T for its quarter of d (16 products). Without DS, a
-// group of 16 rows would leave three waves idle and the fourth would carry all
-// 128 products of every tile. The exchange uses the current stage's K part,
+// NDP (d parts: 1, 2 or 4): the 4 waves form 4 / NDP row blocks of 16 rows
+// times NDP parts of d, and a workgroup holds 64 / NDP packed rows. With
+// NDP > 1 the waves of one row block each form their part's partial S^T (64 /
+// NDP products per tile), the partials meet through the LDS (each of those
+// waves adds them in the same order, so they hold the same S^T and the same
+// softmax state), and each wave forms O^T for its part of d (64 / NDP
+// products). The launch takes NDP = 4 for groups of at most 16 rows (one
+// decode position of a 4-head group), 2 for at most 32, else 1: with NDP = 1
+// such groups would leave waves idle while each live wave carried all 128
+// products of every tile. The exchange uses the current stage's K part,
 // whose K every wave read into registers in the step before.
-template <bool DS>
+template <int NDP>
 __global__ __launch_bounds__(kDecFWaves * 64) void decode_f32_kernel(FwdParams p) {
+  static_assert(NDP == 1 || NDP == 2 || NDP == 4, "1, 2 or 4 parts of d");
   __shared__ DecFSmem sm;
-  constexpr int kBlockRows = DS ? kDecFRows : kDecFBlockRows;  // packed rows per workgroup
-  constexpr int kQCopies = kBlockRows / kDecFWaves;           // 1 KB Q row copies per wave
-  constexpr int kQ = DS ? 4 : 16;                             // 16-byte Q (and K) reads per lane
-  constexpr int kNB = DS ? 4 : 16;                            // O^T blocks of 16 d per wave
+  constexpr int kBlockRows = kDecFBlockRows / NDP;  // packed rows per workgroup
+  constexpr int kQCopies = kBlockRows / kDecFWaves;  // 1 KB Q row copies per wave
+  constexpr int kQ = 16 / NDP;                       // 16-byte Q (and K, and V) reads per lane per tile
+  constexpr int kNA = 4 / NDP;                       // 64-d groups a of O^T per wave
   const int wave = wave_id(), lane = lane_id();
   const int r16 = lane & 15, g = lane >> 4;
-  const int dq = DS ? wave : 0;  // this wave's quarter of d (DS)
+  const int dq = wave % NDP;  // this wave's part of d: 16-d blocks kQ dq .. + kQ - 1
+  const int rbw = wave / NDP;  // this wave's row block (16 rows) in the workgroup
 
   // which (batch, KV head), row block and key split this workgroup owns
   const int n_split = p.n_split > 1 ? p.n_split : 1;
@@ -109,10 +113,9 @@ __global__ __launch_bounds__(kDecFWaves * 64) void decode_f32_kernel(FwdParams p
   const int row0 = rb * kBlockRows;
   const int64_t grow0 = ((int64_t)b * p.Hq + (int64_t)kvh * p.n_rep) * p.Lq;  // global row of packed row 0
 
-  // this lane's row (DS: row r16 of the block in every wave; else rows
-  // 16 wave .. + 15) and its last visible key; a row past the group's end (its
-  // Q reads as zeros) writes nothing
-  const int rw = DS ? r16 : wave * kDecFRows + r16;  // row within the block
+  // this lane's row (row r16 of the wave's row block) and its last visible
+  // key; a row past the group's end (its Q reads as zeros) writes nothing
+  const int rw = rbw * kDecFRows + r16;  // row within the workgroup's block
   const int rr = row0 + rw;
   const bool row_ok = rr < R;
   const int64_t pos = row_ok ? (int64_t)(rr % (int)p.Lq) : 0;
@@ -163,7 +166,8 @@ __global__ __launch_bounds__(kDecFWaves * 64) void decode_f32_kernel(FwdParams p
     }
   };
   // Q of the block (rows past the group's end read as zeros) into the last
-  // two stages (DS: the first 16 KB of them), then tiles 0..2 into stages 0..2
+  // two stages (the first 64 / NDP KB of them), then tiles 0..2 into stages
+  // 0..2
   {
     const int rows = min(kBlockRows, R - row0);
     const rsrc_t rq = make_rsrc((const float*)p.q + (grow0 + row0) * kD, (uint32_t)rows * kDecFRow);
@@ -174,37 +178,38 @@ __global__ __launch_bounds__(kDecFWaves * 64) void decode_f32_kernel(FwdParams p
 #pragma unroll
   for (int j = 0; j < kDecFStages - 2; ++j) copy_tile(j, t_lo + j);
 
-  // LDS read addresses (stage 0; a stage adds st * 32 KB). K: key r16, chunk
-  // 4 bb + g (bb = 0..15) at 256 (bb / 4) + 16 ((4 (bb % 4) + g) ^ r16). V, key
-  // step e: key 4 g + e, chunk 16 a + r16 at 256 a + 16 (r16 ^ (4 g + e)). DS
-  // reads quarter dq of d only: bb = 4 dq + j, a = dq.
+  // LDS read addresses (stage 0; a stage adds st * 32 KB). K: key r16, 16-d
+  // block bb (= kQ dq + j), chunk 4 bb + g at 256 (bb / 4) + 16 ((4 (bb % 4) +
+  // g) ^ r16). V, key step e, 64-d group a (= kNA dq + j % kNA): key 4 g + e,
+  // chunk 16 a + r16 at 256 a + 16 (r16 ^ (4 g + e)).
   decf_lds_cchar* const st0 = (decf_lds_cchar*)sm.stage[0];
   decf_lds_cchar* kr[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) kr[j] = st0 + r16 * kDecFRow + (((4 * j + g) ^ r16) << 4) + (dq << 8);
+  for (int j = 0; j < 4; ++j) kr[j] = st0 + r16 * kDecFRow + (((4 * j + g) ^ r16) << 4);
   decf_lds_cchar* vr[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int key = 4 * g + e;
-    vr[e] = st0 + kDecFPart + key * kDecFRow + ((r16 ^ key) << 4) + (dq << 8);
+    vr[e] = st0 + kDecFPart + key * kDecFRow + ((r16 ^ key) << 4) + ((kNA * dq) << 8);
   }
+  // byte offset of 16-d block bb = kQ dq + j in a 1 KB row, without the XOR part
+  auto kblk = [&](int j) { return ((kQ * dq + j) >> 2) << 8; };
 
   asm volatile("s_waitcnt vmcnt(8)" ::: "memory");  // this wave's Q, tile-0 and tile-1 copies have landed
   __syncthreads();                                   // ... and every wave's
 
   // a wave whose 16 rows all lie past the group's end takes part in the
   // copies and barriers only
-  const bool live = DS || row0 + wave * kDecFRows < R;
-  // Q as the B operand: qf[j] = Q[row rw][16 bb + 4 g .. + 3] (bb = j, or
-  // 4 dq + j with DS), held in AGPRs (read there by the score products); K of
-  // tile 0 into kf
+  const bool live = row0 + rbw * kDecFRows < R;
+  // Q as the B operand: qf[j] = Q[row rw][16 bb + 4 g .. + 3] (bb = kQ dq + j),
+  // held in AGPRs (read there by the score products); K of tile 0 into kf
   f32x4 qf[kQ], kf[kQ];
   {
-    decf_lds_cchar* qb = (decf_lds_cchar*)sm.stage[kDecFStages - 2] + rw * kDecFRow + (dq << 8);
+    decf_lds_cchar* qb = (decf_lds_cchar*)sm.stage[kDecFStages - 2] + rw * kDecFRow;
 #pragma unroll
     for (int j = 0; j < kQ; ++j) {
-      qf[j] = *(decf_lds_f32x4*)(qb + ((j >> 2) << 8) + (((4 * (j & 3) + g) ^ r16) << 4));
-      kf[j] = *(decf_lds_f32x4*)(kr[j & 3] + ((j >> 2) << 8));
+      qf[j] = *(decf_lds_f32x4*)(qb + kblk(j) + (((4 * (j & 3) + g) ^ r16) << 4));
+      kf[j] = *(decf_lds_f32x4*)(kr[j & 3] + kblk(j));
     }
     // every wave's Q is in registers before the first copy into those stages
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -215,9 +220,9 @@ __global__ __launch_bounds__(kDecFWaves * 64) void decode_f32_kernel(FwdParams p
 
   const float sl2 = p.scale_log2;
   float m = -INFINITY, m_use = 0.f, l = 0.f;
-  f32x4 acc[kNB];
+  f32x4 acc[4 * kNA];
 #pragma unroll
-  for (int nb = 0; nb < kNB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int nb = 0; nb < 4 * kNA; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // Step i: K of tile i is in kf (read during step i - 1); the V reads of tile
   // i go out between the score products, the K reads of tile i + 1 between
@@ -233,34 +238,41 @@ __global__ __launch_bounds__(kDecFWaves * 64) void decode_f32_kernel(FwdParams p
     const int t = t_lo + i;
     const int so = st * kDecFStage;
     const int so1 = (st == kDecFStages - 1 ? 0 : st + 1) * kDecFStage;
-    if (!live) continue;
-
-    // S^T = K Q^T: s[e] is key 4 g + e of row r16, summed as four chains (one
-    // per d offset c) added at the end; V read j (key step j / 4 and d blocks
-    // 4 (j % 4) .. + 3; DS: key step j, d blocks of quarter dq) goes out
-    // before score block j
-    f32x4 s4[4] = {};
+    // (every wave, live or not, reaches the exchange barrier below)
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
     f32x4 vf[kQ];
+    if (live) {
+      // S^T = K Q^T over this wave's part of d: s[e] is key 4 g + e of row
+      // r16, summed as four chains (one per d offset c) added at the end; V
+      // read j (key step j / kNA, 64-d group kNA dq + j % kNA) goes out before
+      // score block j
+      f32x4 s4[4] = {};
 #pragma unroll
-    for (int j = 0; j < kQ; ++j) {
-      vf[j] = DS ? *(decf_lds_f32x4*)(vr[j] + so) : *(decf_lds_f32x4*)(vr[j >> 2] + so + ((j & 3) << 8));
+      for (int j = 0; j < kQ; ++j) {
+        vf[j] = *(decf_lds_f32x4*)(vr[j / kNA] + so + ((j % kNA) << 8));
 #pragma unroll
-      for (int c = 0; c < 4; ++c) s4[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[j][c], qf[j][c], s4[c], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
+        for (int c = 0; c < 4; ++c)
+          s4[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[j][c], qf[j][c], s4[c], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
     }
-    f32x4 s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
-    if (DS) {
-      // the four quarters' partial sums meet in the K part of this tile's
-      // stage (every wave read that K in the step before); each wave adds
-      // them in quarter order
+    if (NDP > 1) {
+      // the parts' partial sums meet in the K part of this tile's stage (every
+      // wave read that K in the step before); the waves of a row block add
+      // them in part order
       float* const xw = (float*)sm.stage[st];
       *(f32x4*)(xw + (wave * 64 + lane) * 4) = s;
       __syncthreads();
-      f32x4 part[4];
+      f32x4 part[NDP];
 #pragma unroll
-      for (int w = 0; w < 4; ++w) part[w] = w == wave ? s : *(const f32x4*)(xw + (w * 64 + lane) * 4);
-      s = ((part[0] + part[1]) + part[2]) + part[3];
+      for (int w = 0; w < NDP; ++w)
+        part[w] = w == dq ? s : *(const f32x4*)(xw + ((rbw * NDP + w) * 64 + lane) * 4);
+      s = part[0];
+#pragma unroll
+      for (int w = 1; w < NDP; ++w) s += part[w];
     }
+    if (!live) continue;
     if (t * kDecFBk + kDecFBk - 1 > mask_from) {
       const int k0 = t * kDecFBk + 4 * g;
 #pragma unroll
@@ -275,7 +287,7 @@ __global__ __launch_bounds__(kDecFWaves * 64) void decode_f32_kernel(FwdParams p
       m = mx;
       m_use = mx;
 #pragma unroll
-      for (int nb = 0; nb < kNB; ++nb) acc[nb] *= alpha;
+      for (int nb = 0; nb < 4 * kNA; ++nb) acc[nb] *= alpha;
       l *= alpha;
     }
     float pe[4];
@@ -284,23 +296,23 @@ __global__ __launch_bounds__(kDecFWaves * 64) void decode_f32_kernel(FwdParams p
     l += (pe[0] + pe[1]) + (pe[2] + pe[3]);
     __builtin_amdgcn_sched_barrier(0);
 
-    // O^T += V^T P^T: key step e, d block 4 a + c (DS: a = dq, block c of the
-    // wave); K read j of tile i + 1 goes out before PV group j
+    // O^T += V^T P^T: key step e = j / kNA, d block 4 (kNA dq + j % kNA) + c
+    // (acc[4 (j % kNA) + c]); K read j of tile i + 1 goes out before PV group j
 #pragma unroll
     for (int j = 0; j < kQ; ++j) {
-      kf[j] = *(decf_lds_f32x4*)(kr[j & 3] + so1 + ((j >> 2) << 8));
-      const int e = DS ? j : j >> 2, a = DS ? 0 : j & 3;
+      kf[j] = *(decf_lds_f32x4*)(kr[j & 3] + so1 + kblk(j));
+      const int e = j / kNA, al = j % kNA;
 #pragma unroll
       for (int c = 0; c < 4; ++c)
-        acc[4 * a + c] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf[j][c], pe[e], acc[4 * a + c], 0, 0, 0);
+        acc[4 * al + c] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf[j][c], pe[e], acc[4 * al + c], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
   // the zero copies of the tiles past the range are still in flight
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  // epilogue: lane holds O[row][64 a + 16 g + 4 e + c] in acc[4 a + c][e] (DS:
-  // a = dq, in acc[c][e])
+  // epilogue: lane holds O[row][64 a + 16 g + 4 e + c] (a = kNA dq + al) in
+  // acc[4 al + c][e]
   const float l_tot = row4_sum(l);
   if (row_ok && live) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -308,12 +320,12 @@ __global__ __launch_bounds__(kDecFWaves * 64) void decode_f32_kernel(FwdParams p
     const int64_t grow = grow0 + rr;
     float* op = p.n_split > 1 ? p.o_part + ((int64_t)split * p.part_rows + grow) * kD : (float*)p.o + grow * kD;
 #pragma unroll
-    for (int a = 0; a < kNB / 4; ++a)
+    for (int al = 0; al < kNA; ++al)
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        *(f32x4*)(op + 64 * (a + dq) + 16 * g + 4 * e) = f32x4{acc[4 * a][e] * inv, acc[4 * a + 1][e] * inv,
-                                                               acc[4 * a + 2][e] * inv, acc[4 * a + 3][e] * inv};
-    if (g == 0 && (!DS || wave == 0)) {
+        *(f32x4*)(op + 64 * (kNA * dq + al) + 16 * g + 4 * e) =
+            f32x4{acc[4 * al][e] * inv, acc[4 * al + 1][e] * inv, acc[4 * al + 2][e] * inv, acc[4 * al + 3][e] * inv};
+    if (g == 0 && dq == 0) {
       if (p.n_split > 1)
         p.lse_part[(int64_t)split * p.part_rows + grow] = lse;
       else

@@ -4,9 +4,10 @@ inputs), through gqa_attn_fwd and gqa_attn_fwd_split, against the fp64
 oracle, every output row.
 
 The kernels pack the query rows of one KV head (n_rep heads x Lq positions)
-into blocks of 64, 16 per wave (the fp32 kernel: groups of at most 16 rows
-share one block of 16 across the 4 waves, each wave a quarter of d), so the
-cases vary what that packing meets (16 rows exactly: (4, 4), (2, 8), (8, 2)):
+into blocks of 64, 16 per wave (the fp32 kernel: groups of at most 16 or 32
+rows take one block of 16 or 32 rows, whose waves each own a quarter or a
+half of d), so the cases vary what that packing meets (16 rows: (4, 4),
+(2, 8), (8, 2); 17-32 rows: (4, 5), (4, 8), (1, 17), (1, 31), (16, 2)):
 group sizes 1..16 and Lq 1..31 (a wave's 16 rows spanning several heads, a
 last block cut short, several blocks per head), causal rows whose visible
 keys end before, at and past the key sequence's end, ragged key counts (16-key
@@ -48,8 +49,8 @@ def check(x, label, n_split=None, unsplit=True, tol_scale=1.0):
 
 
 @pytest.mark.parametrize("dtype", DT)
-@pytest.mark.parametrize("rep,Lq", [(4, 16), (4, 1), (4, 4), (4, 5), (4, 31), (1, 3), (1, 31), (2, 7), (2, 8),
-                                    (8, 2), (8, 16), (16, 2), (16, 31)])
+@pytest.mark.parametrize("rep,Lq", [(4, 16), (4, 1), (4, 4), (4, 5), (4, 8), (4, 31), (1, 3), (1, 17), (1, 31),
+                                    (2, 7), (2, 8), (8, 2), (8, 16), (16, 2), (16, 31)])
 def test_group_sizes_and_lengths(dtype, rep, Lq):
     """Decode rows at the end of a ragged key sequence (2,017 keys: 63 full
     tiles and one of a single key)."""
@@ -105,11 +106,11 @@ def test_peaky_scores_rescale(dtype):
     check(x, "peaky " + dtype, n_split=6, tol_scale=6.0 if dtype == "f32" else 1.0)
 
 
-@pytest.mark.parametrize("dtype,Lq", [("f32", 16), ("f32", 1), ("bf16", 16), ("bf16", 1)])
+@pytest.mark.parametrize("dtype,Lq", [("f32", 16), ("f32", 6), ("f32", 1), ("bf16", 16), ("bf16", 1)])
 def test_full_size_decode_every_row(dtype, Lq):
-    """16 decode positions (64 rows per KV head) or one (4 rows: the fp32
-    kernel's split-d mode) after 60,926 keys, at the library's split count
-    (the measured decode workloads): every row of every head."""
+    """16, 6 or 1 decode positions (64, 24 or 4 rows per KV head: in fp32 one,
+    two or four parts of d per row block) after 60,926 keys, at the library's
+    split count (the measured decode workloads): every row of every head."""
     Lk = 60926
     x = synth.gqa(1, 16, 4, Lq, Lk, seed=370 + Lq, dtype=dtype, q_offset=Lk - Lq)
     check(x, "full size decode %s Lq=%d" % (dtype, Lq), n_split=None, unsplit=False)
