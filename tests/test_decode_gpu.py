@@ -82,9 +82,12 @@ def test_short_key_sequences(dtype, Lk):
 
 
 @pytest.mark.parametrize("dtype", DT)
-def test_noncausal_batch_two(dtype):
-    x = synth.gqa(2, 16, 4, 9, 3001, seed=340, dtype=dtype, causal=False)
-    check(x, "B2 noncausal Lq=9 Lk=3001 " + dtype, n_split=13)
+@pytest.mark.parametrize("Lq", [9, 6, 1])
+def test_noncausal_batch_two(dtype, Lq):
+    """B = 2, not causal; 36, 24 and 4 rows per KV head (in fp32 one, two and
+    four parts of d)."""
+    x = synth.gqa(2, 16, 4, Lq, 3001, seed=340 + Lq, dtype=dtype, causal=False)
+    check(x, "B2 noncausal Lq=%d Lk=3001 %s" % (Lq, dtype), n_split=13)
 
 
 @pytest.mark.parametrize("dtype", DT)
