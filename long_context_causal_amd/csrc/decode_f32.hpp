@@ -8,14 +8,15 @@
 // the PV product.
 //
 // Rows are packed as in the 16-bit decode kernel: the n_rep heads x Lq
-// positions of one KV head form blocks of 64 rows (row rr of a block is head
-// rr / Lq of the group at position rr % Lq; a block is one contiguous run of
-// rows of Q and of O). One workgroup = 4 waves x 16 rows = one block over one
-// key range (a split). Per key tile of 16 keys a wave forms S^T = K Q^T (64
-// products of 16 keys x 16 rows x 4 d), the softmax of its 16 rows and
-// O^T += V^T P^T (4 key steps x 16 d blocks). The long-block kernel's 32-row
-// tiles over 32 positions of 4 heads would leave most rows empty at these
-// lengths: it streams K and V at about 2 TB/s here.
+// positions of one KV head form blocks (row rr of a block is head rr / Lq of
+// the group at position rr % Lq; a block is one contiguous run of rows of Q
+// and of O). One workgroup = one block over one key range (a split); its 4
+// waves hold 16-row blocks, each over all of d or over a half or a quarter of
+// it (NDP below). Per key tile of 16 keys and 16 rows over all of d, S^T =
+// K Q^T takes 64 products of 16 keys x 16 rows x 4 d, and O^T += V^T P^T
+// 64 more (4 key steps x 16 d blocks). The long-block kernel's 32-row tiles
+// over 32 positions of 4 heads would leave most rows empty at these lengths:
+// it streams K and V at about 2 TB/s here.
 //
 // Operand layouts (16x16x4 fp32 product: A lane l = row l % 16, k l / 16; B
 // lane l = column l % 16, k l / 16; D lane l = rows 4 (l / 16) + e, column
@@ -35,8 +36,8 @@
 // 32 KB; all 160 KB) and one workgroup barrier per tile. In step i the V reads
 // of tile i go out between the score products and the K reads of tile i + 1
 // between the PV products (so neither waits for the LDS), while tiles i + 2 ..
-// i + 4 are in flight. Q (64 rows x 1 KB) arrives by the same kind of copy
-// into the last two stages, issued before the first three tiles' copies so
+// i + 4 are in flight. Q (up to 64 rows x 1 KB) arrives by the same kind of
+// copy into the last two stages, issued before the first three tiles' copies so
 // that one wait covers Q and tiles 0 and 1; once every wave holds its Q in
 // registers (a second barrier) those two stages take tiles 3 and 4.
 #pragma once
