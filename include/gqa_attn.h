@@ -72,7 +72,11 @@ enum gqa_status {
 
 /*
  * Attention forward (the operation above). Shapes as above; D must be 256.
- * `stream` is a hipStream_t passed as void*. Returns a gqa_status.
+ * `stream` is a hipStream_t passed as void*. Returns a gqa_status. Calls with
+ * fewer than 32 query positions and no segment ids (decoding) run on kernels
+ * of their own that pack a key/value head's query heads x positions into
+ * 16-row products; their results equal the other kernels' up to the order of
+ * the fp32 sums.
  */
 int gqa_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                  int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
