@@ -55,19 +55,20 @@ def test_forward_replays(dtype):
                  "forward " + dtype)
 
 
-@pytest.mark.parametrize("Lq", [16, 48])
-def test_split_replays(Lq):
-    """16 rows (the decode kernel) and 48 rows (the long-block kernel's split
-    launch), 9 splits over 5,000 keys, with the caller's workspace."""
+@pytest.mark.parametrize("Lq,dtype", [(16, "bf16"), (48, "bf16"), (16, "f32"), (1, "f32")])
+def test_split_replays(Lq, dtype):
+    """16 positions (the decode kernels; fp32 also 1 position, its split-d
+    mode) and 48 (the long-block kernel's split launch), 9 splits over 5,000
+    keys, with the caller's workspace."""
     Lk = 5000
-    q, k, v = inputs(410 + Lq, Lq, Lk)
-    q2, k2, v2 = inputs(420 + Lq, Lq, Lk)
+    q, k, v = inputs(410 + Lq, Lq, Lk, dtype)
+    q2, k2, v2 = inputs(420 + Lq, Lq, Lk, dtype)
     o = torch.empty_like(q)
     lse = torch.empty(1, 16, Lq, dtype=torch.float32, device=q.device)
     ws = torch.empty(gqa.split_workspace(1, 16, Lq, 256, 9), dtype=torch.uint8, device=q.device)
     kw = dict(q_offset=Lk - Lq, n_split=9, out=o, lse=lse, workspace=ws)
     replay_check(lambda: gqa.fwd_split(q, k, v, **kw), lambda: gqa.fwd_split(q2, k2, v2, **kw), o, lse,
-                 "split Lq=%d" % Lq)
+                 "split Lq=%d %s" % (Lq, dtype))
 
 
 def test_noalloc_replays():
