@@ -24,11 +24,10 @@ bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
 
 bool is_pow2_rep(int64_t r) { return r == 1 || r == 2 || r == 4 || r == 8 || r == 16; }
 
-// Launches the short-block (decode) kernel serves: 16-bit inputs, no segment
-// ids, fewer than 32 query positions, and key counts whose 32-key tile ends
-// stay below 2^31 (its tile arithmetic is 32-bit).
-bool decode_shape(int dtype, int64_t Lq, int64_t Lk, bool seg) {
-  (void)dtype;  // every input type has a decode kernel
+// Launches the short-block (decode) kernels serve, for every input type: no
+// segment ids, fewer than 32 query positions, and key counts whose tile ends
+// stay below 2^31 (their tile arithmetic is 32-bit).
+bool decode_shape(int64_t Lq, int64_t Lk, bool seg) {
   return !seg && Lq < gqa::kDecodeMaxLq && Lk < ((int64_t)1 << 31) - 64;
 }
 
@@ -90,7 +89,7 @@ static int fwd_plan(gqa::FwdParams& p, const void* q, const void* k, const void*
   p.n_split = 1;
   p.part_rows = B * Hq * Lq;
   p.decode = 0;
-  if (decode_shape(dtype, Lq, Lk, seg_q != nullptr)) {
+  if (decode_shape(Lq, Lk, seg_q != nullptr)) {
     // row blocks of 64 packed (head, position) rows per KV head
     p.decode = 1;
     p.n_qb = (int)((n_rep * Lq + gqa::kDecodeBlockRows - 1) / gqa::kDecodeBlockRows);
@@ -141,7 +140,7 @@ GQA_API int gqa_attn_split_count(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq,
   const int64_t ppc = (W / hpc) * (dtype == GQA_F32 ? gqa::kRowsF32 : gqa::kRowsH16);
   // workgroups of one split (for short blocks, those of the decode kernel: the
   // count assumes no segment ids)
-  const bool dec = decode_shape(dtype, Lq, Lk, false);
+  const bool dec = decode_shape(Lq, Lk, false);
   const int64_t base = dec ? ((n_rep * Lq + gqa::kDecodeBlockRows - 1) / gqa::kDecodeBlockRows) * B * Hkv
                            : ((Lq + ppc - 1) / ppc) * B * Hkv * (n_rep / hpc);
   const int64_t tile = dec ? decode_tile_keys(dtype) : dtype == GQA_F32 ? gqa::kTileKeysF32 : gqa::kTileKeysH16;
