@@ -396,15 +396,21 @@ def cpu_branch(synth, threads, n_sample=2):
 
 
 def cpu_model():
-    """The host CPU's model name (/proc/cpuinfo, else lscpu), or None where
-    neither lists one."""
-    name = None
+    """The host CPU's model name (/proc/cpuinfo, else lscpu), with its family,
+    model and stepping numbers where /proc/cpuinfo gives them (a virtual
+    machine may list only the brand), or None where neither lists a name."""
+    name, ids = None, {}
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    name = line.split(":", 1)[1].strip()
-                    break
+                if not line.strip():
+                    break  # the first processor's block is enough
+                key, _, val = line.partition(":")
+                key = key.strip()
+                if key == "model name":
+                    name = val.strip()
+                elif key in ("cpu family", "model", "stepping"):
+                    ids[key] = val.strip()
     except OSError:
         pass
     try:
@@ -417,6 +423,8 @@ def cpu_model():
                     name = lname
     except (OSError, subprocess.SubprocessError):
         pass
+    if name and len(ids) == 3:
+        name += " (family %s, model %s, stepping %s)" % (ids["cpu family"], ids["model"], ids["stepping"])
     return name
 
 
