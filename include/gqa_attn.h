@@ -62,7 +62,7 @@ enum gqa_status {
   GQA_OK = 0,
   GQA_ERR_NULL = 1,        /* q, k, v, o or lse is NULL */
   GQA_ERR_SHAPE = 2,       /* an extent <= 0, Hq % Hkv != 0, q_offset < 0, or exactly one segment pointer NULL */
-  GQA_ERR_UNSUPPORTED = 3, /* D != 256, dtype not F32/BF16/F16, Hq/Hkv not in {1,2,4,8,16}, or Lq/Lk >= 2^31
+  GQA_ERR_UNSUPPORTED = 3, /* D != 256, dtype not F32/BF16/F16, Hq/Hkv above 64, or Lq/Lk >= 2^31
                               (backward: Lq/Lk > 2^21) */
   GQA_ERR_ALIGN = 4,       /* q, k, v, o not 16-byte aligned, or lse/seg not 4-byte aligned */
   GQA_ERR_LAUNCH = 5,      /* the HIP runtime reported an error at launch */

@@ -109,7 +109,7 @@ __global__ __launch_bounds__(kDecFWaves * 64) void decode_f32_kernel(FwdParams p
   const int rb = rest % p.n_qb;
   const int bh = rest / p.n_qb;
   const int b = bh / p.Hkv, kvh = bh % p.Hkv;
-  // packed rows of the group (n_rep <= 16 heads x Lq < 32 positions: 32-bit)
+  // packed rows of the group (n_rep <= 64 heads x Lq < 32 positions: 32-bit)
   const int R = p.n_rep * (int)p.Lq;
   const int row0 = rb * kBlockRows;
   const int64_t grow0 = ((int64_t)b * p.Hq + (int64_t)kvh * p.n_rep) * p.Lq;  // global row of packed row 0

@@ -22,7 +22,17 @@ bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
   return x < y + (uintptr_t)nb && y < x + (uintptr_t)na;
 }
 
-bool is_pow2_rep(int64_t r) { return r == 1 || r == 2 || r == 4 || r == 8 || r == 16; }
+// Query heads per key/value head the library takes (any count from 1 to this).
+constexpr int64_t kMaxRep = 64;
+
+// Query heads of one group that a workgroup's waves share out: the largest of
+// W, W / 2, ... that divides n_rep (W = 4: 4, 2 or 1), so that the waves split
+// evenly into heads x position blocks and the group into whole head chunks.
+int64_t heads_per_workgroup(int64_t n_rep, int64_t W) {
+  int64_t h = W;
+  while (n_rep % h != 0) h >>= 1;
+  return h;
+}
 
 // Launches the short-block (decode) kernels serve, for every input type: no
 // segment ids, fewer than 32 query positions, and key counts whose tile ends
@@ -56,7 +66,7 @@ static int fwd_plan(gqa::FwdParams& p, const void* q, const void* k, const void*
   if ((seg_q == nullptr) != (seg_k == nullptr)) return GQA_ERR_SHAPE;
   if (D != gqa::kD || (dtype != GQA_F32 && dtype != GQA_BF16 && dtype != GQA_F16)) return GQA_ERR_UNSUPPORTED;
   const int64_t n_rep = Hq / Hkv;
-  if (!is_pow2_rep(n_rep) || Lq >= ((int64_t)1 << 31) || Lk >= ((int64_t)1 << 31) || B * Hkv >= ((int64_t)1 << 24))
+  if (n_rep > kMaxRep || Lq >= ((int64_t)1 << 31) || Lk >= ((int64_t)1 << 31) || B * Hkv >= ((int64_t)1 << 24))
     return GQA_ERR_UNSUPPORTED;
   if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16) || misaligned(lse, 4) ||
       misaligned(seg_q, 4) || misaligned(seg_k, 4))
@@ -77,7 +87,7 @@ static int fwd_plan(gqa::FwdParams& p, const void* q, const void* k, const void*
   p.seg_q = seg_q; p.seg_k = seg_k;
   p.Lq = Lq; p.Lk = Lk; p.q_offset = q_offset;
   p.Hq = (int)Hq; p.Hkv = (int)Hkv; p.n_rep = (int)n_rep;
-  p.hpc = (int)(n_rep < W ? n_rep : W);
+  p.hpc = (int)heads_per_workgroup(n_rep, W);
   p.ppc = (W / p.hpc) * (dtype == GQA_F32 ? gqa::kRowsF32 : gqa::kRowsH16);
   const int64_t n_qb = (Lq + p.ppc - 1) / p.ppc;
   const int64_t G = B * Hkv * (n_rep / p.hpc);
@@ -136,7 +146,7 @@ GQA_API int gqa_attn_split_count(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq,
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Lq <= 0 || Lk <= 0 || Hq % Hkv != 0) return 1;
   const int64_t n_rep = Hq / Hkv;
   const int W = dtype == GQA_F32 ? gqa::kWavesF32 : gqa::kWavesH16;
-  const int64_t hpc = n_rep < W ? n_rep : W;
+  const int64_t hpc = heads_per_workgroup(n_rep, W);
   const int64_t ppc = (W / hpc) * (dtype == GQA_F32 ? gqa::kRowsF32 : gqa::kRowsH16);
   // workgroups of one split (for short blocks, those of the decode kernel: the
   // count assumes no segment ids)
@@ -290,7 +300,7 @@ GQA_API int gqa_attn_bwd(const void* q, const void* k, const void* v, const void
   if ((seg_q == nullptr) != (seg_k == nullptr)) return GQA_ERR_SHAPE;
   if (D != gqa::kD || (dtype != GQA_F32 && dtype != GQA_BF16 && dtype != GQA_F16)) return GQA_ERR_UNSUPPORTED;
   const int64_t n_rep = Hq / Hkv;
-  if (!is_pow2_rep(n_rep) || Lq > ((int64_t)1 << 21) || Lk > ((int64_t)1 << 21) || B * Hkv >= ((int64_t)1 << 24))
+  if (n_rep > kMaxRep || Lq > ((int64_t)1 << 21) || Lk > ((int64_t)1 << 21) || B * Hkv >= ((int64_t)1 << 24))
     return GQA_ERR_UNSUPPORTED;
   if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16) || misaligned(dout, 16) ||
       misaligned(dq, 16) || misaligned(dk, 16) || misaligned(dv, 16) || misaligned(lse, 4) ||
@@ -320,7 +330,7 @@ GQA_API int gqa_attn_bwd(const void* q, const void* k, const void* v, const void
   const int wq = h16 ? gqa::kBwdWavesDQH : gqa::kBwdWavesDQ;
   const int rq = h16 ? gqa::kBwdRowsDQH : gqa::kBwdRowsDQ;
   const int kb = h16 ? gqa::kBwdKeysDKVH : gqa::kBwdKeysDKV;
-  p.hpc = (int)(n_rep < 4 ? n_rep : 4);
+  p.hpc = (int)heads_per_workgroup(n_rep, 4);
   p.ppc = (wq / p.hpc) * rq;
   const int64_t n_qb = (Lq + p.ppc - 1) / p.ppc;
   const int64_t G = B * Hkv * (n_rep / p.hpc);
@@ -389,4 +399,4 @@ GQA_API const char* gqa_attn_strerror(int code) {
   }
 }
 
-GQA_API int gqa_attn_version(void) { return (1 << 16) | 6; }
+GQA_API int gqa_attn_version(void) { return (1 << 16) | 7; }

@@ -45,7 +45,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_strerror():
-    assert gqa.version() == (1, 6)
+    assert gqa.version() == (1, 7)
     msgs = [gqa.strerror(c) for c in range(8)]
     assert len(set(msgs)) == 8 and msgs[0] == "success"
     assert "unknown" in gqa.strerror(99)
@@ -55,7 +55,7 @@ def test_version_and_strerror():
     (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(o=None), 1), (dict(lse=None), 1),
     (dict(B=0), 2), (dict(Hq=0), 2), (dict(Hkv=0), 2), (dict(Lq=0), 2), (dict(Lk=-1), 2), (dict(D=0), 2),
     (dict(Hq=16, Hkv=3), 2), (dict(q_offset=-1), 2), (dict(seg_q=SQ), 2), (dict(seg_k=SK), 2),
-    (dict(D=128), 3), (dict(dtype=3), 3), (dict(dtype=-1), 3), (dict(Hq=12, Hkv=4), 3), (dict(Hq=32, Hkv=1), 3),
+    (dict(D=128), 3), (dict(dtype=3), 3), (dict(dtype=-1), 3), (dict(Hq=65, Hkv=1), 3), (dict(Hq=256, Hkv=2), 3),
     (dict(Lq=1 << 31), 3), (dict(Lk=1 << 31), 3),
     (dict(q=Q + 2), 4), (dict(k=K + 8), 4), (dict(v=V + 4), 4), (dict(o=O + 2), 4), (dict(lse=LSE + 2), 4),
     (dict(seg_q=SQ + 2, seg_k=SK), 4),
@@ -92,7 +92,7 @@ BWD_GOOD = dict(q=Q, k=K, v=V, o=O, lse=LSE, dout=DO, dq=DQ, dk=DK, dv=DV, delta
     (dict(q=None), 1), (dict(o=None), 1), (dict(lse=None), 1), (dict(dout=None), 1), (dict(dq=None), 1),
     (dict(dk=None), 1), (dict(dv=None), 1), (dict(delta=None), 1),
     (dict(B=0), 2), (dict(Lq=0), 2), (dict(Hq=16, Hkv=3), 2), (dict(q_offset=-1), 2), (dict(seg_q=SQ), 2),
-    (dict(D=128), 3), (dict(dtype=7), 3), (dict(Hq=12, Hkv=4), 3), (dict(Lq=(1 << 21) + 1), 3),
+    (dict(D=128), 3), (dict(dtype=7), 3), (dict(Hq=130, Hkv=2), 3), (dict(Lq=(1 << 21) + 1), 3),
     (dict(Lk=(1 << 21) + 1), 3),
     (dict(dout=DO + 4), 4), (dict(dq=DQ + 8), 4), (dict(dk=DK + 2), 4), (dict(delta=DEL + 2), 4),
     (dict(dq=Q), 6), (dict(dq=DO + 256), 6), (dict(dk=V), 6), (dict(dv=DK), 6), (dict(delta=LSE), 6),
@@ -177,6 +177,13 @@ def test_split_workspace_and_count():
     assert gqa.split_count(1, 16, 4, 16, 260, gqa.GQA_BF16) == 2
     # 16-key tiles (fp32): 200 keys = 13 tiles, a quarter of them (3)
     assert gqa.split_count(1, 16, 4, 16, 200, gqa.GQA_F32) == 3
+    # group sizes that are not powers of two: a workgroup takes the largest of
+    # 4, 2 and 1 heads that divides the group. 3 heads: 1 head x 4 blocks of
+    # 32 positions, so 100 rows are one block x 4 KV heads x 3 head chunks =
+    # 12 workgroups and 22 splits; 6 heads: 2 heads x 64 positions, 2 blocks
+    # x 4 x 3 = 24 workgroups and 11 splits
+    assert gqa.split_count(1, 12, 4, 100, 60926, gqa.GQA_BF16) == 22
+    assert gqa.split_count(1, 24, 4, 100, 60926, gqa.GQA_BF16) == 11
 
 
 def test_python_binding_rejects_host_tensors():

@@ -87,7 +87,7 @@ def test_bwd_noncausal(dtype):
 
 
 @pytest.mark.parametrize("dtype", BWD_DTYPES)
-@pytest.mark.parametrize("rep", [1, 2, 8, 16])
+@pytest.mark.parametrize("rep", [1, 2, 3, 6, 8, 12, 16])
 def test_bwd_group_sizes(dtype, rep):
     Hkv = 2 if rep >= 8 else 4
     check_bwd(synth.gqa(1, Hkv * rep, Hkv, 160, seed=130 + rep, dtype=dtype), "bwd rep%d %s" % (rep, dtype))

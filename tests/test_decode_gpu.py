@@ -8,7 +8,7 @@ into blocks of 64, 16 per wave (the fp32 kernel: groups of at most 16 or 32
 rows take one block of 16 or 32 rows, whose waves each own a quarter or a
 half of d), so the cases vary what that packing meets (16 rows: (4, 4),
 (2, 8), (8, 2); 17-32 rows: (4, 5), (4, 8), (1, 17), (1, 31), (16, 2)):
-group sizes 1..16 and Lq 1..31 (a wave's 16 rows spanning several heads, a
+group sizes 1..16, 3, 6, 12 and 64, and Lq 1..31 (a wave's 16 rows spanning several heads, a
 last block cut short, several blocks per head), causal rows whose visible
 keys end before, at and past the key sequence's end, ragged key counts (16-key
 tiles in fp32, 32-key tiles in 16-bit; a ring of 4 tiles in flight), B = 2,
@@ -50,7 +50,8 @@ def check(x, label, n_split=None, unsplit=True, tol_scale=1.0):
 
 @pytest.mark.parametrize("dtype", DT)
 @pytest.mark.parametrize("rep,Lq", [(4, 16), (4, 1), (4, 4), (4, 5), (4, 8), (4, 31), (1, 3), (1, 17), (1, 31),
-                                    (2, 7), (2, 8), (8, 2), (8, 16), (16, 2), (16, 31)])
+                                    (2, 7), (2, 8), (8, 2), (8, 16), (16, 2), (16, 31), (3, 1), (3, 11),
+                                    (6, 5), (12, 3), (64, 1), (64, 31)])
 def test_group_sizes_and_lengths(dtype, rep, Lq):
     """Decode rows at the end of a ragged key sequence (2,017 keys: 63 full
     tiles and one of a single key)."""

@@ -75,9 +75,12 @@ def test_branch_offset(dtype):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
-@pytest.mark.parametrize("rep", [1, 2, 8, 16])
+@pytest.mark.parametrize("rep", [1, 2, 3, 5, 6, 8, 12, 16, 64])
 def test_other_group_sizes(dtype, rep):
-    Hkv = 2 if rep >= 8 else 4
+    """Query heads per KV head: powers of two, and 3, 5, 6, 12 (a workgroup
+    takes 1 or 2 heads of the group, the most of 4, 2, 1 dividing it) up to
+    the largest group the library takes (64)."""
+    Hkv = 1 if rep == 64 else 2 if rep >= 8 else 4
     check(synth.gqa(1, Hkv * rep, Hkv, 200, seed=rep, dtype=dtype), "rep%d %s" % (rep, dtype))
 
 

@@ -2,10 +2,10 @@
 fp64 oracle, every output row.
 
 Each case draws, from a seed of its own: the input type, batch 1-2, 1-3
-key/value heads, a group size of 1-16 query heads per key/value head, query
-and key lengths from 1 to a few hundred (half the cases below the decode
-bound of 32 positions, half of those without ids), causal or not, q_offset at the end of the keys, at 0
-or anywhere up to 500, segment ids absent, packed (sorted runs over the
+key/value heads, a group of 1, 2, 3, 4, 6, 8, 12 or 16 query heads per
+key/value head, query and key lengths from 1 to a few hundred (half the cases
+below the decode bound of 32 positions, half of those without ids), causal or
+not, q_offset at the end of the keys, at 0 or anywhere up to 500, segment ids absent, packed (sorted runs over the
 position axis) or random over 3 values, and a split count from 1 to more than
 the key tiles. So the cases reach the long-block kernels, both decode
 kernels with each of their modes, the segment paths, ragged tiles, empty
@@ -35,7 +35,7 @@ def draw(case):
     dtype = ("f32", "bf16", "f16")[case % 3]
     B = int(rng.integers(1, 3))
     Hkv = int(rng.integers(1, 4))
-    rep = int(rng.choice([1, 2, 4, 8, 16]))
+    rep = int(rng.choice([1, 2, 3, 4, 6, 8, 12, 16]))
     short = (case // 3) % 2 == 0  # half the cases below the decode bound, for each type
     Lq = int(rng.integers(1, 32)) if short else int(rng.integers(1, 300))
     Lk = int(rng.integers(1, 400))

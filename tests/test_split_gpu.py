@@ -59,7 +59,7 @@ def test_noncausal_batch_and_ragged_keys(dtype):
 
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_other_group_sizes(dtype):
-    for rep in (1, 16):
+    for rep in (1, 3, 6, 16):
         Hkv = 2 if rep == 16 else 4
         x = synth.gqa(1, Hkv * rep, Hkv, 8, 2100, seed=230 + rep, dtype=dtype, q_offset=2092)
         check_split(x, "rep%d %s" % (rep, dtype), 5)
