@@ -123,6 +123,42 @@ def test_tiny_with_segments(dtype, L):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("packed", [True, False])
+def test_extreme_segment_ids(dtype, packed):
+    """Ids at the ends of int32, which the id scan also uses to mark an empty
+    range: packed runs of INT32_MIN, -1, 0, INT32_MAX (each id once), or those
+    four drawn at random; some query rows take an id no key has, so their
+    rows are empty."""
+    lo, hi = np.iinfo(np.int32).min, np.iinfo(np.int32).max
+    L = 700
+    vals = np.array([lo, -1, 0, hi], dtype=np.int32)
+    if packed:
+        ids = np.repeat(vals, [150, 200, 100, 250])[None]
+    else:
+        ids = np.random.default_rng(60).choice(vals, size=(1, L)).astype(np.int32)
+    for causal in (True, False):
+        x = synth.gqa(1, 16, 4, L, seed=61, dtype=dtype, causal=causal)
+        x.seg_k = ids
+        x.seg_q = ids.copy()
+        x.seg_q[0, 5::97] = 7
+        check(x, "ids at the int32 ends, %s %s causal=%s" % ("packed" if packed else "random", dtype, causal))
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_causal_offset_far_past_the_keys(dtype):
+    """A causal call whose query positions start 2^40 past the keys sees every
+    key: it equals the non-causal call, bit for bit (the same tiles, in the
+    same order, with no mask), and the oracle."""
+    x = synth.gqa(2, 16, 4, 100, 300, seed=62, dtype=dtype, q_offset=1 << 40, causal=True)
+    check(x, "causal q_offset=2^40 " + dtype)
+    o, lse = run(x)
+    q, k, v = to_dev(x)
+    o2, l2 = gqa.fwd(q, k, v, causal=False)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, l2)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("causal", [True, False])
 def test_packed_segments_equal_per_segment_calls(dtype, causal):
     """Packed segments with ids give, row for row, what each segment gives as
