@@ -118,6 +118,28 @@ def test_bwd_random_segments_empty_rows(dtype, causal):
 
 
 @pytest.mark.parametrize("dtype", BWD_DTYPES)
+@pytest.mark.parametrize("packed", [True, False])
+def test_bwd_extreme_segment_ids(dtype, packed):
+    """Ids at the ends of int32 (the id scans' empty-range marks): packed runs
+    of INT32_MIN, -1, 0, INT32_MAX, or those four at random; some query rows
+    and some keys take an id the other side lacks."""
+    lo, hi = np.iinfo(np.int32).min, np.iinfo(np.int32).max
+    L = 300
+    vals = np.array([lo, -1, 0, hi], dtype=np.int32)
+    if packed:
+        sk = np.repeat(vals, [70, 90, 40, 100])[None]
+    else:
+        sk = np.random.default_rng(152).choice(vals, size=(1, L)).astype(np.int32)
+    sq = sk.copy()
+    sq[0, 3::53] = 9
+    sk = sk.copy()
+    sk[0, 7::61] = 8
+    x = synth.gqa(1, 16, 4, L, seed=153, dtype=dtype)
+    x.seg_q, x.seg_k = sq, sk
+    check_bwd(x, "bwd ids at the int32 ends, %s %s" % ("packed" if packed else "random", dtype))
+
+
+@pytest.mark.parametrize("dtype", BWD_DTYPES)
 @pytest.mark.parametrize("L", [1, 2, 3, 5])
 def test_bwd_tiny_with_segments(dtype, L):
     """Fewer id entries than one 16-byte load: the id scan's small-array path."""
