@@ -407,12 +407,60 @@ __device__ void seg_scan(SegBits& sb, int sh, const FwdParams& p, const Work& w,
                            p.Lk, n_tiles);
 }
 
-// The map word holding group g, in a scalar register: the tile index derived
-// from it then feeds scalar address arithmetic (the tile copies take their
-// buffer resource from SGPRs written by scalar instructions, never straight
-// from a VALU write, which a copy would have to trail by 5 wait states).
-__device__ __forceinline__ unsigned map_word(const unsigned* bits, int g) {
-  return __builtin_amdgcn_readfirstlane(bits[g >> 5]);
+// The searches below run on every lane of the wave with the same arguments
+// (the kernels call them where control flow is wave-uniform): lane l reads map
+// word w0 + l (or w1 - l), so one LDS read and one ballot cover 64 words
+// (2,048 groups), and the word that holds the answer comes over from its lane
+// into a scalar register (v_readlane). The tile index derived from it then
+// feeds scalar address arithmetic: the tile copies take their buffer resource
+// from SGPRs written by scalar instructions, never straight from a VALU
+// write, which a copy would have to trail by 5 wait states. A serial walk
+// word by word took one LDS round trip per 32 groups, thousands of cycles for
+// a workgroup far into a long sequence.
+
+// First group in [g, ng) whose bit in `bits` is `val` (ng if none).
+__device__ __forceinline__ int seg_find(const unsigned* bits, int g, int ng, bool val) {
+  const int lane = lane_id();
+  const int wg = g >> 5, wlast = (ng - 1) >> 5;
+  for (int w0 = wg; w0 <= wlast; w0 += 64) {
+    const int wi = w0 + lane;
+    unsigned w = 0u;
+    if (wi <= wlast) {
+      w = bits[wi];
+      if (!val) w = ~w;
+      if (wi == wg) w &= ~0u << (g & 31);  // groups below g
+    }
+    const uint64_t m = __builtin_amdgcn_ballot_w64(w != 0u);
+    if (m) {
+      const int l = __builtin_ctzll(m);
+      const unsigned wf = (unsigned)__builtin_amdgcn_readlane((int)w, l);
+      const int r = ((w0 + l) << 5) + __builtin_ctz(wf);
+      return r < ng ? r : ng;
+    }
+  }
+  return ng;
+}
+
+// Last group in [glo, g] whose bit in `bits` is set (glo - 1 if none).
+__device__ __forceinline__ int seg_find_last(const unsigned* bits, int g, int glo) {
+  const int lane = lane_id();
+  const int wg = g >> 5, wlo = glo >> 5;
+  for (int w1 = wg; w1 >= wlo; w1 -= 64) {
+    const int wi = w1 - lane;
+    unsigned w = 0u;
+    if (wi >= wlo) {
+      w = bits[wi];
+      if (wi == wg) w &= (2u << (g & 31)) - 1u;  // groups above g
+    }
+    const uint64_t m = __builtin_amdgcn_ballot_w64(w != 0u);
+    if (m) {
+      const int l = __builtin_ctzll(m);
+      const unsigned wf = (unsigned)__builtin_amdgcn_readlane((int)w, l);
+      const int r = ((w1 - l) << 5) + 31 - __builtin_clz(wf);
+      return r >= glo ? r : glo - 1;
+    }
+  }
+  return glo - 1;
 }
 
 // First tile >= t of a visible group (n_tiles if none): t itself when its
@@ -420,17 +468,9 @@ __device__ __forceinline__ unsigned map_word(const unsigned* bits, int g) {
 __device__ __forceinline__ int seg_next(const SegBits& sb, int sh, int t, int n_tiles) {
   if (t >= n_tiles) return n_tiles;
   const int g0 = t >> sh, ng = ((n_tiles - 1) >> sh) + 1;
-  int g = g0;
-  while (g < ng) {
-    const unsigned m = map_word(sb.vis, g) >> (g & 31);
-    if (m) {
-      const int r = g + __builtin_ctz(m);
-      if (r >= ng) return n_tiles;
-      return r == g0 ? t : min(n_tiles, r << sh);
-    }
-    g = (g | 31) + 1;
-  }
-  return n_tiles;
+  const int r = seg_find(sb.vis, g0, ng, true);
+  if (r >= ng) return n_tiles;
+  return r == g0 ? t : min(n_tiles, r << sh);
 }
 
 // Last tile <= t and >= lo of a visible group (lo - 1 if none): t itself when
@@ -438,32 +478,9 @@ __device__ __forceinline__ int seg_next(const SegBits& sb, int sh, int t, int n_
 __device__ __forceinline__ int seg_prev(const SegBits& sb, int sh, int t, int lo) {
   if (t < lo) return lo - 1;
   const int g0 = t >> sh, glo = lo >> sh;
-  int g = g0;
-  while (g >= glo) {
-    const unsigned m = map_word(sb.vis, g) << (31 - (g & 31));
-    if (m) {
-      const int r = g - __builtin_clz(m);
-      if (r < glo) return lo - 1;
-      return r == g0 ? t : ((r + 1) << sh) - 1;
-    }
-    g = (g & ~31) - 1;
-  }
-  return lo - 1;
-}
-
-// First group in [g, ng) whose bit in `bits` is `val` (ng if none).
-__device__ __forceinline__ int seg_find(const unsigned* bits, int g, int ng, bool val) {
-  while (g < ng) {
-    unsigned w = map_word(bits, g);
-    if (!val) w = ~w;
-    w >>= (g & 31);
-    if (w) {
-      const int r = g + __builtin_ctz(w);
-      return r < ng ? r : ng;
-    }
-    g = (g | 31) + 1;
-  }
-  return ng;
+  const int r = seg_find_last(sb.vis, g0, glo);
+  if (r < glo) return lo - 1;
+  return r == g0 ? t : ((r + 1) << sh) - 1;
 }
 
 // The first run of set bits of a map (vis or full) at or after tile t, in
