@@ -25,6 +25,7 @@ if ROOT not in sys.path:
 
 METRIC = "causal GQA attn fwd TFLOP/s + % MFMA peak (fp32 & bf16, L=32k/64k); peak GiB"
 HQ, HKV, D = 16, 4, 256
+SEG_IDX_NOTE = ", id index built per call"
 
 
 def dev_inputs(x, torch):
@@ -55,7 +56,9 @@ def time_calls(fn, steps, warmup, torch):
     return wall_ms, float(np.mean(ev_ms)), float(np.min(ev_ms)), float(np.max(ev_ms))
 
 
-def run_fwd_workload(name, x, steps, warmup, torch, gqa, work, seg=None):
+def run_fwd_workload(name, x, steps, warmup, torch, gqa, work, seg=None, indexed=False):
+    """One forward workload. indexed: every timed call first builds the ids'
+    range index (gqa_attn_seg_index) and then runs gqa_attn_fwd_indexed."""
     torch.cuda.synchronize()
     torch.cuda.reset_peak_memory_stats()
     base = torch.cuda.memory_allocated()
@@ -68,6 +71,13 @@ def run_fwd_workload(name, x, steps, warmup, torch, gqa, work, seg=None):
     B, Hq, Lq, Dh = q.shape
     lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device)
     fn = lambda: gqa.fwd(q, k, v, causal=x.causal, q_offset=x.q_offset, seg_q=sq, seg_k=sk, out=o, lse=lse)
+    if indexed and seg is not None:
+        ibuf = gqa.seg_index(sk)
+
+        def fn():
+            idx = gqa.seg_index(sk, out=ibuf)
+            gqa.fwd(q, k, v, causal=x.causal, q_offset=x.q_offset, seg_q=sq, seg_k=sk, out=o, lse=lse,
+                    seg_q_index=idx, seg_k_index=idx)
     fn()  # first launch loads the code object; device memory is compared after it
     torch.cuda.synchronize()
     free0, _ = torch.cuda.mem_get_info()
@@ -86,7 +96,7 @@ def run_fwd_workload(name, x, steps, warmup, torch, gqa, work, seg=None):
                 bytes=work.hbm_bytes(B, Hq, Hkv_, Lq, Lk, Dh, 4 if x.dtype == "f32" else 2, seg is not None))
 
 
-def run_bwd_workload(name, x, steps, warmup, torch, gqa, work, synth, seg=None):
+def run_bwd_workload(name, x, steps, warmup, torch, gqa, work, synth, seg=None, indexed=False):
     """The backward (dQ kernel + dK/dV kernel) on the forward's own o and lse;
     dout drawn N(0,1) (seed 1); optional packed segment ids. Times the backward
     call only."""
@@ -105,6 +115,14 @@ def run_bwd_workload(name, x, steps, warmup, torch, gqa, work, synth, seg=None):
     delta = torch.empty_like(lse)
     fn = lambda: gqa.bwd(q, k, v, o, lse, do, causal=x.causal, q_offset=x.q_offset, seg_q=sid, seg_k=sid, dq=dq,
                          dk=dk, dv=dv, delta=delta)
+    if indexed and seg is not None:
+        # the ids' range index built in every timed call, then the indexed backward
+        ibuf = gqa.seg_index(sid)
+
+        def fn():
+            idx = gqa.seg_index(sid, out=ibuf)
+            gqa.bwd(q, k, v, o, lse, do, causal=x.causal, q_offset=x.q_offset, seg_q=sid, seg_k=sid, dq=dq, dk=dk,
+                    dv=dv, delta=delta, seg_q_index=idx, seg_k_index=idx)
     fn()
     torch.cuda.synchronize()
     wall_ms, ev_ms, ev_min, ev_max = time_calls(fn, steps, warmup, torch)
@@ -596,7 +614,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only", default=None,
                     help="run one workload: f32-15231, f32-30468, f32-60926, bf16-60926, f16-60926, "
-                         "seg-bf16-131072, noids-bf16-131072, branch-f32, bwd-f32-30468, bwd-bf16-60926, "
+                         "seg-bf16-131072, segidx-bf16-131072, noids-bf16-131072, branch-f32, bwd-f32-30468, bwd-bf16-60926, "
                          "split-decode-bf16, split-decode1-bf16, split-decode-f32, split-decode1-f32, "
                          "split-branch-f32, cp-f32-30468")
     ap.add_argument("--copy-probe", action="store_true",
@@ -676,14 +694,16 @@ def main():
         print(json.dumps(r), flush=True)
         return
     Lseg = 131072
-    if args.only in ("seg-bf16-131072", "noids-bf16-131072"):
-        # a profiling aid: the packed-segment workload (or its id-free comparator) alone
+    if args.only in ("seg-bf16-131072", "segidx-bf16-131072", "noids-bf16-131072"):
+        # a profiling aid: the packed-segment workload (plain or through the id
+        # index) or its id-free comparator alone
         lens = synth.segment_lengths(Lseg, 2048, 32768, seed=1)
         xs = synth.gqa(1, HQ, HKV, Lseg, seed=0, dtype="bf16")
         seg = synth.segment_ids(lens) if args.only.startswith("seg") else None
-        nm = ("segmented bf16 L=131072, %d segments (2k-32k)" % len(lens) if seg is not None else
-              "single-segment comparator bf16 L=131072 (no ids)")
-        r = run_fwd_workload(nm, xs, args.steps, args.warmup, torch, gqa, work, seg=seg)
+        indexed = args.only.startswith("segidx")
+        nm = ("segmented bf16 L=131072, %d segments (2k-32k)%s" % (len(lens), SEG_IDX_NOTE if indexed else "")
+              if seg is not None else "single-segment comparator bf16 L=131072 (no ids)")
+        r = run_fwd_workload(nm, xs, args.steps, args.warmup, torch, gqa, work, seg=seg, indexed=indexed)
         r["pct_mfma_peak"] = 100.0 * r["kernel_tflops"] / work.PEAK_TFLOPS["bf16"]
         if args.copy_probe:
             r["copy_probe_bytes"] = copy_probe(torch)
@@ -749,10 +769,16 @@ def main():
         secondary.append(r)
         if cpu:
             cpu_cfg.append(cpu_entry(r["workload"], xs, threads, r["flops"] // (4 * D * HQ), seg=ids))
+        r = run_fwd_workload("segmented bf16 L=131072, %d segments (2k-32k)%s" % (len(lens), SEG_IDX_NOTE), xs,
+                             max(3, args.steps // 2), 2, torch, gqa, work, seg=ids, indexed=True)
+        secondary.append(r)
         r = run_fwd_workload("single-segment comparator bf16 L=131072 (no ids)", xs, 3, 1, torch, gqa, work)
         secondary.append(r)
         r = run_bwd_workload("segmented bwd bf16 L=131072, %d segments (2k-32k)" % len(lens), xs, 3, 1, torch, gqa,
                              work, synth, seg=ids)
+        secondary.append(r)
+        r = run_bwd_workload("segmented bwd bf16 L=131072, %d segments (2k-32k)%s" % (len(lens), SEG_IDX_NOTE), xs,
+                             3, 1, torch, gqa, work, synth, seg=ids, indexed=True)
         secondary.append(r)
         del xs
         # context-parallel shards of the headline workload, N = 2, 4, 8 ranks

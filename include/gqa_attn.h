@@ -61,13 +61,16 @@ enum gqa_dtype { GQA_F32 = 0, GQA_BF16 = 1, GQA_F16 = 2 };
 enum gqa_status {
   GQA_OK = 0,
   GQA_ERR_NULL = 1,        /* q, k, v, o or lse is NULL */
-  GQA_ERR_SHAPE = 2,       /* an extent <= 0, Hq % Hkv != 0, q_offset < 0, or exactly one segment pointer NULL */
+  GQA_ERR_SHAPE = 2,       /* an extent <= 0, Hq % Hkv != 0, q_offset < 0, exactly one segment pointer NULL,
+                              or an id index without segment ids */
   GQA_ERR_UNSUPPORTED = 3, /* D != 256, dtype not F32/BF16/F16, Hq/Hkv above 64, or Lq/Lk >= 2^31
                               (backward: Lq/Lk > 2^21) */
-  GQA_ERR_ALIGN = 4,       /* q, k, v, o not 16-byte aligned, or lse/seg not 4-byte aligned */
+  GQA_ERR_ALIGN = 4,       /* q, k, v, o not 16-byte aligned, lse/seg not 4-byte aligned, or an id index
+                              not 8-byte aligned */
   GQA_ERR_LAUNCH = 5,      /* the HIP runtime reported an error at launch */
   GQA_ERR_ALIAS = 6,       /* o overlaps q, k or v (or, for merge, partially overlaps an input) */
-  GQA_ERR_WORKSPACE = 7    /* split-KV workspace smaller than gqa_attn_split_workspace() requires */
+  GQA_ERR_WORKSPACE = 7    /* split-KV workspace smaller than gqa_attn_split_workspace() requires,
+                              or an id index buffer smaller than gqa_attn_seg_index_bytes() */
 };
 
 /*
@@ -135,6 +138,55 @@ int gqa_attn_bwd(const void* q, const void* k, const void* v, const void* o, con
                  int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
                  int64_t q_offset, const int32_t* seg_q, const int32_t* seg_k,
                  int causal, int dtype, void* stream);
+
+/*
+ * Id-range index of a segment-id array, for callers that run many calls over
+ * the same ids (every layer's forward and backward of one packed batch). With
+ * ids, each workgroup of gqa_attn_fwd and gqa_attn_bwd finds the key (or row)
+ * tiles it must visit by reading every id up to its causal end. The index
+ * holds, for each block of 16 consecutive ids of a batch row, their minimum
+ * and maximum (int32 pairs, row-major [B][ceil(L / 16)][2]); the *_indexed
+ * calls classify the tiles from it, from one eighth of the bytes, and give
+ * results identical bit for bit to the calls without it. The same role as the
+ * per-block mask metadata that splash attention builds ahead of its kernel
+ * (maxtext pull request 4929, the problem statement: fwd_mask_info.data_next,
+ * block_mask, mask_next, the kernel's prefetched operands), but linear in L.
+ *
+ * gqa_attn_seg_index_bytes: the index size in bytes for B rows of L ids
+ * (0 for a non-positive extent).
+ * gqa_attn_seg_index: writes the index of seg [B, L] (device, int32) into
+ * `index` (device, 8-byte aligned, at least gqa_attn_seg_index_bytes(B, L)
+ * bytes, not overlapping seg); enqueued on `stream`. Errors: GQA_ERR_NULL,
+ * GQA_ERR_SHAPE (B or L <= 0), GQA_ERR_UNSUPPORTED (L >= 2^31 or B >= 2^24),
+ * GQA_ERR_ALIGN, GQA_ERR_WORKSPACE (index too small), GQA_ERR_ALIAS; nothing is
+ * enqueued on an error.
+ */
+int64_t gqa_attn_seg_index_bytes(int64_t B, int64_t L);
+int gqa_attn_seg_index(const int32_t* seg, int64_t B, int64_t L, void* index, int64_t index_bytes, void* stream);
+
+/*
+ * gqa_attn_fwd and gqa_attn_bwd with the indexes of seg_q (over Lq) and seg_k
+ * (over Lk) from gqa_attn_seg_index, written on this stream or complete before
+ * the call. Either index may be NULL (its ids are then scanned as in the plain
+ * call); both must be NULL without segment ids (else GQA_ERR_SHAPE). The
+ * forward reads the key index; the backward's dQ kernel the key index, its
+ * dK/dV kernel the row index. An index that does not match its ids gives
+ * unspecified results (the ids themselves still mask every element the tile
+ * classification lets through). Indexes must be 8-byte aligned (else
+ * GQA_ERR_ALIGN) and must not overlap an output (else GQA_ERR_ALIAS). Other
+ * arguments, outputs and errors as the plain calls.
+ */
+int gqa_attn_fwd_indexed(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
+                         int64_t q_offset, const int32_t* seg_q, const int32_t* seg_k,
+                         const void* seg_q_index, const void* seg_k_index,
+                         int causal, int dtype, void* stream);
+int gqa_attn_bwd_indexed(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                         const void* dout, void* dq, void* dk, void* dv, float* delta,
+                         int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
+                         int64_t q_offset, const int32_t* seg_q, const int32_t* seg_k,
+                         const void* seg_q_index, const void* seg_k_index,
+                         int causal, int dtype, void* stream);
 
 /*
  * Split-KV forward: the same operation and outputs as gqa_attn_fwd (equal up

@@ -19,7 +19,9 @@ GQA_F32, GQA_BF16, GQA_F16 = 0, 1, 2
 STATUS = {0: "GQA_OK", 1: "GQA_ERR_NULL", 2: "GQA_ERR_SHAPE", 3: "GQA_ERR_UNSUPPORTED",
           4: "GQA_ERR_ALIGN", 5: "GQA_ERR_LAUNCH", 6: "GQA_ERR_ALIAS", 7: "GQA_ERR_WORKSPACE"}
 EXPORTS = ("gqa_attn_fwd", "gqa_attn_merge", "gqa_attn_bwd", "gqa_attn_fwd_split", "gqa_attn_fwd_split_noalloc",
-           "gqa_attn_split_workspace", "gqa_attn_split_count", "gqa_attn_strerror", "gqa_attn_version")
+           "gqa_attn_split_workspace", "gqa_attn_split_count", "gqa_attn_seg_index_bytes", "gqa_attn_seg_index",
+           "gqa_attn_fwd_indexed", "gqa_attn_bwd_indexed", "gqa_attn_strerror", "gqa_attn_version")
+SEG_BLOCK = 16  # ids per entry of an id-range index (gqa_attn_seg_index)
 NOALLOC_SCRATCH_BYTES = 64 << 20  # GQA_NOALLOC_SCRATCH_BYTES
 
 _lib = None
@@ -56,6 +58,15 @@ def load_library():
         lib.gqa_attn_split_workspace.restype = i64
         lib.gqa_attn_split_count.argtypes = [i64, i64, i64, i64, i64, c_int]
         lib.gqa_attn_split_count.restype = c_int
+        lib.gqa_attn_seg_index_bytes.argtypes = [i64, i64]
+        lib.gqa_attn_seg_index_bytes.restype = i64
+        lib.gqa_attn_seg_index.argtypes = [p, i64, i64, p, i64, p]
+        lib.gqa_attn_seg_index.restype = c_int
+        lib.gqa_attn_fwd_indexed.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i64, i64, i64, p, p, p, p, c_int,
+                                             c_int, p]
+        lib.gqa_attn_fwd_indexed.restype = c_int
+        lib.gqa_attn_bwd_indexed.argtypes = [p] * 10 + [i64] * 7 + [p, p, p, p, c_int, c_int, p]
+        lib.gqa_attn_bwd_indexed.restype = c_int
         lib.gqa_attn_strerror.argtypes = [c_int]
         lib.gqa_attn_strerror.restype = ctypes.c_char_p
         lib.gqa_attn_version.argtypes = []
@@ -84,6 +95,31 @@ def bwd_raw(q, k, v, o, lse, dout, dq, dk, dv, delta, B, Hq, Hkv, Lq, Lk, D, q_o
     """Direct call of gqa_attn_bwd with integer pointers; returns the status code."""
     return load_library().gqa_attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, Hq, Hkv, Lq, Lk, D,
                                        q_offset, seg_q, seg_k, int(causal), int(dtype), stream)
+
+
+def seg_index_bytes(B, L) -> int:
+    """Bytes of the id-range index of B rows of L segment ids."""
+    return int(load_library().gqa_attn_seg_index_bytes(B, L))
+
+
+def seg_index_raw(seg, B, L, index, index_bytes, stream) -> int:
+    """Direct call of gqa_attn_seg_index with integer pointers; returns the status code."""
+    return load_library().gqa_attn_seg_index(seg, B, L, index, index_bytes, stream)
+
+
+def fwd_indexed_raw(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, D, q_offset, seg_q, seg_k, seg_q_index, seg_k_index,
+                    causal, dtype, stream) -> int:
+    """Direct call of gqa_attn_fwd_indexed with integer pointers; returns the status code."""
+    return load_library().gqa_attn_fwd_indexed(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, D, q_offset, seg_q, seg_k,
+                                               seg_q_index, seg_k_index, int(causal), int(dtype), stream)
+
+
+def bwd_indexed_raw(q, k, v, o, lse, dout, dq, dk, dv, delta, B, Hq, Hkv, Lq, Lk, D, q_offset, seg_q, seg_k,
+                    seg_q_index, seg_k_index, causal, dtype, stream) -> int:
+    """Direct call of gqa_attn_bwd_indexed with integer pointers; returns the status code."""
+    return load_library().gqa_attn_bwd_indexed(q, k, v, o, lse, dout, dq, dk, dv, delta, B, Hq, Hkv, Lq, Lk, D,
+                                               q_offset, seg_q, seg_k, seg_q_index, seg_k_index, int(causal),
+                                               int(dtype), stream)
 
 
 def fwd_split_raw(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, D, q_offset, seg_q, seg_k, causal, dtype, n_split,
@@ -143,11 +179,43 @@ def _stream_ptr(stream):
     return s.cuda_stream
 
 
-def fwd(q, k, v, *, causal=True, q_offset=0, seg_q=None, seg_k=None, out=None, lse=None, stream=None):
+def seg_index(seg, *, out=None, stream=None):
+    """Id-range index of int32 segment ids seg [B, L]: for each block of 16
+    consecutive ids of a row their (min, max), an int32 tensor [B, ceil(L/16), 2].
+    fwd() and bwd() take it (seg_q_index, seg_k_index) in place of scanning the
+    ids in every workgroup; results are the same bit for bit."""
+    import torch
+    _check_dev(seg, out)
+    if seg.dtype != torch.int32 or seg.dim() != 2:
+        raise TypeError("segment ids must be an int32 [B, L] tensor")
+    B, L = seg.shape
+    shape = (B, (L + SEG_BLOCK - 1) // SEG_BLOCK, 2)
+    out = torch.empty(shape, dtype=torch.int32, device=seg.device) if out is None else out
+    if tuple(out.shape) != shape or out.dtype != torch.int32:
+        raise ValueError("index must be an int32 tensor of shape %s" % (shape,))
+    rc = seg_index_raw(seg.data_ptr(), B, L, out.data_ptr(), out.numel() * 4, _stream_ptr(stream))
+    if rc != 0:
+        raise GqaError(rc, strerror(rc))
+    return out
+
+
+def _check_index(idx, B, L, name):
+    import torch
+    if idx is None:
+        return None
+    _check_dev(idx)
+    if idx.dtype != torch.int32 or tuple(idx.shape) != (B, (L + SEG_BLOCK - 1) // SEG_BLOCK, 2):
+        raise ValueError("%s must be seg_index() of the matching ids" % name)
+    return idx.data_ptr()
+
+
+def fwd(q, k, v, *, causal=True, q_offset=0, seg_q=None, seg_k=None, out=None, lse=None, stream=None,
+        seg_q_index=None, seg_k_index=None):
     """Attention forward: q [B,Hq,Lq,D], k/v [B,Hkv,Lk,D] (fp32, bf16 or fp16, same dtype),
     optional int32 segment ids seg_q [B,Lq] / seg_k [B,Lk]. Returns (o, lse) with
     o like q and lse [B,Hq,Lq] fp32. Work is enqueued on `stream` (default: the
-    current stream)."""
+    current stream). seg_q_index / seg_k_index: optional seg_index() of the ids
+    (the call then goes to gqa_attn_fwd_indexed)."""
     import torch
     _check_dev(q, k, v, seg_q, seg_k, out, lse)
     if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
@@ -172,10 +240,13 @@ def fwd(q, k, v, *, causal=True, q_offset=0, seg_q=None, seg_k=None, out=None, l
         lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device)
     if out.shape != q.shape or out.dtype != q.dtype or lse.shape != (B, Hq, Lq) or lse.dtype != torch.float32:
         raise ValueError("out must match q and lse must be [B,Hq,Lq] float32")
-    rc = fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                 B, Hq, Hkv, Lq, Lk, D, int(q_offset),
-                 None if seg_q is None else seg_q.data_ptr(), None if seg_k is None else seg_k.data_ptr(),
-                 causal, dt, _stream_ptr(stream))
+    qi, ki = _check_index(seg_q_index, B, Lq, "seg_q_index"), _check_index(seg_k_index, B, Lk, "seg_k_index")
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Hq, Hkv, Lq, Lk, D,
+            int(q_offset), None if seg_q is None else seg_q.data_ptr(), None if seg_k is None else seg_k.data_ptr())
+    if qi is None and ki is None:
+        rc = fwd_raw(*args, causal, dt, _stream_ptr(stream))
+    else:
+        rc = fwd_indexed_raw(*args, qi, ki, causal, dt, _stream_ptr(stream))
     if rc != 0:
         raise GqaError(rc, strerror(rc))
     return out, lse
@@ -204,12 +275,13 @@ def merge(o1, lse1, o2, lse2, *, out=None, out_lse=None, stream=None):
 
 
 def bwd(q, k, v, o, lse, dout, *, causal=True, q_offset=0, seg_q=None, seg_k=None, dq=None, dk=None, dv=None,
-        delta=None, stream=None):
+        delta=None, stream=None, seg_q_index=None, seg_k_index=None):
     """Attention backward: gradients with respect to q, k and v of a loss whose
     gradient with respect to the forward output o is `dout` (like q). o and lse
     are the forward's outputs for the same arguments (or the merged ones of a
     split key set). Returns (dq, dk, dv, delta): dq like q, dk and dv like k,
-    delta [B,Hq,Lq] float32 (the row dot products dout . o)."""
+    delta [B,Hq,Lq] float32 (the row dot products dout . o). seg_q_index /
+    seg_k_index: optional seg_index() of the ids (gqa_attn_bwd_indexed)."""
     import torch
     _check_dev(q, k, v, o, lse, dout, seg_q, seg_k, dq, dk, dv, delta)
     if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape or o.shape != q.shape or dout.shape != q.shape:
@@ -238,10 +310,14 @@ def bwd(q, k, v, o, lse, dout, *, causal=True, q_offset=0, seg_q=None, seg_k=Non
         raise ValueError("gradient buffers must match q, k, v and delta [B,Hq,Lq]")
     if any(t.dtype != q.dtype for t in (dq, dk, dv)) or delta.dtype != torch.float32:
         raise TypeError("gradients share q's dtype; delta is float32")
-    rc = bwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
-                 dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, Hq, Hkv, Lq, Lk, D,
-                 int(q_offset), None if seg_q is None else seg_q.data_ptr(),
-                 None if seg_k is None else seg_k.data_ptr(), causal, dt, _stream_ptr(stream))
+    qi, ki = _check_index(seg_q_index, B, Lq, "seg_q_index"), _check_index(seg_k_index, B, Lk, "seg_k_index")
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(), dq.data_ptr(),
+            dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, Hq, Hkv, Lq, Lk, D, int(q_offset),
+            None if seg_q is None else seg_q.data_ptr(), None if seg_k is None else seg_k.data_ptr())
+    if qi is None and ki is None:
+        rc = bwd_raw(*args, causal, dt, _stream_ptr(stream))
+    else:
+        rc = bwd_indexed_raw(*args, qi, ki, causal, dt, _stream_ptr(stream))
     if rc != 0:
         raise GqaError(rc, strerror(rc))
     return dq, dk, dv, delta

@@ -294,9 +294,11 @@ __global__ __launch_bounds__(kWavesDKV * 64) void bwd_dkv_f32_kernel(BwdParams b
 
   const bool seg = p.seg_q != nullptr;
   const int sh = seg ? seg_shift(n_rb) : 0;
+  // the row ids' index, where the call brings one (rows of ceil(Lq / 16) entries per batch)
+  const SegBlk* qix = p.seg_q_idx ? p.seg_q_idx + (int64_t)b * ((p.Lq + kSegBlk - 1) / kSegBlk) : nullptr;
   if (seg)
-    seg_scan_ids<kWavesDKV * 64, kRowsDKV>(sm.bits, sh, p.seg_k + (int64_t)b * p.Lk, j0, kKeysBlockDKV, p.Lk,
-                                           p.seg_q + (int64_t)b * p.Lq, p.Lq, n_rb, rb0);
+    seg_scan_any<kWavesDKV * 64, kRowsDKV>(sm.bits, sh, p.seg_k + (int64_t)b * p.Lk, j0, kKeysBlockDKV, p.Lk,
+                                           p.seg_q + (int64_t)b * p.Lq, qix, p.Lq, n_rb, rb0);
   const int sk = seg ? p.seg_k[(int64_t)b * p.Lk + key_c] : 0;
 
   // K of the lane's key in registers: chunk 4 c + g (d = 16 c + 4 g + e). V of

@@ -369,9 +369,11 @@ __global__ __launch_bounds__(kWavesH * 64) void bwd_dkv_h16_kernel(BwdParams bp)
   const int rb0 = (int)(r_first / kRowsDKVH);
   const int n_rb = (int)((p.Lq + kRowsDKVH - 1) / kRowsDKVH);
   const int sh = SEG ? seg_shift(n_rb) : 0;
+  // the row ids' index, where the call brings one (rows of ceil(Lq / 16) entries per batch)
+  const SegBlk* qix = p.seg_q_idx ? p.seg_q_idx + (int64_t)b * ((p.Lq + kSegBlk - 1) / kSegBlk) : nullptr;
   if (SEG)
-    seg_scan_ids<kWavesH * 64, kRowsDKVH>(sm.bits, sh, p.seg_k + (int64_t)b * p.Lk, j0, kKeysBlockDKVH, p.Lk,
-                                          p.seg_q + (int64_t)b * p.Lq, p.Lq, n_rb, rb0);
+    seg_scan_any<kWavesH * 64, kRowsDKVH>(sm.bits, sh, p.seg_k + (int64_t)b * p.Lk, j0, kKeysBlockDKVH, p.Lk,
+                                          p.seg_q + (int64_t)b * p.Lq, qix, p.Lq, n_rb, rb0);
   const int sk = SEG ? p.seg_k[(int64_t)b * p.Lk + key_c] : 0;
 
   // K of the lane's key (B-operand layout: chunk 2 c + g); V of the block's

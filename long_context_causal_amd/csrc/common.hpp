@@ -21,6 +21,13 @@ constexpr float kInvSqrtD = 0.0625f;  // 1/sqrt(kD), exact
 static_assert(kD == 256, "kInvSqrtD is 1/sqrt(256)");
 constexpr int kRowsPerWave = 32;    // query rows (one head, 32 positions) per wave
 
+// Id range (min, max) of one block of kSegBlk consecutive segment ids: the
+// entry type of the index that gqa_attn_seg_index writes.
+constexpr int kSegBlk = 16;
+struct SegBlk {
+  int32_t lo, hi;
+};
+
 // Arguments of one forward launch (passed by value).
 struct FwdParams {
   const void* q;
@@ -30,6 +37,10 @@ struct FwdParams {
   float* lse;
   const int32_t* seg_q;
   const int32_t* seg_k;
+  // optional id-range indexes of seg_q / seg_k (SegBlk per 16 entries, rows of
+  // ceil(L / 16) per batch; null: the kernels scan the ids themselves)
+  const SegBlk* seg_q_idx;
+  const SegBlk* seg_k_idx;
   int64_t Lq, Lk, q_offset;
   int Hq, Hkv, n_rep;
   int hpc;        // query heads per workgroup (a divisor of n_rep)
@@ -278,15 +289,12 @@ __device__ __forceinline__ unsigned pack_quads(uint64_t m) {
 // batch come from one ballot; larger groups reduce further across lanes (and
 // across batches) and set their bits with LDS atomics. Each wave owns a
 // contiguous run of map words.
-template <int NT, int BT>
-__device__ void seg_scan_ids(SegBits& sb, int sh, const int32_t* own, int64_t own0, int own_n, int64_t own_len,
-                             const int32_t* other, int64_t other_len, int n_tiles, int t_first = 0) {
-  static_assert(BT == 16 || BT == 32 || BT == 64, "tiles of 16, 32 or 64 entries");
-  constexpr int W = NT / 64;
-  constexpr int kCh = BT / 16;     // 16-entry chunks per tile: loads per batch
-  constexpr int kNB = 16 / kCh;    // batches per pass (16 loads per lane in flight)
-  const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
-  const int q = lane >> 2, r = lane & 3;
+// First part of both scans: the id range of the own entries into sb.qmin /
+// sb.qmax, and the map words of n_tiles tiles cleared; returns the word count.
+template <int NT>
+__device__ int seg_scan_begin(SegBits& sb, int sh, const int32_t* own, int64_t own0, int own_n, int64_t own_len,
+                              int n_tiles) {
+  const int tid = threadIdx.x, lane = lane_id();
   if (tid == 0) { sb.qmin = INT32_MAX; sb.qmax = INT32_MIN; }
   __syncthreads();
   {
@@ -303,6 +311,19 @@ __device__ void seg_scan_ids(SegBits& sb, int sh, const int32_t* own, int64_t ow
   const int n_words = (n_groups + 31) >> 5;
   for (int wd = tid; wd < n_words; wd += NT) { sb.vis[wd] = 0u; sb.full[wd] = 0u; }
   __syncthreads();
+  return n_words;
+}
+
+template <int NT, int BT>
+__device__ void seg_scan_ids(SegBits& sb, int sh, const int32_t* own, int64_t own0, int own_n, int64_t own_len,
+                             const int32_t* other, int64_t other_len, int n_tiles, int t_first = 0) {
+  static_assert(BT == 16 || BT == 32 || BT == 64, "tiles of 16, 32 or 64 entries");
+  constexpr int W = NT / 64;
+  constexpr int kCh = BT / 16;     // 16-entry chunks per tile: loads per batch
+  constexpr int kNB = 16 / kCh;    // batches per pass (16 loads per lane in flight)
+  const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+  const int q = lane >> 2, r = lane & 3;
+  const int n_words = seg_scan_begin<NT>(sb, sh, own, own0, own_n, own_len, n_tiles);
   const int qmin = sb.qmin, qmax = sb.qmax;
   const int64_t lim = min(other_len, (int64_t)n_tiles * BT);  // entries past it count as absent
   const int w_first = min(n_words, (min(t_first, n_tiles) >> sh) >> 5);
@@ -400,11 +421,109 @@ __device__ void seg_scan_ids(SegBits& sb, int sh, const int32_t* own, int64_t ow
   __syncthreads();
 }
 
+// The same classification from an id-range index of the scanned side
+// (SegBlk per kSegBlk entries, nblk = ceil(other_len / kSegBlk) entries) in
+// place of its ids: a tile's range is the range of its BT / kSegBlk index
+// entries, which is the range of its ids, so the map comes out bit for bit as
+// seg_scan_ids makes it, from 1/8 of the bytes. Layout of the reads: a batch
+// is 64 consecutive tiles, one per lane; 4 batches per pass, their entries
+// loaded together (addresses clamped into the index, entries past its end
+// taken as empty).
+template <int NT, int BT>
+__device__ void seg_scan_index(SegBits& sb, int sh, const int32_t* own, int64_t own0, int own_n, int64_t own_len,
+                               const SegBlk* other, int64_t other_len, int n_tiles, int t_first = 0) {
+  static_assert(BT == 16 || BT == 32 || BT == 64, "tiles of 16, 32 or 64 entries");
+  constexpr int W = NT / 64;
+  constexpr int kE = BT / kSegBlk;  // index entries per tile
+  constexpr int kB = 4;             // batches of 64 tiles per pass
+  const int lane = lane_id(), wave = wave_id();
+  const int n_words = seg_scan_begin<NT>(sb, sh, own, own0, own_n, own_len, n_tiles);
+  const int qmin = sb.qmin, qmax = sb.qmax;
+  const int64_t nblk = (other_len + kSegBlk - 1) / kSegBlk;
+  const int w_first = min(n_words, (min(t_first, n_tiles) >> sh) >> 5);
+  const int per_wave = (n_words - w_first + W - 1) / W;
+  const int wb = w_first + wave * per_wave, we = min(n_words, wb + per_wave);
+  if (wb < we) {
+    const int64_t tb = (int64_t)wb << (5 + sh), te = min((int64_t)n_tiles, (int64_t)we << (5 + sh));
+    const int gq = sh < 6 ? 1 << sh : 64;        // lanes per group within a batch
+    const int nbg = sh > 6 ? 1 << (sh - 6) : 1;  // batches per group
+    int bg = 0, lo_acc = INT32_MAX, hi_acc = INT32_MIN;
+    for (int64_t t0 = tb; t0 < te; t0 += 64 * kB) {
+      SegBlk e[kB][kE];
+#pragma unroll
+      for (int b = 0; b < kB; ++b)
+#pragma unroll
+        for (int i = 0; i < kE; ++i) {
+          const int64_t blk = (t0 + 64 * b + lane) * kE + i;
+          e[b][i] = other[blk < nblk ? blk : nblk - 1];
+        }
+#pragma unroll
+      for (int b = 0; b < kB; ++b) {
+        const int64_t tbat = t0 + 64 * b;
+        if (tbat >= te) break;  // uniform
+        const int64_t t = tbat + lane;
+        int lo = INT32_MAX, hi = INT32_MIN;
+#pragma unroll
+        for (int i = 0; i < kE; ++i) {
+          const bool ok = t < te && t * kE + i < nblk;
+          lo = ok ? min(lo, e[b][i].lo) : lo;
+          hi = ok ? max(hi, e[b][i].hi) : hi;
+        }
+        if (sh == 0) {
+          // one tile per bit: the batch's 64 bits from one ballot, two map
+          // words (the second only while it is this wave's)
+          const uint64_t vm = __builtin_amdgcn_ballot_w64(lo <= hi && lo <= qmax && hi >= qmin);
+          const uint64_t fm = __builtin_amdgcn_ballot_w64(lo <= hi && lo == hi && qmin == qmax && lo == qmin);
+          const int wd = (int)(tbat >> 5);
+          if (lane == 0) {
+            sb.vis[wd] = (unsigned)vm;
+            sb.full[wd] = (unsigned)fm;
+            if (wd + 1 < we) {
+              sb.vis[wd + 1] = (unsigned)(vm >> 32);
+              sb.full[wd + 1] = (unsigned)(fm >> 32);
+            }
+          }
+        } else {
+          // groups of 2^sh tiles: gq lanes of this batch (and nbg batches)
+          group_minmax(lo, hi, gq);
+          lo_acc = min(lo_acc, lo);
+          hi_acc = max(hi_acc, hi);
+          if (++bg < nbg && tbat + 64 < te) continue;  // the range's last group may be cut short
+          bg = 0;
+          lo = lo_acc;
+          hi = hi_acc;
+          lo_acc = INT32_MAX;
+          hi_acc = INT32_MIN;
+          if ((lane & (gq - 1)) == 0 && lo <= hi) {
+            const int gi = (int)(t >> sh);
+            if (lo <= qmax && hi >= qmin) atomicOr(&sb.vis[gi >> 5], 1u << (gi & 31));
+            if (lo == hi && qmin == qmax && lo == qmin) atomicOr(&sb.full[gi >> 5], 1u << (gi & 31));
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// Scans of the forward, the dQ kernel (key tiles) and the dK/dV kernel (row
+// tiles): from the index where the call brings one, else from the ids.
+template <int NT, int BT>
+__device__ __forceinline__ void seg_scan_any(SegBits& sb, int sh, const int32_t* own, int64_t own0, int own_n,
+                                             int64_t own_len, const int32_t* other, const SegBlk* other_idx,
+                                             int64_t other_len, int n_tiles, int t_first = 0) {
+  if (other_idx)
+    seg_scan_index<NT, BT>(sb, sh, own, own0, own_n, own_len, other_idx, other_len, n_tiles, t_first);
+  else
+    seg_scan_ids<NT, BT>(sb, sh, own, own0, own_n, own_len, other, other_len, n_tiles, t_first);
+}
+
 // The forward's use: own = the workgroup's query rows, scanned = key tiles of BK.
 template <int W, int BK>
 __device__ void seg_scan(SegBits& sb, int sh, const FwdParams& p, const Work& w, int n_tiles) {
-  seg_scan_ids<W * 64, BK>(sb, sh, p.seg_q + (int64_t)w.b * p.Lq, w.p0, p.ppc, p.Lq, p.seg_k + (int64_t)w.b * p.Lk,
-                           p.Lk, n_tiles);
+  const int64_t nblk = (p.Lk + kSegBlk - 1) / kSegBlk;
+  seg_scan_any<W * 64, BK>(sb, sh, p.seg_q + (int64_t)w.b * p.Lq, w.p0, p.ppc, p.Lq, p.seg_k + (int64_t)w.b * p.Lk,
+                           p.seg_k_idx ? p.seg_k_idx + (int64_t)w.b * nblk : nullptr, p.Lk, n_tiles);
 }
 
 // The searches below run on every lane of the wave with the same arguments

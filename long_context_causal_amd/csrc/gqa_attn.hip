@@ -11,6 +11,7 @@
 #include "common.hpp"
 #include "launch.hpp"
 #include "merge.hpp"
+#include "seg_index.hpp"
 
 namespace {
 
@@ -138,6 +139,64 @@ GQA_API int gqa_attn_fwd(const void* q, const void* k, const void* v, void* o, f
   gqa::FwdParams p{};
   const int rc = fwd_plan(p, q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, D, q_offset, seg_q, seg_k, causal, dtype);
   if (rc != GQA_OK) return rc;
+  (void)hipGetLastError();
+  return launch_fwd(p, dtype, (hipStream_t)stream) == hipSuccess ? GQA_OK : GQA_ERR_LAUNCH;
+}
+
+// Index rows of a sequence of L ids.
+static int64_t seg_index_blocks(int64_t L) { return (L + gqa::kSegBlk - 1) / gqa::kSegBlk; }
+
+GQA_API int64_t gqa_attn_seg_index_bytes(int64_t B, int64_t L) {
+  if (B <= 0 || L <= 0) return 0;
+  return B * seg_index_blocks(L) * (int64_t)sizeof(gqa::SegBlk);
+}
+
+GQA_API int gqa_attn_seg_index(const int32_t* seg, int64_t B, int64_t L, void* index, int64_t index_bytes,
+                               void* stream) {
+  if (!seg || !index) return GQA_ERR_NULL;
+  if (B <= 0 || L <= 0) return GQA_ERR_SHAPE;
+  if (L >= ((int64_t)1 << 31) || B >= ((int64_t)1 << 24)) return GQA_ERR_UNSUPPORTED;
+  if (misaligned(seg, 4) || misaligned(index, 8)) return GQA_ERR_ALIGN;
+  const int64_t need = gqa_attn_seg_index_bytes(B, L);
+  if (index_bytes < need) return GQA_ERR_WORKSPACE;
+  if (overlap(index, need, seg, B * L * 4)) return GQA_ERR_ALIAS;
+  const int64_t nblk = seg_index_blocks(L), total = B * nblk;
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(gqa::seg_index_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, seg, L, nblk,
+                     total, (gqa::SegBlk*)index);
+  return hipGetLastError() == hipSuccess ? GQA_OK : GQA_ERR_LAUNCH;
+}
+
+// Checks of the optional id-range indexes of an indexed call: each only
+// beside segment ids, 8-byte aligned, and apart from every output.
+static int index_checks(const void* seg_q, const void* seg_q_index, const void* seg_k_index, int64_t B, int64_t Lq,
+                        int64_t Lk, const void* const* outs, const int64_t* out_n, int n_out) {
+  if (!seg_q && (seg_q_index || seg_k_index)) return GQA_ERR_SHAPE;
+  if (misaligned(seg_q_index, 8) || misaligned(seg_k_index, 8)) return GQA_ERR_ALIGN;
+  const int64_t qn = gqa_attn_seg_index_bytes(B, Lq), kn = gqa_attn_seg_index_bytes(B, Lk);
+  for (int a = 0; a < n_out; ++a)
+    if ((seg_q_index && overlap(outs[a], out_n[a], seg_q_index, qn)) ||
+        (seg_k_index && overlap(outs[a], out_n[a], seg_k_index, kn)))
+      return GQA_ERR_ALIAS;
+  return GQA_OK;
+}
+
+GQA_API int gqa_attn_fwd_indexed(const void* q, const void* k, const void* v, void* o, float* lse,
+                                 int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
+                                 int64_t q_offset, const int32_t* seg_q, const int32_t* seg_k,
+                                 const void* seg_q_index, const void* seg_k_index,
+                                 int causal, int dtype, void* stream) {
+  gqa::FwdParams p{};
+  const int rc = fwd_plan(p, q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, D, q_offset, seg_q, seg_k, causal, dtype);
+  if (rc != GQA_OK) return rc;
+  const int64_t es = dtype == GQA_F32 ? 4 : 2;
+  const void* outs[2] = {o, lse};
+  const int64_t out_n[2] = {B * Hq * Lq * D * es, B * Hq * Lq * 4};
+  const int ri = index_checks(seg_q, seg_q_index, seg_k_index, B, Lq, Lk, outs, out_n, 2);
+  if (ri != GQA_OK) return ri;
+  p.seg_q_idx = (const gqa::SegBlk*)seg_q_index;
+  p.seg_k_idx = (const gqa::SegBlk*)seg_k_index;
   (void)hipGetLastError();
   return launch_fwd(p, dtype, (hipStream_t)stream) == hipSuccess ? GQA_OK : GQA_ERR_LAUNCH;
 }
@@ -289,11 +348,11 @@ GQA_API int gqa_attn_fwd_split_noalloc(const void* q, const void* k, const void*
                        GQA_NOALLOC_SCRATCH_BYTES, s);
 }
 
-GQA_API int gqa_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                         const void* dout, void* dq, void* dk, void* dv, float* delta,
-                         int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
-                         int64_t q_offset, const int32_t* seg_q, const int32_t* seg_k,
-                         int causal, int dtype, void* stream) {
+static int bwd_run(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dout, void* dq, void* dk, void* dv, float* delta,
+                   int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
+                   int64_t q_offset, const int32_t* seg_q, const int32_t* seg_k,
+                   const void* seg_q_index, const void* seg_k_index, int causal, int dtype, void* stream) {
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !delta) return GQA_ERR_NULL;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Lq <= 0 || Lk <= 0 || D <= 0) return GQA_ERR_SHAPE;
   if (Hq % Hkv != 0 || q_offset < 0 || q_offset > ((int64_t)1 << 62)) return GQA_ERR_SHAPE;
@@ -318,11 +377,15 @@ GQA_API int gqa_attn_bwd(const void* q, const void* k, const void* v, const void
     for (int b2 = a + 1; b2 < 4; ++b2)
       if (overlap(outs[a], out_n[a], outs[b2], out_n[b2])) return GQA_ERR_ALIAS;
   }
+  const int ri = index_checks(seg_q, seg_q_index, seg_k_index, B, Lq, Lk, outs, out_n, 4);
+  if (ri != GQA_OK) return ri;
 
   gqa::BwdParams bp{};
   gqa::FwdParams& p = bp.f;
   p.q = q; p.k = k; p.v = v; p.o = const_cast<void*>(o); p.lse = const_cast<float*>(lse);
   p.seg_q = seg_q; p.seg_k = seg_k;
+  p.seg_q_idx = (const gqa::SegBlk*)seg_q_index;
+  p.seg_k_idx = (const gqa::SegBlk*)seg_k_index;
   p.Lq = Lq; p.Lk = Lk; p.q_offset = q_offset;
   p.Hq = (int)Hq; p.Hkv = (int)Hkv; p.n_rep = (int)n_rep;
   // work shapes: dQ kernel waves x rows per wave, keys per dK/dV workgroup
@@ -350,6 +413,25 @@ GQA_API int gqa_attn_bwd(const void* q, const void* k, const void* v, const void
                        : dtype == GQA_BF16 ? gqa::launch_bwd_bf16(bp, s)
                                            : gqa::launch_bwd_f16(bp, s);
   return e == hipSuccess ? GQA_OK : GQA_ERR_LAUNCH;
+}
+
+GQA_API int gqa_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                         const void* dout, void* dq, void* dk, void* dv, float* delta,
+                         int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
+                         int64_t q_offset, const int32_t* seg_q, const int32_t* seg_k,
+                         int causal, int dtype, void* stream) {
+  return bwd_run(q, k, v, o, lse, dout, dq, dk, dv, delta, B, Hq, Hkv, Lq, Lk, D, q_offset, seg_q, seg_k, nullptr,
+                 nullptr, causal, dtype, stream);
+}
+
+GQA_API int gqa_attn_bwd_indexed(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                                 const void* dout, void* dq, void* dk, void* dv, float* delta,
+                                 int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
+                                 int64_t q_offset, const int32_t* seg_q, const int32_t* seg_k,
+                                 const void* seg_q_index, const void* seg_k_index,
+                                 int causal, int dtype, void* stream) {
+  return bwd_run(q, k, v, o, lse, dout, dq, dk, dv, delta, B, Hq, Hkv, Lq, Lk, D, q_offset, seg_q, seg_k,
+                 seg_q_index, seg_k_index, causal, dtype, stream);
 }
 
 GQA_API int gqa_attn_merge(const void* o1, const float* lse1, const void* o2, const float* lse2,
@@ -387,16 +469,18 @@ GQA_API const char* gqa_attn_strerror(int code) {
   switch (code) {
     case GQA_OK: return "success";
     case GQA_ERR_NULL: return "a required pointer is NULL";
-    case GQA_ERR_SHAPE: return "invalid shape: non-positive extent, Hq not a multiple of Hkv, negative q_offset, or only one segment-id array";
-    case GQA_ERR_UNSUPPORTED: return "unsupported: D must be 256, dtype F32, BF16 or F16, Hq/Hkv in {1,2,4,8,16}, "
+    case GQA_ERR_SHAPE: return "invalid shape: non-positive extent, Hq not a multiple of Hkv, negative q_offset, "
+                               "only one segment-id array, or an id index without segment ids";
+    case GQA_ERR_UNSUPPORTED: return "unsupported: D must be 256, dtype F32, BF16 or F16, Hq/Hkv at most 64, "
                                      "lengths below 2^31 (backward: at most 2^21)";
     case GQA_ERR_ALIGN: return "misaligned pointer: tensors need 16-byte alignment, lse and segment ids 4-byte";
     case GQA_ERR_LAUNCH: return "kernel launch failed";
     case GQA_ERR_ALIAS: return "output overlaps an input";
     case GQA_ERR_WORKSPACE: return "workspace smaller than gqa_attn_split_workspace() for the split count "
-                                   "(allocation-free call: the partials exceed GQA_NOALLOC_SCRATCH_BYTES)";
+                                   "(allocation-free call: the partials exceed GQA_NOALLOC_SCRATCH_BYTES; "
+                                   "id index: smaller than gqa_attn_seg_index_bytes())";
     default: return "unknown status code";
   }
 }
 
-GQA_API int gqa_attn_version(void) { return (1 << 16) | 7; }
+GQA_API int gqa_attn_version(void) { return (1 << 16) | 8; }

@@ -45,7 +45,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_strerror():
-    assert gqa.version() == (1, 7)
+    assert gqa.version() == (1, 8)
     msgs = [gqa.strerror(c) for c in range(8)]
     assert len(set(msgs)) == 8 and msgs[0] == "success"
     assert "unknown" in gqa.strerror(99)
@@ -201,3 +201,52 @@ def test_product_path_does_not_import_the_oracle():
             if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "oracle_attn" not in text, f
+
+
+# id-range index (gqa_attn_seg_index) and the indexed forward and backward
+QI, KI = 14 << 40, 15 << 40
+
+
+def test_seg_index_bytes():
+    assert gqa.seg_index_bytes(1, 131072) == 131072 // 16 * 8
+    assert gqa.seg_index_bytes(3, 17) == 3 * 2 * 8  # a partial last block of one id
+    assert gqa.seg_index_bytes(0, 16) == 0 and gqa.seg_index_bytes(1, 0) == 0
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(seg=None), 1), (dict(index=None), 1), (dict(B=0), 2), (dict(L=-3), 2), (dict(L=1 << 31), 3),
+    (dict(B=1 << 24), 3), (dict(seg=SQ + 2), 4), (dict(index=QI + 4), 4), (dict(index_bytes=8 * 63 - 1), 7),
+    (dict(index=SQ + 256), 6), (dict(index=SQ - 64), 6),
+])
+def test_seg_index_rejects_before_launch(over, code):
+    a = dict(seg=SQ, B=1, L=1000, index=QI, index_bytes=8 * 64, stream=None)
+    a.update(over)
+    assert gqa.seg_index_raw(a["seg"], a["B"], a["L"], a["index"], a["index_bytes"], a["stream"]) == code
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), 1), (dict(Lq=0), 2), (dict(D=128), 3),
+    # an index without segment ids, misaligned, or under an output
+    (dict(seg_q=None, seg_k=None), 2), (dict(seg_q=None, seg_k=None, seg_q_index=None), 2),
+    (dict(seg_q_index=QI + 4), 4), (dict(seg_k_index=KI + 2), 4),
+    (dict(o=QI - 4096), 6), (dict(lse=KI + 8), 6), (dict(lse=KI - 64), 6),
+])
+def test_fwd_indexed_rejects_before_launch(over, code):
+    a = dict(GOOD, seg_q=SQ, seg_k=SK, seg_q_index=QI, seg_k_index=KI)
+    a.update(over)
+    assert gqa.fwd_indexed_raw(*(a[n] for n in ("q", "k", "v", "o", "lse", "B", "Hq", "Hkv", "Lq", "Lk", "D",
+                                                "q_offset", "seg_q", "seg_k", "seg_q_index", "seg_k_index",
+                                                "causal", "dtype", "stream"))) == code
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(dq=None), 1), (dict(seg_q=None, seg_k=None), 2), (dict(seg_k_index=KI + 4), 4),
+    (dict(dq=QI - 64), 6), (dict(delta=KI + 16), 6), (dict(dk=QI - 1024), 6),
+])
+def test_bwd_indexed_rejects_before_launch(over, code):
+    a = dict(BWD_GOOD, seg_q=SQ, seg_k=SK, seg_q_index=QI, seg_k_index=KI)
+    a.update(over)
+    assert gqa.bwd_indexed_raw(*(a[n] for n in ("q", "k", "v", "o", "lse", "dout", "dq", "dk", "dv", "delta", "B",
+                                                "Hq", "Hkv", "Lq", "Lk", "D", "q_offset", "seg_q", "seg_k",
+                                                "seg_q_index", "seg_k_index", "causal", "dtype",
+                                                "stream"))) == code
