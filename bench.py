@@ -617,6 +617,9 @@ def main():
                          "seg-bf16-131072, segidx-bf16-131072, noids-bf16-131072, branch-f32, bwd-f32-30468, bwd-bf16-60926, "
                          "split-decode-bf16, split-decode1-bf16, split-decode-f32, split-decode1-f32, "
                          "split-branch-f32, cp-f32-30468")
+    ap.add_argument("--cpu-full", action="store_true",
+                    help="also time the oracle on the whole headline workload (every row, all threads; "
+                         "about 90 s on 16 host threads at L=30468)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (3 times) to calibrate HBM byte counters")
     ap.add_argument("--pmc-summary", nargs="+", metavar="DB",
@@ -825,6 +828,14 @@ def main():
         out["copy_probe_bytes"] = copy_probe(torch)
     if cpu:
         out["cpu_baseline"] = cpu_baseline(x, threads, aff)
+        if args.cpu_full:
+            from long_context_causal_amd import work as _work
+            Lh = x.q.shape[2]
+            print("bench: timing the oracle on the whole fp32 L=%d forward on %d threads" % (Lh, threads),
+                  file=sys.stderr, flush=True)
+            full = cpu_entry("causal GQA fwd fp32 L=%d, every row" % Lh, x, threads, _work.visible_pairs(Lh, Lh),
+                             full=True)
+            out["cpu_baseline"]["full"] = {k: (round(v, 5) if isinstance(v, float) else v) for k, v in full.items()}
         if cpu_cfg:
             out["cpu_baseline"]["per_config"] = [{k: (round(v, 5) if isinstance(v, float) else v)
                                                  for k, v in c.items()} for c in cpu_cfg]
